@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+A step is one pass of the decode hot path over the 32-stream x 32768-slot
+workload: append one token per stream (index key + K + V) at position 32767,
+score -> causal mask -> block max-pool (indexer scan), top-16 block selection,
+and sparse attention of all 64 heads over the 2048 selected keys.  `value` is
+decode queries/s (32 queries per step), inputs resident in HBM.
+
+Also measured in the same run and reported under "extra": the indexer scan
+and decode attention GB/s, the 4096-query prefill chunk at positions
+28672..32767 (append + MFMA block scores + top-16 + block-sparse attention,
+prefill tok/s), and the DSA lightning-indexer decode (16 streams x 65536).
+
+`roofline` is the dominant kernel (the decode indexer scan): algorithmic bytes
+per launch / mean launch time from HIP events recorded on the stream the
+kernel runs on.  `cpu_baseline` times the fp64 oracle on the host cores on
+the same workload (one step's 32 queries).
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MSA decode queries/s at 32 streams×32K ctx; indexer GB/s; prefill tok/s"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="decode step only (for profiling)")
+    return ap.parse_args()
+
+
+def kernel_source_hash(name):
+    with open(os.path.join(ROOT, "block_sparse_attention_msa_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src):
+    """HBM traffic per launch measured by rocprofv3 counters (profiles/
+    traffic.json), valid only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != kernel_source_hash(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards across GPUs without exchange by stream, group or query; see the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_msa_amd as M
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def bits(a, dtype):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dtype).to(dev)
+
+    def tens(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def wsbuf(dims, op, n_q, max_pos):
+        return torch.empty(max(M.workspace_bytes(dims, op, n_q, max_pos), 256), dtype=torch.uint8, device=dev)
+
+    # ------------------------------------------------------------------
+    # decode 32 x 32K
+    # ------------------------------------------------------------------
+    wl = W.CONFIGS["decode_32x32k"]
+    t0 = time.time()
+    host = W.caches(wl)
+    qs = W.queries(wl)
+    log(f"[bench] generated {wl.name} inputs in {time.time() - t0:.1f}s")
+    S, cap, p = wl.n_stream, wl.cap, wl.max_pos
+    dims = M.msa_dims(16, W.SCALE)
+    idx_k = tens(host["idx_k"])
+    k = bits(host["k"], torch.bfloat16)
+    v = bits(host["v"], torch.bfloat16)
+    cache = M.make_cache(k=k, v=v, idx_k=idx_k)
+    stream = tens(qs["stream"])
+    pos = tens(qs["pos"])
+    idx_q = tens(qs["idx_q"])
+    q = bits(qs["q"], torch.bfloat16)
+    new_idx = tens(host["idx_k"][np.arange(S), qs["pos"]])
+    new_k = bits(host["k"][np.arange(S), qs["pos"]], torch.bfloat16)
+    new_v = bits(host["v"][np.arange(S), qs["pos"]], torch.bfloat16)
+    nblk = p // 128 + 1
+    bs = torch.empty((S, 4, nblk), dtype=torch.float32, device=dev)
+    sel = torch.empty((S, 4, 16), dtype=torch.int32, device=dev)
+    n_sel = torch.empty((S, 4), dtype=torch.int32, device=dev)
+    out = torch.empty((S, 64, 128), dtype=torch.float32, device=dev)
+    ws_att = wsbuf(dims, M.MSA_OP_ATTEND_DECODE, S, p)
+
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_ev)]
+
+    def step(e=None):
+        if e: e[0].record()
+        M.msa_index_append(dims, cache, stream, pos, p, new_idx, new_k, new_v)
+        if e: e[1].record()
+        M.msa_block_scores(dims, cache, idx_q, stream, pos, p, bs)
+        if e: e[2].record()
+        M.msa_topk_blocks(dims, bs, pos, p, sel, n_sel)
+        if e: e[3].record()
+        M.msa_attend_decode(dims, cache, q, stream, pos, p, sel, out, ws_att)
+        if e: e[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # untimed-instrumentation run of the whole step loop (wall clock)
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    # instrumented pass for the per-kernel split
+    for i in range(n_ev):
+        step(ev[i])
+    torch.cuda.synchronize()
+    seg = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(n_ev)])  # ms
+    t_append, t_scan, t_topk, t_att = seg.mean(0)
+    ms_per_step = wall * 1e3 / args.steps
+    value = S / (ms_per_step / 1e3)
+    scan_bytes = S * (p + 1) * 4 * 128 * 4 + S * 4 * 128 * 4 + S * 4 * nblk * 4
+    att_bytes = S * 4 * 16 * 128 * 128 * 2 * 2 + S * 64 * 128 * 2 + S * 64 * 128 * 4 + S * 4 * 16 * 4
+    scan_gbps = scan_bytes / (t_scan * 1e-3) / 1e9
+    att_gbps = att_bytes / (t_att * 1e-3) / 1e9
+    log(f"[bench] decode step {ms_per_step * 1e3:.1f} us: append {t_append * 1e3:.1f} scan {t_scan * 1e3:.1f} "
+        f"topk {t_topk * 1e3:.1f} attend {t_att * 1e3:.1f} us; scan {scan_gbps:.0f} GB/s, attend {att_gbps:.0f} GB/s")
+
+    extra = {
+        "decode_us": {"append": round(t_append * 1e3, 2), "indexer_scan": round(t_scan * 1e3, 2),
+                      "topk": round(t_topk * 1e3, 2), "attend": round(t_att * 1e3, 2)},
+        "indexer_GBps": round(scan_gbps, 1),
+        "indexer_frac_hbm": round(scan_gbps / HBM_PEAK_GBPS, 4),
+        "decode_attend_GBps": round(att_gbps, 1),
+        "decode_attend_frac_hbm": round(att_gbps / HBM_PEAK_GBPS, 4),
+        "decode_path_GBps": round((scan_bytes + att_bytes) / (ms_per_step * 1e-3) / 1e9, 1),
+    }
+
+    # ------------------------------------------------------------------
+    # CPU baseline: the fp64 oracle on the same step's 32 queries
+    # ------------------------------------------------------------------
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+        oracle.lib()
+        t0 = time.perf_counter()
+        _, o_sel, _ = oracle.msa_select(host["idx_k"], qs["stream"], qs["pos"], qs["idx_q"])
+        oracle.sparse_attend(host["k"], host["v"], qs["stream"], qs["pos"], qs["q"], o_sel, unit=128,
+                             scale=W.SCALE)
+        t_cpu = time.perf_counter() - t0
+        cpu_baseline = {"value": round(S / t_cpu, 3), "unit": "queries/s", "cores": min(threads, cores),
+                        "kind": "oracle",
+                        "sample": f"one full step: all {S} decode queries (select + attention) of "
+                                  f"{wl.name}, fp64, {t_cpu:.2f} s wall"}
+        log(f"[bench] oracle: {t_cpu:.2f} s for {S} queries on {min(threads, cores)} threads")
+    del idx_k, k, v, cache
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------
+    # prefill chunk and DSA decode
+    # ------------------------------------------------------------------
+    if not args.no_extra:
+        extra.update(bench_prefill(M, W, torch, dev, bits, tens, wsbuf))
+        torch.cuda.empty_cache()
+        extra.update(bench_dsa(M, W, torch, dev, bits, tens, wsbuf))
+
+    traffic = load_traffic("block_scores_decode_kernel@decode_32x32k", "block_scores.hip")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode_32x32k", "streams": S, "ctx": cap, "query_pos": p,
+                   "groups": 4, "q_heads": 64, "kv_heads": 4, "head_dim": 128, "idx_dim": 128,
+                   "block": 128, "top_k": 16, "kv_dtype": "bf16", "index_cache_dtype": "f32"},
+        "roofline": {"bound": "hbm", "kernel": "block_scores_decode_kernel",
+                     "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(scan_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": scan_bytes},
+        "cpu_baseline": cpu_baseline,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10):
+    wl = W.CONFIGS["prefill_4096_at_32k"]
+    host = W.caches(wl)
+    qs = W.queries(wl)
+    n_q, pos0, cap = wl.n_q, wl.pos[0], wl.cap
+    dims = M.msa_dims(16, W.SCALE)
+    idx_k = tens(host["idx_k"])
+    k = bits(host["k"], torch.bfloat16)
+    v = bits(host["v"], torch.bfloat16)
+    cache = M.make_cache(k=k, v=v, idx_k=idx_k)
+    st = torch.zeros(n_q, dtype=torch.int32, device=dev)
+    ps = torch.arange(pos0, pos0 + n_q, dtype=torch.int32, device=dev)
+    new_idx = tens(host["idx_k"][0, pos0:pos0 + n_q])
+    new_k = bits(host["k"][0, pos0:pos0 + n_q], torch.bfloat16)
+    new_v = bits(host["v"][0, pos0:pos0 + n_q], torch.bfloat16)
+    idx_q = tens(qs["idx_q"])
+    q = bits(qs["q"], torch.bfloat16)
+    sel = torch.empty((n_q, 4, 16), dtype=torch.int32, device=dev)
+    n_sel = torch.empty((n_q, 4), dtype=torch.int32, device=dev)
+    out = torch.empty((n_q, 64, 128), dtype=torch.float32, device=dev)
+    ws_sel = wsbuf(dims, M.MSA_OP_SELECT_PREFILL, n_q, pos0 + n_q - 1)
+    ws_att = wsbuf(dims, M.MSA_OP_ATTEND_PREFILL, n_q, pos0 + n_q - 1)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+
+    def run(e=None):
+        if e: e[0].record()
+        M.msa_index_append(dims, cache, st, ps, pos0 + n_q - 1, new_idx, new_k, new_v)
+        if e: e[1].record()
+        M.msa_select_prefill(dims, cache, idx_q, 0, pos0, sel, n_sel, ws_sel)
+        if e: e[2].record()
+        M.msa_attend_prefill(dims, cache, q, 0, pos0, sel, out, ws_att)
+        if e: e[3].record()
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    for i in range(iters):
+        run(ev[i])
+    torch.cuda.synchronize()
+    seg = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(iters)]).mean(0)
+    total = seg.sum()
+    idx_flop = sum((p + 1) for p in range(pos0, pos0 + n_q)) * 128 * 2 * 4
+    att_flop = 0
+    for p in range(pos0, pos0 + n_q):
+        loc = p // 128
+        keys = 15 * 128 + (p - loc * 128 + 1) if loc >= 15 else p + 1
+        att_flop += keys * 64 * 128 * 4
+    log(f"[bench] prefill: append {seg[0] * 1e3:.1f} select {seg[1] * 1e3:.1f} attend {seg[2] * 1e3:.1f} us "
+        f"-> {n_q / (total * 1e-3):.0f} tok/s")
+    return {
+        "prefill_tok_s": round(n_q / (total * 1e-3), 1),
+        "prefill_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
+                       "attend": round(seg[2] * 1e3, 2)},
+        "prefill_indexer_TFLOPs": round(idx_flop / (seg[1] * 1e-3) / 1e12, 2),
+        "prefill_indexer_frac_fp32_mfma": round(idx_flop / (seg[1] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "prefill_attend_TFLOPs": round(att_flop / (seg[2] * 1e-3) / 1e12, 2),
+        "prefill_attend_frac_bf16_mfma": round(att_flop / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+    }
+
+
+def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20):
+    wl = W.CONFIGS["dsa_16x64k"]
+    host = W.caches(wl)
+    qs = W.queries(wl)
+    S, cap, p = wl.n_stream, wl.cap, wl.max_pos
+    dims = M.dsa_dims(2048, W.SCALE)
+    k = bits(host["k"], torch.bfloat16)
+    v = bits(host["v"], torch.bfloat16)
+    dsa_k = torch.empty((S, cap, 128), dtype=torch.float16, device=dev)
+    cache = M.make_cache(k=k, v=v, dsa_k=dsa_k)
+    # fill the rotated key cache through the append entry point (untimed)
+    st_all = torch.arange(S, dtype=torch.int32, device=dev).repeat_interleave(cap)
+    ps_all = torch.arange(cap, dtype=torch.int32, device=dev).repeat(S)
+    M.dsa_index_append(dims, cache, st_all, ps_all, cap - 1,
+                       bits(host["dsa_k"].reshape(S * cap, 128), torch.float16))
+    stream = tens(qs["stream"])
+    pos = tens(qs["pos"])
+    q_idx = bits(qs["q_idx"], torch.float16)
+    q = bits(qs["q"], torch.bfloat16)
+    new_key = bits(host["dsa_k"][np.arange(S), qs["pos"]], torch.float16)
+    new_k = bits(host["k"][np.arange(S), qs["pos"]], torch.bfloat16)
+    new_v = bits(host["v"][np.arange(S), qs["pos"]], torch.bfloat16)
+    sel = torch.empty((S, 2048), dtype=torch.int32, device=dev)
+    n_sel = torch.empty(S, dtype=torch.int32, device=dev)
+    out = torch.empty((S, 64, 128), dtype=torch.float32, device=dev)
+    ws_sel = wsbuf(dims, M.DSA_OP_SELECT, S, p)
+    ws_att = wsbuf(dims, M.DSA_OP_ATTEND_DECODE, S, p)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+
+    def run(e=None):
+        if e: e[0].record()
+        M.dsa_index_append(dims, cache, stream, pos, p, new_key, new_k, new_v)
+        if e: e[1].record()
+        M.dsa_select(dims, cache, q_idx, stream, pos, p, sel, n_sel, ws_sel)
+        if e: e[2].record()
+        M.dsa_attend_decode(dims, cache, q, stream, pos, p, sel, out, ws_att)
+        if e: e[3].record()
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    for i in range(iters):
+        run(ev[i])
+    torch.cuda.synchronize()
+    seg = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(iters)]).mean(0)
+    scan_bytes = S * cap * 128 * 2
+    att_bytes = S * 4 * 2048 * 128 * 2 * 2 + S * 2048 * 4
+    total = seg.sum()
+    log(f"[bench] dsa: append {seg[0] * 1e3:.1f} select {seg[1] * 1e3:.1f} attend {seg[2] * 1e3:.1f} us")
+    return {
+        "dsa_queries_s": round(S / (total * 1e-3), 1),
+        "dsa_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
+                   "attend": round(seg[2] * 1e3, 2)},
+        "dsa_select_GBps": round(scan_bytes / (seg[1] * 1e-3) / 1e9, 1),
+        "dsa_path_GBps": round((scan_bytes + att_bytes) / (total * 1e-3) / 1e9, 1),
+    }
+
+
+if __name__ == "__main__":
+    main()

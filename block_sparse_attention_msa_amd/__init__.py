@@ -1,0 +1,252 @@
+"""Python binding of the gfx950 MSA hot-path library (libmsa_hip.so).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks dtype / device / contiguity, and forwards raw
+pointers and sizes to the C ABI declared in include/msa.h.  Every step of the
+computation runs in the HIP kernels of that library; there is no CPU or
+PyTorch fallback, and importing the compute functions without the built
+library raises.  Errors from the library are raised as MsaError carrying the
+msa_status code.
+
+Build the library in-tree first:  python -m block_sparse_attention_msa_amd.build
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa_hip.so")
+
+# msa_status
+MSA_OK = 0
+# msa_op
+MSA_OP_SELECT = 1
+MSA_OP_SELECT_PREFILL = 2
+MSA_OP_ATTEND_DECODE = 3
+MSA_OP_ATTEND_PREFILL = 4
+DSA_OP_SELECT = 5
+DSA_OP_ATTEND_DECODE = 6
+
+EXPORTS = (
+    "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",
+    "msa_topk_blocks", "msa_select", "msa_block_scores_prefill", "msa_select_prefill",
+    "msa_attend_decode", "msa_attend_prefill", "dsa_index_append", "dsa_select",
+    "dsa_attend_decode",
+)
+
+
+class MsaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} ({code})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_group", ctypes.c_int32), ("heads_per_group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("top_k", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("idx_k", ctypes.c_void_p), ("dsa_k", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("cap", ctypes.c_int64), ("n_stream", ctypes.c_int32)]
+
+
+def msa_dims(top_k: int = 16, scale: float = 128 ** -0.5) -> Dims:
+    """The MiniMax-M3 sparse-layer geometry: 4 groups x 16 heads, d = 128,
+    indexer d = 128, block 128."""
+    return Dims(4, 16, 128, 128, 128, top_k, scale)
+
+
+def dsa_dims(top_k: int = 2048, scale: float = 128 ** -0.5) -> Dims:
+    """The DSA variant: token-granular selection (block 1) of top_k keys."""
+    return Dims(4, 16, 128, 128, 1, top_k, scale)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_msa_amd.build` "
+                "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        D, C = ctypes.POINTER(Dims), ctypes.POINTER(Cache)
+        L.msa_workspace_bytes.argtypes = [D, ctypes.c_int, I64, I32]
+        L.msa_workspace_bytes.restype = ctypes.c_size_t
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        sig = {
+            "msa_index_append": [D, C, P, P, I64, I32, P, P, P, P],
+            "dsa_index_append": [D, C, P, P, I64, I32, P, P, P, P],
+            "msa_block_scores": [D, C, P, P, P, I64, I32, P, I64, P],
+            "msa_topk_blocks": [D, P, I64, P, I64, I32, P, P, P],
+            "msa_select": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "msa_block_scores_prefill": [D, C, P, I32, I32, I64, P, I64, P],
+            "msa_select_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
+            "msa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "msa_attend_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
+            "dsa_select": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "dsa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().msa_status_string(code).decode()
+
+
+def workspace_bytes(dims: Dims, op: int, n_q: int, max_pos: int) -> int:
+    n = lib().msa_workspace_bytes(ctypes.byref(dims), op, n_q, max_pos)
+    if n == ctypes.c_size_t(-1).value:
+        raise MsaError(-6, "msa_workspace_bytes")
+    return n
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _p(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(hip_stream) -> ctypes.c_void_p:
+    if hip_stream is None:
+        hip_stream = torch.cuda.current_stream()
+    if isinstance(hip_stream, torch.cuda.Stream):
+        hip_stream = hip_stream.cuda_stream
+    return ctypes.c_void_p(int(hip_stream))
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return None, 0
+    return _p(ws, name="ws"), ws.numel() * ws.element_size()
+
+
+def _check(code: int, where: str):
+    if code != MSA_OK:
+        raise MsaError(code, where)
+
+
+def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor] = None,
+               dsa_k: Optional[torch.Tensor] = None) -> Cache:
+    """Cache descriptor over caller-owned tensors (keep them alive):
+    k, v [S][cap][4][128] bf16; idx_k [S][cap][4][128] f32; dsa_k [S][cap][128] f16."""
+    S, cap = k.shape[0], k.shape[1]
+    return Cache(_p(idx_k, torch.float32, "idx_k"), _p(dsa_k, torch.float16, "dsa_k"),
+                 _p(k, torch.bfloat16, "k"), _p(v, torch.bfloat16, "v"), cap, S)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def msa_index_append(dims, cache, stream, pos, max_pos, idx_k_new=None, k_new=None, v_new=None,
+                     hip_stream=None):
+    _check(lib().msa_index_append(ctypes.byref(dims), ctypes.byref(cache), _p(stream, torch.int32),
+                                  _p(pos, torch.int32), pos.numel(), max_pos,
+                                  _p(idx_k_new, torch.float32, "idx_k_new"),
+                                  _p(k_new, torch.bfloat16, "k_new"), _p(v_new, torch.bfloat16, "v_new"),
+                                  _stream(hip_stream)), "msa_index_append")
+
+
+def dsa_index_append(dims, cache, stream, pos, max_pos, key_new, k_new=None, v_new=None,
+                     hip_stream=None):
+    _check(lib().dsa_index_append(ctypes.byref(dims), ctypes.byref(cache), _p(stream, torch.int32),
+                                  _p(pos, torch.int32), pos.numel(), max_pos,
+                                  _p(key_new, torch.float16, "key_new"),
+                                  _p(k_new, torch.bfloat16, "k_new"), _p(v_new, torch.bfloat16, "v_new"),
+                                  _stream(hip_stream)), "dsa_index_append")
+
+
+def msa_block_scores(dims, cache, idx_q, stream, pos, max_pos, bs, hip_stream=None):
+    """bs: [n_q][4][nblk_stride] float32."""
+    _check(lib().msa_block_scores(ctypes.byref(dims), ctypes.byref(cache), _p(idx_q, torch.float32),
+                                  _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                                  _p(bs, torch.float32, "bs"), bs.shape[-1], _stream(hip_stream)),
+           "msa_block_scores")
+
+
+def msa_topk_blocks(dims, bs, pos, max_pos, sel, n_sel, hip_stream=None):
+    _check(lib().msa_topk_blocks(ctypes.byref(dims), _p(bs, torch.float32, "bs"), bs.shape[-1],
+                                 _p(pos, torch.int32), pos.numel(), max_pos, _p(sel, torch.int32),
+                                 _p(n_sel, torch.int32), _stream(hip_stream)), "msa_topk_blocks")
+
+
+def msa_select(dims, cache, idx_q, stream, pos, max_pos, sel, n_sel, ws, hip_stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().msa_select(ctypes.byref(dims), ctypes.byref(cache), _p(idx_q, torch.float32),
+                            _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                            _p(sel, torch.int32), _p(n_sel, torch.int32), wp, wn, _stream(hip_stream)),
+           "msa_select")
+
+
+def msa_block_scores_prefill(dims, cache, idx_q, stream_id, pos0, bs, hip_stream=None):
+    _check(lib().msa_block_scores_prefill(ctypes.byref(dims), ctypes.byref(cache),
+                                          _p(idx_q, torch.float32), stream_id, pos0, idx_q.shape[0],
+                                          _p(bs, torch.float32, "bs"), bs.shape[-1], _stream(hip_stream)),
+           "msa_block_scores_prefill")
+
+
+def msa_select_prefill(dims, cache, idx_q, stream_id, pos0, sel, n_sel, ws, hip_stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().msa_select_prefill(ctypes.byref(dims), ctypes.byref(cache), _p(idx_q, torch.float32),
+                                    stream_id, pos0, idx_q.shape[0], _p(sel, torch.int32),
+                                    _p(n_sel, torch.int32), wp, wn, _stream(hip_stream)),
+           "msa_select_prefill")
+
+
+def msa_attend_decode(dims, cache, q, stream, pos, max_pos, sel, out, ws=None, hip_stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().msa_attend_decode(ctypes.byref(dims), ctypes.byref(cache), _p(q, torch.bfloat16, "q"),
+                                   _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                                   _p(sel, torch.int32), _p(out, torch.float32, "out"), wp, wn,
+                                   _stream(hip_stream)), "msa_attend_decode")
+
+
+def msa_attend_prefill(dims, cache, q, stream_id, pos0, sel, out, ws=None, hip_stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().msa_attend_prefill(ctypes.byref(dims), ctypes.byref(cache), _p(q, torch.bfloat16, "q"),
+                                    stream_id, pos0, q.shape[0], _p(sel, torch.int32),
+                                    _p(out, torch.float32, "out"), wp, wn, _stream(hip_stream)),
+           "msa_attend_prefill")
+
+
+def dsa_select(dims, cache, q_idx, stream, pos, max_pos, sel, n_sel, ws, hip_stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().dsa_select(ctypes.byref(dims), ctypes.byref(cache), _p(q_idx, torch.float16, "q_idx"),
+                            _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                            _p(sel, torch.int32), _p(n_sel, torch.int32), wp, wn, _stream(hip_stream)),
+           "dsa_select")
+
+
+def dsa_attend_decode(dims, cache, q, stream, pos, max_pos, sel, out, ws=None, hip_stream=None):
+    wp, wn = _ws(ws)
+    _check(lib().dsa_attend_decode(ctypes.byref(dims), ctypes.byref(cache), _p(q, torch.bfloat16, "q"),
+                                   _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                                   _p(sel, torch.int32), _p(out, torch.float32, "out"), wp, wn,
+                                   _stream(hip_stream)), "dsa_attend_decode")

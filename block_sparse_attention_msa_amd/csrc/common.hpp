@@ -1,0 +1,160 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of the MSA hot
+// path: vector types, bf16/fp16 conversions, DPP row reductions, MFMA
+// wrappers and the internal launcher declarations used by msa_api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+// ---------------------------------------------------------------------------
+// Fixed geometry of the supported layer (validated on the host).
+// ---------------------------------------------------------------------------
+constexpr int kGroups = 4;        // GQA groups = KV heads = indexer heads
+constexpr int kHeadsPerGroup = 16;
+constexpr int kHeadDim = 128;
+constexpr int kIdxDim = 128;
+constexpr int kBlock = 128;       // MSA key block
+constexpr int kMaxTopkBlocks = 64;
+constexpr int kMaxBlocks = 4096;  // candidates one top-k wave can rank (8 B of LDS each)
+constexpr int kChunk = 32;        // keys per attention step (one MFMA K-depth)
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// DPP reductions inside one 16-lane row (lanes 16r .. 16r + 15).  After the
+// four steps every lane of the row holds the row's result.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<kDppQuadXor1>(x);
+    x += dpp_f32<kDppQuadXor2>(x);
+    x += dpp_f32<kDppRowHalfMirror>(x);
+    x += dpp_f32<kDppRowMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+    return x;
+}
+
+// Cross-row exchange (lane ^ 16, lane ^ 32) through the LDS permute unit.
+__device__ __forceinline__ float xor_lane(float x, int mask) {
+    int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x, int mask) {
+    int lane = __lane_id();
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, static_cast<int>(x)));
+}
+
+// Order-preserving map of a finite or infinite f32 onto u32 (+0 and -0 map
+// to the same key so that equal scores tie).
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+    uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (gfx950 matrix cores).
+//  16x16x32 bf16: lane l holds A[m = l % 16][k-slot 8 * (l / 16) + j] and
+//  B[k-slot 8 * (l / 16) + j][n = l % 16] (j = 0..7), and receives
+//  D[m = 4 * (l / 16) + r][n = l % 16] (r = 0..3).  Only the pairing of A and
+//  B k-slots matters for correctness, so callers may permute the contraction
+//  index as long as both operands use the same permutation.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_16x16x32_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+//  16x16x4 f32: lane l holds A[m = l % 16][k = l / 16], B[k = l / 16][n = l % 16].
+__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace msa
+
+// ---------------------------------------------------------------------------
+// Internal launchers (one translation unit per kernel family).  Each returns
+// hipSuccess or the launch error; arguments were validated by the caller.
+// ---------------------------------------------------------------------------
+namespace msa {
+
+struct CacheView {
+    const float* idx_k;
+    const uint16_t* dsa_k;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t cap;
+};
+
+hipError_t launch_append(float* idx_k, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
+                         const int32_t* stream, const int32_t* pos, int64_t n_new,
+                         const float* idx_k_new, const uint16_t* dsa_key_new,
+                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
+
+hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
+                                      const int32_t* pos, int64_t n_q, int nblk, float* bs,
+                                      int64_t nblk_stride, hipStream_t s);
+
+hipError_t launch_block_scores_prefill(const CacheView& c, const float* idx_q, int32_t stream,
+                                       int32_t pos0, int64_t n_q, int nblk, float* bs,
+                                       int64_t nblk_stride, hipStream_t s);
+
+hipError_t launch_topk_blocks(const float* bs, int64_t nblk_stride, const int32_t* pos,
+                              int64_t n_q, int nblk, int top_k, int32_t* sel, int32_t* n_sel,
+                              hipStream_t s);
+// Same, for the consecutive positions pos0 .. pos0 + n_q - 1.
+hipError_t launch_topk_blocks_range(const float* bs, int64_t nblk_stride, int32_t pos0, int64_t n_q,
+                                    int nblk, int top_k, int32_t* sel, int32_t* n_sel, hipStream_t s);
+
+// Attention over selected keys.  Token t of entry e of (query i, group g):
+//   MSA (unit = 128): entry ids are blocks, keys id * 128 + 0..127;
+//   DSA (unit = 1):   entry ids are tokens shared by all groups.
+struct AttendArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t cap;
+    const uint16_t* q;
+    const int32_t* stream;   // per query, or NULL with stream0 for prefill
+    const int32_t* pos;      // per query, or NULL with pos0 for prefill
+    int32_t stream0;
+    int32_t pos0;
+    int64_t n_q;
+    const int32_t* sel;
+    int sel_len;             // entries per (query, group)
+    int sel_g_stride;        // sel_len (MSA) or 0 (DSA, shared list)
+    int unit;                // 128 or 1
+    float scale;
+    float* out;
+    void* ws;
+};
+int attend_num_splits(int64_t n_q, int sel_len, int unit);
+size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
+hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,
+                             const int32_t* stream, const int32_t* pos, int64_t n_q,
+                             int32_t max_pos, int top_k, int32_t* sel, int32_t* n_sel,
+                             void* ws, hipStream_t s);
+
+}  // namespace msa

@@ -1,0 +1,191 @@
+// dsa_select.hip -- DSA lightning-indexer token selection.
+//
+// "deepseek2 : GLM-DSA sparse attention (lightning indexer), --dsa off by
+// default", What this does: each query is scored against every (Hadamard-
+// rotated, F16-cached) indexer key and keeps its top-k highest-scoring keys.
+// Readings: one score per (query, key) = fp16 dot product accumulated in f32;
+// keys j <= pos only; k = min(top_k, pos + 1); ties to the lower token id.
+//
+// Kernel 1 streams the fp16 key cache once with 128-bit loads (a 16-lane DPP
+// row per 256-byte key row, v_dot2 on fp16 pairs) and writes the f32 scores.
+// Kernel 2 is an exact radix select on order-preserving u32 keys: four 8-bit
+// digit passes find the k-th largest key T, then an order-preserving
+// compaction writes every key > T and the lowest-id keys == T, so the output
+// is already in ascending id order and unique.
+#include "common.hpp"
+
+namespace msa {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kScoreKeysPerWg = 1024;
+constexpr int kScoreUnroll = 8;
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ float dot8_f16(const u32x4& q, const u32x4& k) {
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q[e]), __builtin_bit_cast(half2_t, k[e]), d,
+                                   false);
+    return d;
+}
+
+__global__ __launch_bounds__(256) void dsa_score_kernel(const uint16_t* __restrict__ dsa_k, int64_t cap,
+                                                        const uint16_t* __restrict__ q_idx,
+                                                        const int32_t* __restrict__ q_stream,
+                                                        const int32_t* __restrict__ q_pos,
+                                                        float* __restrict__ scores, int64_t stride) {
+    const int64_t i = blockIdx.y;
+    const int p = q_pos[i];
+    const int j_wg = blockIdx.x * kScoreKeysPerWg;
+    if (j_wg > p) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int r = lane >> 4;     // key row within a group of four
+    const int c = lane & 15;     // 16-byte column (8 fp16 dims)
+    const u32x4 q = *reinterpret_cast<const u32x4*>(q_idx + i * kIdxDim + 8 * c);
+    const uint16_t* base = dsa_k + static_cast<int64_t>(q_stream[i]) * cap * kIdxDim;
+    float* out = scores + i * stride;
+    const int j_begin = j_wg + wave * (kScoreKeysPerWg / 4);
+    const int j_end = min(j_begin + kScoreKeysPerWg / 4, p + 1);
+    for (int j0 = j_begin; j0 < j_end; j0 += 4 * kScoreUnroll) {
+        u32x4 kr[kScoreUnroll];
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u) {
+            int j = j0 + 4 * u + r;
+            j = min(j, p);                                   // rows past p are never written
+            kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(j) * kIdxDim + 8 * c));
+        }
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u) {
+            const float d = row16_sum(dot8_f16(q, kr[u]));
+            const int j = j0 + 4 * u + r;
+            if (c == 0 && j < j_end) out[j] = d;
+        }
+    }
+}
+
+// Inclusive prefix sum over the 1024 threads of the workgroup.
+__device__ int block_inclusive_scan(int v, int* wave_sums) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) wave_sums[wave] = v;
+    __syncthreads();
+    if (wave == 0) {
+        int sum = lane < kSelThreads / 64 ? wave_sums[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < kSelThreads / 64; o <<= 1) {
+            const int y = __shfl_up(sum, o, 64);
+            if (lane >= o) sum += y;
+        }
+        if (lane < kSelThreads / 64) wave_sums[lane] = sum;
+    }
+    __syncthreads();
+    if (wave > 0) v += wave_sums[wave - 1];
+    __syncthreads();
+    return v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __restrict__ scores,
+                                                               int64_t stride,
+                                                               const int32_t* __restrict__ q_pos,
+                                                               int top_k, int32_t* __restrict__ sel,
+                                                               int32_t* __restrict__ n_sel) {
+    __shared__ int hist[256];
+    __shared__ int wave_sums[kSelThreads / 64];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_remaining;
+    const int64_t i = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = q_pos[i] + 1;
+    const float* t = scores + i * stride;
+    int32_t* out = sel + i * top_k;
+    if (n <= top_k) {                                   // every visible key is kept
+        for (int j = tid; j < top_k; j += kSelThreads) out[j] = j < n ? j : -1;
+        if (tid == 0) n_sel[i] = n;
+        return;
+    }
+    // ---- radix select of the k-th largest key (k = top_k here)
+    uint32_t prefix = 0, mask = 0;
+    int remaining = top_k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += kSelThreads) {
+            const uint32_t key = ordered_key(t[j]);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
+        __syncthreads();
+        // digits from the top: thread d' counts bin 255 - d'
+        const int cnt = tid < 256 ? hist[255 - tid] : 0;
+        const int incl = block_inclusive_scan(cnt, wave_sums);
+        if (tid < 256 && incl >= remaining && incl - cnt < remaining) {
+            s_digit = 255u - tid;
+            s_remaining = remaining - (incl - cnt);
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        mask |= 255u << shift;
+        remaining = s_remaining;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;          // the k-th largest key; `remaining` keys equal to it are kept
+    // ---- order-preserving compaction over contiguous per-thread ranges
+    const int R = (n + kSelThreads - 1) / kSelThreads;
+    const int j0 = min(tid * R, n), j1 = min(j0 + R, n);
+    int n_gt = 0, n_eq = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t key = ordered_key(t[j]);
+        n_gt += key > T;
+        n_eq += key == T;
+    }
+    const int eq_before = block_inclusive_scan(n_eq, wave_sums) - n_eq;
+    const int take_eq = max(0, min(n_eq, remaining - eq_before));
+    const int mine = n_gt + take_eq;
+    int w = block_inclusive_scan(mine, wave_sums) - mine;
+    int taken = 0;
+    for (int j = j0; j < j1; ++j) {
+        const uint32_t key = ordered_key(t[j]);
+        if (key > T || (key == T && taken < take_eq)) {
+            if (w < top_k) out[w] = j;     // exactly top_k keys qualify; the bound is defensive
+            ++w;
+            taken += key == T;
+        }
+    }
+    if (tid == 0) n_sel[i] = top_k;
+}
+
+int64_t score_stride(int32_t max_pos) {
+    return ((static_cast<int64_t>(max_pos) + 1 + 63) / 64) * 64;
+}
+
+}  // namespace
+
+size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos) {
+    return static_cast<size_t>(n_q) * score_stride(max_pos) * sizeof(float);
+}
+
+hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,
+                             const int32_t* stream, const int32_t* pos, int64_t n_q,
+                             int32_t max_pos, int top_k, int32_t* sel, int32_t* n_sel, void* ws,
+                             hipStream_t s) {
+    float* scores = static_cast<float*>(ws);
+    const int64_t stride = score_stride(max_pos);
+    const unsigned nx = static_cast<unsigned>((max_pos + kScoreKeysPerWg) / kScoreKeysPerWg);
+    hipLaunchKernelGGL(dsa_score_kernel, dim3(nx, static_cast<unsigned>(n_q)), dim3(256), 0, s, dsa_k,
+                       cap, q_idx, stream, pos, scores, stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dsa_topk_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kSelThreads), 0, s, scores,
+                       stride, pos, top_k, sel, n_sel);
+    return hipGetLastError();
+}
+
+}  // namespace msa

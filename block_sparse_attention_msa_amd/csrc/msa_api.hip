@@ -1,0 +1,312 @@
+// msa_api.hip -- the extern "C" entry points declared in include/msa.h:
+// host-side validation (everything is checked before anything is launched),
+// workspace sizing and kernel dispatch.  No allocation, no synchronisation,
+// no state between calls.
+#include "../../include/msa.h"
+#include "common.hpp"
+
+namespace {
+
+using msa::kBlock;
+using msa::kGroups;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum class Mode { Msa, Dsa };
+
+msa_status check_dims(const msa_dims* d, Mode mode) {
+    if (!d) return MSA_ERR_NULL_ARG;
+    if (d->n_group != msa::kGroups || d->heads_per_group != msa::kHeadsPerGroup ||
+        d->head_dim != msa::kHeadDim || d->idx_dim != msa::kIdxDim)
+        return MSA_ERR_UNSUPPORTED;
+    if (!(d->scale > 0.f) || !(d->scale < 1e30f)) return MSA_ERR_UNSUPPORTED;
+    if (mode == Mode::Msa) {
+        if (d->block != kBlock || d->top_k < 1 || d->top_k > msa::kMaxTopkBlocks) return MSA_ERR_UNSUPPORTED;
+    } else {
+        if (d->block != 1 || d->top_k < 1 || d->top_k > 4096) return MSA_ERR_UNSUPPORTED;
+    }
+    return MSA_OK;
+}
+
+msa_status check_cache(const msa_cache* c) {
+    if (!c) return MSA_ERR_NULL_ARG;
+    if (c->cap < 1 || c->n_stream < 1) return MSA_ERR_BAD_SHAPE;
+    if (c->cap > (int64_t(1) << 31) - 1) return MSA_ERR_UNSUPPORTED;   // positions are int32
+    return MSA_OK;
+}
+
+// n_q: 0 is an empty call, negative is a shape error; max_pos must lie in the cache.
+msa_status check_count_pos(int64_t n, int32_t max_pos, const msa_cache* c) {
+    if (n < 0) return MSA_ERR_BAD_SHAPE;
+    if (n > (int64_t(1) << 31) - 1) return MSA_ERR_UNSUPPORTED;
+    if (max_pos < 0 || static_cast<int64_t>(max_pos) >= c->cap) return MSA_ERR_OUT_OF_RANGE;
+    return MSA_OK;
+}
+
+msa_status check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps)
+        if (!p) return MSA_ERR_NULL_ARG;
+    for (const void* p : ps)
+        if (!aligned16(p)) return MSA_ERR_MISALIGNED;
+    return MSA_OK;
+}
+
+msa_status hip_status(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_HIP; }
+
+#define MSA_TRY(expr)                    \
+    do {                                 \
+        const msa_status _st = (expr);   \
+        if (_st != MSA_OK) return _st;   \
+    } while (0)
+
+int nblk_of(int32_t max_pos) { return max_pos / kBlock + 1; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t select_ws(int64_t n_q, int32_t max_pos) {
+    return align256(static_cast<size_t>(n_q) * kGroups * nblk_of(max_pos) * sizeof(float));
+}
+
+msa::CacheView view(const msa_cache* c) {
+    return msa::CacheView{c->idx_k, c->dsa_k, c->k, c->v, c->cap};
+}
+
+msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
+                       const int32_t* d_pos, int64_t n_new, int32_t max_pos, const float* d_idx_k_new,
+                       const uint16_t* d_key_new, const uint16_t* d_k_new, const uint16_t* d_v_new,
+                       void* hip_stream) {
+    MSA_TRY(check_dims(dims, mode));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_new, max_pos, cache));
+    MSA_TRY(check_ptrs({d_stream, d_pos}));
+    if (d_idx_k_new) MSA_TRY(check_ptrs({d_idx_k_new, cache->idx_k}));
+    if (d_key_new) MSA_TRY(check_ptrs({d_key_new, cache->dsa_k}));
+    if (d_k_new) MSA_TRY(check_ptrs({d_k_new, cache->k}));
+    if (d_v_new) MSA_TRY(check_ptrs({d_v_new, cache->v}));
+    if (n_new == 0) return MSA_OK;
+    return hip_status(msa::launch_append(cache->idx_k, cache->dsa_k, cache->k, cache->v, cache->cap,
+                                         d_stream, d_pos, n_new, d_idx_k_new, d_key_new, d_k_new,
+                                         d_v_new, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(msa_status s) {
+    switch (s) {
+        case MSA_OK: return "MSA_OK";
+        case MSA_ERR_NULL_ARG: return "MSA_ERR_NULL_ARG: a required pointer is NULL";
+        case MSA_ERR_BAD_SHAPE: return "MSA_ERR_BAD_SHAPE: negative count or empty cache";
+        case MSA_ERR_OUT_OF_RANGE: return "MSA_ERR_OUT_OF_RANGE: position or stream outside the cache";
+        case MSA_ERR_MISALIGNED: return "MSA_ERR_MISALIGNED: device pointer not 16-byte aligned";
+        case MSA_ERR_WORKSPACE_TOO_SMALL: return "MSA_ERR_WORKSPACE_TOO_SMALL";
+        case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: geometry outside the supported set";
+        case MSA_ERR_HIP: return "MSA_ERR_HIP: a kernel launch failed";
+    }
+    return "unknown msa_status";
+}
+
+size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t max_pos) {
+    const size_t bad = static_cast<size_t>(-1);
+    if (n_q < 0 || max_pos < 0) return bad;
+    const bool dsa = op == DSA_OP_SELECT || op == DSA_OP_ATTEND_DECODE;
+    if (check_dims(dims, dsa ? Mode::Dsa : Mode::Msa) != MSA_OK) return bad;
+    switch (op) {
+        case MSA_OP_SELECT:
+        case MSA_OP_SELECT_PREFILL:
+            if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;
+            return select_ws(n_q, max_pos);
+        case MSA_OP_ATTEND_DECODE:
+        case MSA_OP_ATTEND_PREFILL:
+            return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
+        case DSA_OP_SELECT:
+            return align256(msa::dsa_select_ws_bytes(n_q, max_pos));
+        case DSA_OP_ATTEND_DECODE:
+            return align256(msa::attend_ws_bytes(n_q, dims->top_k, 1));
+    }
+    return bad;
+}
+
+msa_status msa_index_append(const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
+                            const int32_t* d_pos, int64_t n_new, int32_t max_pos,
+                            const float* d_idx_k_new, const uint16_t* d_k_new,
+                            const uint16_t* d_v_new, void* hip_stream) {
+    return append_impl(Mode::Msa, dims, cache, d_stream, d_pos, n_new, max_pos, d_idx_k_new, nullptr,
+                       d_k_new, d_v_new, hip_stream);
+}
+
+msa_status dsa_index_append(const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
+                            const int32_t* d_pos, int64_t n_new, int32_t max_pos,
+                            const uint16_t* d_key_new, const uint16_t* d_k_new,
+                            const uint16_t* d_v_new, void* hip_stream) {
+    return append_impl(Mode::Dsa, dims, cache, d_stream, d_pos, n_new, max_pos, nullptr, d_key_new,
+                       d_k_new, d_v_new, hip_stream);
+}
+
+msa_status msa_block_scores(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                            const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                            int32_t max_pos, float* d_bs, int64_t nblk_stride, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_stream, d_pos, d_bs}));
+    if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
+    if (n_q == 0) return MSA_OK;
+    return hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q,
+                                                      nblk_of(max_pos), d_bs, nblk_stride,
+                                                      static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status msa_topk_blocks(const msa_dims* dims, const float* d_bs, int64_t nblk_stride,
+                           const int32_t* d_pos, int64_t n_q, int32_t max_pos, int32_t* d_sel,
+                           int32_t* d_n_sel, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (max_pos < 0) return MSA_ERR_OUT_OF_RANGE;
+    MSA_TRY(check_ptrs({d_bs, d_pos, d_sel, d_n_sel}));
+    if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
+    if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
+    if (n_q == 0) return MSA_OK;
+    return hip_status(msa::launch_topk_blocks(d_bs, nblk_stride, d_pos, n_q, nblk_of(max_pos), dims->top_k,
+                                              d_sel, d_n_sel, static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                      const int32_t* d_stream, const int32_t* d_pos, int64_t n_q, int32_t max_pos,
+                      int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes,
+                      void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
+    if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
+    if (n_q == 0) return MSA_OK;
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < select_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    float* bs = static_cast<float*>(d_ws);
+    const int nblk = nblk_of(max_pos);
+    MSA_TRY(hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q, nblk,
+                                                       bs, nblk, s)));
+    return hip_status(msa::launch_topk_blocks(bs, nblk, d_pos, n_q, nblk, dims->top_k, d_sel, d_n_sel, s));
+}
+
+msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                                    int32_t stream, int32_t pos0, int64_t n_q, float* d_bs,
+                                    int64_t nblk_stride, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
+        return MSA_ERR_OUT_OF_RANGE;
+    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_bs}));
+    if (n_q == 0) return MSA_OK;
+    const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
+    if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
+    return hip_status(msa::launch_block_scores_prefill(view(cache), d_idx_q, stream, pos0, n_q,
+                                                       nblk_of(max_pos), d_bs, nblk_stride,
+                                                       static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                              int32_t stream, int32_t pos0, int64_t n_q, int32_t* d_sel,
+                              int32_t* d_n_sel, void* d_ws, size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
+        return MSA_ERR_OUT_OF_RANGE;
+    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_sel, d_n_sel}));
+    if (n_q == 0) return MSA_OK;
+    const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
+    if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < select_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    // The top-k kernel reads each query's position from device memory; the
+    // prefill positions pos0 + i are materialised after the block scores.
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int nblk = nblk_of(max_pos);
+    float* bs = static_cast<float*>(d_ws);
+    MSA_TRY(hip_status(msa::launch_block_scores_prefill(view(cache), d_idx_q, stream, pos0, n_q, nblk,
+                                                        bs, nblk, s)));
+    return hip_status(msa::launch_topk_blocks_range(bs, nblk, pos0, n_q, nblk, dims->top_k, d_sel,
+                                                    d_n_sel, s));
+}
+
+msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
+                             const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                             int32_t max_pos, const int32_t* d_sel, float* d_out, void* d_ws,
+                             size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_stream, d_pos, d_sel, d_out}));
+    if (n_q == 0) return MSA_OK;
+    const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, kBlock);
+    if (need) {
+        MSA_TRY(check_ptrs({d_ws}));
+        if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, 0, 0, n_q, d_sel,
+                      dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws};
+    return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
+                              int32_t stream, int32_t pos0, int64_t n_q, const int32_t* d_sel,
+                              float* d_out, void* d_ws, size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
+        return MSA_ERR_OUT_OF_RANGE;
+    MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out}));
+    if (n_q == 0) return MSA_OK;
+    const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, kBlock);
+    if (need) {
+        MSA_TRY(check_ptrs({d_ws}));
+        if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, nullptr, nullptr, stream, pos0, n_q, d_sel,
+                      dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws};
+    return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q_idx,
+                      const int32_t* d_stream, const int32_t* d_pos, int64_t n_q, int32_t max_pos,
+                      int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes,
+                      void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Dsa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    MSA_TRY(check_ptrs({cache->dsa_k, d_q_idx, d_stream, d_pos, d_sel, d_n_sel}));
+    if (n_q > 65535) return MSA_ERR_UNSUPPORTED;
+    if (n_q == 0) return MSA_OK;
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < msa::dsa_select_ws_bytes(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(msa::launch_dsa_select(cache->dsa_k, cache->cap, d_q_idx, d_stream, d_pos, n_q,
+                                             max_pos, dims->top_k, d_sel, d_n_sel, d_ws,
+                                             static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
+                             const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                             int32_t max_pos, const int32_t* d_sel, float* d_out, void* d_ws,
+                             size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Dsa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_stream, d_pos, d_sel, d_out}));
+    if (n_q == 0) return MSA_OK;
+    const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, 1);
+    if (need) {
+        MSA_TRY(check_ptrs({d_ws}));
+        if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, 0, 0, n_q, d_sel,
+                      dims->top_k, 0, 1, dims->scale, d_out, d_ws};
+    return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,278 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MiniMax Sparse Attention hot path.
+ *
+ * What is computed (web pages cited by title and section):
+ *  - "Add MiniMax-M3 (MSA: MiniMax Sparse Attention) support", llama.cpp pull
+ *    request 24908 [MSA-PR]:
+ *      Overview: a per-GQA-group indexer scores the visible causal context,
+ *      the scores are max-pooled into 128-token key blocks, the top-16 blocks
+ *      are selected with the query's own (local) block always included, and
+ *      attention runs over the selected 16 x 128 = 2048 keys only.
+ *      Implementation: block scores bs = maxpool_128(idx_q . idx_k^T + causal
+ *      mask) plus a large positive bias on the local block, ranked together
+ *      for top-k; one indexer head per group, shared by the group's 16 query
+ *      heads; prefill and decode share these semantics; the index keys live in
+ *      their own per-layer F32 cache beside the K/V cache; per-stream caches
+ *      are slot-anchored (slot == position).
+ *  - llama.cpp compare page b10146, MSA commit log [MSA-LOG]: F32 index cache
+ *    by default, F32 indexer score accumulation, unified selection for
+ *    prefill and decode, K/V in F16/BF16.
+ *  - "deepseek2 : GLM-DSA sparse attention (lightning indexer), --dsa off by
+ *    default", ik_llama.cpp pull request 2045 [DSA-PR], "What this does":
+ *    indexer keys are Hadamard-rotated and cached as F16; each query keeps
+ *    its top-k highest-scoring keys and the rest are masked out.
+ *
+ * Readings where the pages leave a step open: a key at slot j is visible to a
+ * query at position p iff j <= p; a block's score is the max over its visible
+ * keys; the local-block bias is "rank first"; ties rank the lower block (or
+ * token) id first; query head h uses group h / heads_per_group; the softmax
+ * scale is dims->scale with no sink and no soft-cap; DSA rotates keys with
+ * the orthonormal Sylvester Hadamard transform and rounds once to fp16.
+ *
+ * Conventions common to every entry point:
+ *  - All pointers named d_* are DEVICE pointers on the current HIP device;
+ *    the caller owns every byte of device memory (caches, inputs, outputs,
+ *    workspace).  The library keeps no state between calls, allocates
+ *    nothing, never synchronises, and enqueues work only on `hip_stream`
+ *    (a hipStream_t; NULL means the legacy default stream).  Outputs are
+ *    valid once the stream has completed.
+ *  - bf16 and fp16 values are passed as uint16_t bit patterns.
+ *  - Cache layout (token-major: one row per (token, KV head)):
+ *      idx_k [n_stream][cap][n_group][idx_dim] f32   (MSA index keys)
+ *      dsa_k [n_stream][cap][idx_dim]          fp16  (DSA rotated keys)
+ *      k, v  [n_stream][cap][n_group][head_dim] bf16
+ *  - Every call validates its host-visible arguments BEFORE launching
+ *    anything; on any error nothing is launched and a negative msa_status is
+ *    returned.  Device-side preconditions (documented per call, not
+ *    checked): every stream id is < cache->n_stream, every position is in
+ *    [0, max_pos], and the keys 0..pos of a query's stream have been
+ *    appended.  No exception crosses this ABI.
+ *  - Device pointers must be 16-byte aligned (128-bit vector access).
+ *  - n_q == 0 (or n_new == 0) is a valid empty call: MSA_OK, nothing runs.
+ *  - Supported geometry: n_group 4, heads_per_group 16, head_dim 128,
+ *    idx_dim 128; MSA: block 128, 1 <= top_k <= 64; DSA: block 1,
+ *    1 <= top_k <= 4096.  Anything else returns MSA_ERR_UNSUPPORTED.
+ *  - Results are deterministic: no floating-point atomics; split partial
+ *    results are combined in a fixed order.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define MSA_API __attribute__((visibility("default")))
+#else
+#define MSA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_NULL_ARG = -1,            /* a required pointer is NULL */
+    MSA_ERR_BAD_SHAPE = -2,           /* negative count, cap < 1, n_stream < 1, bad stride */
+    MSA_ERR_OUT_OF_RANGE = -3,        /* max_pos / pos0 / stream outside the cache */
+    MSA_ERR_MISALIGNED = -4,          /* a device pointer is not 16-byte aligned */
+    MSA_ERR_WORKSPACE_TOO_SMALL = -5, /* ws_bytes < msa_workspace_bytes(...) */
+    MSA_ERR_UNSUPPORTED = -6,         /* geometry outside the supported set */
+    MSA_ERR_HIP = -7                  /* a kernel launch failed */
+} msa_status;
+
+/* Head geometry of one sparse attention layer. */
+typedef struct msa_dims {
+    int32_t n_group;          /* GQA groups = KV heads = indexer heads (4) */
+    int32_t heads_per_group;  /* query heads per group (16) */
+    int32_t head_dim;         /* Q/K/V head dim (128) */
+    int32_t idx_dim;          /* indexer dim (128) */
+    int32_t block;            /* key block for MSA (128); 1 for DSA token ids */
+    int32_t top_k;            /* blocks (MSA, 16) or tokens (DSA, 2048) kept */
+    float scale;              /* softmax scale (1/sqrt(head_dim)) */
+} msa_dims;
+
+/* Per-layer caches (device memory owned by the caller). */
+typedef struct msa_cache {
+    float* idx_k;       /* MSA index keys, or NULL when unused */
+    uint16_t* dsa_k;    /* DSA rotated indexer keys (fp16), or NULL */
+    uint16_t* k;        /* bf16 keys */
+    uint16_t* v;        /* bf16 values (not transposed) */
+    int64_t cap;        /* slots per stream */
+    int32_t n_stream;   /* independent streams (sequences) */
+} msa_cache;
+
+/* Operations whose workspace size can be queried. */
+typedef enum msa_op {
+    MSA_OP_SELECT = 1,          /* msa_select */
+    MSA_OP_SELECT_PREFILL = 2,  /* msa_select_prefill */
+    MSA_OP_ATTEND_DECODE = 3,   /* msa_attend_decode */
+    MSA_OP_ATTEND_PREFILL = 4,  /* msa_attend_prefill */
+    DSA_OP_SELECT = 5,          /* dsa_select */
+    DSA_OP_ATTEND_DECODE = 6    /* dsa_attend_decode */
+} msa_op;
+
+/* Bytes of workspace `op` needs for n_q queries whose positions are all
+ * <= max_pos (msa_select_prefill / msa_attend_prefill: max_pos = pos0 +
+ * n_q - 1).  Returns 0 when the op needs no workspace and (size_t)-1 for an
+ * unsupported geometry, op or size. */
+MSA_API size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t max_pos);
+
+/* Human-readable name of a status code (static storage). */
+MSA_API const char* msa_status_string(msa_status s);
+
+/*
+ * [MSA-PR] Implementation (per-layer F32 index-key cache beside K/V);
+ * [DSA-PR] "What this does" (recent index keys must be written before the
+ * same step's queries score).
+ * Writes n_new token rows: row i goes to slot d_pos[i] of stream
+ * d_stream[i] in cache->idx_k (from d_idx_k_new [n_new][n_group][idx_dim]
+ * f32), cache->k and cache->v (from d_k_new / d_v_new [n_new][n_group]
+ * [head_dim] bf16).  Any of the three sources may be NULL to skip that
+ * cache; a non-NULL source needs its cache pointer.  Exact copies.
+ * Device preconditions: d_pos[i] <= max_pos < cache->cap; the (stream, pos)
+ * pairs are distinct.
+ */
+MSA_API msa_status msa_index_append(const msa_dims* dims, const msa_cache* cache,
+                            const int32_t* d_stream, const int32_t* d_pos, int64_t n_new,
+                            int32_t max_pos, const float* d_idx_k_new,
+                            const uint16_t* d_k_new, const uint16_t* d_v_new,
+                            void* hip_stream);
+
+/*
+ * [MSA-PR] Implementation: bs = maxpool_128(idx_q . idx_k^T + causal mask),
+ * per group, F32 accumulation ([MSA-LOG]).
+ * For each query i (stream d_stream[i], position d_pos[i]) and group g
+ * writes d_bs[(i * n_group + g) * nblk_stride + b] for b = 0 ..
+ * max_pos / block: the max over keys j in [block*b, block*b + block) with
+ * j <= pos of sum_d idx_q[i][g][d] * idx_k[stream][j][g][d] (f32), and -inf
+ * for blocks past pos / block.  No bias is added (the local block is forced
+ * by the selection).  Requires nblk_stride >= max_pos / block + 1.  One
+ * wavefront-reduced dot product per key, streamed with 128-bit loads.
+ */
+MSA_API msa_status msa_block_scores(const msa_dims* dims, const msa_cache* cache,
+                            const float* d_idx_q, const int32_t* d_stream,
+                            const int32_t* d_pos, int64_t n_q, int32_t max_pos,
+                            float* d_bs, int64_t nblk_stride, void* hip_stream);
+
+/*
+ * [MSA-PR] Overview and Implementation (top-k over bs plus the local-force
+ * bias; k = min(indexer_top_k, nblk) per the review thread).
+ * From block scores laid out as msa_block_scores writes them, selects per
+ * (query, group) k = min(top_k, pos / block + 1) blocks: the local block
+ * pos / block first, then the highest scores, ties to the lower block id.
+ * Writes d_sel[(i * n_group + g) * top_k + t] in ascending id order, padded
+ * with -1, and d_n_sel[i * n_group + g] = k.  Only blocks <= pos / block are
+ * candidates.  Requires max_pos / block + 1 <= 4096.
+ */
+MSA_API msa_status msa_topk_blocks(const msa_dims* dims, const float* d_bs, int64_t nblk_stride,
+                           const int32_t* d_pos, int64_t n_q, int32_t max_pos,
+                           int32_t* d_sel, int32_t* d_n_sel, void* hip_stream);
+
+/*
+ * msa_block_scores followed by msa_topk_blocks, with the block scores kept
+ * in the workspace (size: msa_workspace_bytes(dims, MSA_OP_SELECT, n_q,
+ * max_pos)).  Decode form: any mix of streams and positions.
+ *   d_idx_q [n_q][n_group][idx_dim] f32; d_sel [n_q][n_group][top_k] i32;
+ *   d_n_sel [n_q][n_group] i32.
+ */
+MSA_API msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                      const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                      int32_t max_pos, int32_t* d_sel, int32_t* d_n_sel,
+                      void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Prefill form of msa_block_scores ([MSA-PR] Implementation, batch path;
+ * [MSA-LOG] unified selection semantics): n_q consecutive queries at
+ * positions pos0 .. pos0 + n_q - 1 of stream `stream` (host values), scored
+ * with matrix-core tiles.  Same output layout and values as
+ * msa_block_scores (f32 sums, summation order differs).
+ */
+MSA_API msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache,
+                                    const float* d_idx_q, int32_t stream, int32_t pos0,
+                                    int64_t n_q, float* d_bs, int64_t nblk_stride,
+                                    void* hip_stream);
+
+/* msa_block_scores_prefill followed by msa_topk_blocks (workspace:
+ * MSA_OP_SELECT_PREFILL with max_pos = pos0 + n_q - 1). */
+MSA_API msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cache,
+                              const float* d_idx_q, int32_t stream, int32_t pos0, int64_t n_q,
+                              int32_t* d_sel, int32_t* d_n_sel,
+                              void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * [MSA-PR] Overview and Implementation, decode path: each of a group's
+ * query heads attends over only the keys of the group's selected blocks.
+ * For query i, head h (group g = h / heads_per_group):
+ *   out[i][h][:] = sum_{j in J} softmax_j(scale * q[i][h] . k[stream][j][g])
+ *                  * v[stream][j][g][:]
+ * with J = { j : j / block in sel[i][g][0..top_k), j <= pos } (ids < 0 are
+ * padding).  Keys are read from the cache by block id (no gather); the
+ * selected blocks are split across workgroups and their partial softmax
+ * states are merged in a fixed order.
+ *   d_q [n_q][n_group*heads_per_group][head_dim] bf16;
+ *   d_sel as msa_select writes it; d_out [n_q][n_group*heads_per_group]
+ *   [head_dim] f32.  Workspace: MSA_OP_ATTEND_DECODE.
+ * Device precondition: at least one selected key per (query, group) (the
+ * local block always provides key pos's block start).
+ */
+MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
+                             const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                             int32_t max_pos, const int32_t* d_sel, float* d_out,
+                             void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * Prefill form of msa_attend_decode ([MSA-PR] Implementation, batch path:
+ * block-level mask of the selection combined with the causal mask): n_q
+ * consecutive queries at positions pos0 .. pos0 + n_q - 1 of `stream`.
+ * Same arguments and output as msa_attend_decode.  Workspace:
+ * MSA_OP_ATTEND_PREFILL.
+ */
+MSA_API msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
+                              int32_t stream, int32_t pos0, int64_t n_q, const int32_t* d_sel,
+                              float* d_out, void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * [DSA-PR] "What this does": the indexer keys are Hadamard-rotated and kept
+ * in a persistent per-layer F16 cache.
+ * Row i: dsa_k[stream][pos] = fp16_rne(H x / sqrt(idx_dim)) where x is
+ * d_key_new[i] ([n_new][idx_dim] fp16) and H the Sylvester Hadamard matrix
+ * (H[a][b] = (-1)^popcount(a & b)); the transform is exact in fp64 and
+ * rounded once (round to nearest, ties to even).  d_k_new / d_v_new (may be
+ * NULL) are copied into cache->k / cache->v as in msa_index_append.
+ */
+MSA_API msa_status dsa_index_append(const msa_dims* dims, const msa_cache* cache,
+                            const int32_t* d_stream, const int32_t* d_pos, int64_t n_new,
+                            int32_t max_pos, const uint16_t* d_key_new,
+                            const uint16_t* d_k_new, const uint16_t* d_v_new,
+                            void* hip_stream);
+
+/*
+ * [DSA-PR] "What this does": one score per (query, key),
+ * t[j] = sum_d q_idx[i][d] * dsa_k[stream][j][d] (fp16 products, f32 sums)
+ * for j <= pos; keeps k = min(top_k, pos + 1) keys with the largest t, ties
+ * to the lower token id, no local forcing.  Writes d_sel [n_q][top_k]
+ * ascending token ids padded with -1 and d_n_sel [n_q] = k.
+ *   d_q_idx [n_q][idx_dim] fp16.  Workspace: DSA_OP_SELECT.
+ */
+MSA_API msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q_idx,
+                      const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                      int32_t max_pos, int32_t* d_sel, int32_t* d_n_sel,
+                      void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * [DSA-PR] "What this does": attention over the kept keys only.  As
+ * msa_attend_decode, but d_sel [n_q][top_k] holds token ids shared by all
+ * groups (dims->block must be 1).  Workspace: DSA_OP_ATTEND_DECODE.
+ */
+MSA_API msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
+                             const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                             int32_t max_pos, const int32_t* d_sel, float* d_out,
+                             void* d_ws, size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,143 @@
+"""Host-side tests of the C ABI (no GPU needed, nothing is launched).
+
+* libmsa_hip.so loads and exports every function include/msa.h declares;
+* every entry point validates its host-visible arguments and returns the
+  documented msa_status before touching the GPU (fake, never dereferenced
+  pointers are used, so a validation bug that let a call through would be
+  an error launch on this GPU-less host and show up as MSA_ERR_HIP);
+* empty calls (n_q = 0) return MSA_OK without launching;
+* workspace sizes follow the documented layouts.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_msa_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, RANGE, ALIGN, WS, UNSUP = 0, -1, -2, -3, -4, -5, -6
+A = ctypes.c_void_p(0x10000)     # fake 16-byte-aligned device address (never dereferenced)
+B = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)   # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        from block_sparse_attention_msa_amd import build
+        build.build()
+    return M.lib()
+
+
+def _cache(cap=4096, n_stream=2, idx=A, dsa=A):
+    return M.Cache(idx, dsa, A, A, cap, n_stream)
+
+
+def test_exports_every_declared_symbol(L):
+    hdr = open(os.path.join(ROOT, "include", "msa.h")).read()
+    declared = set(re.findall(r"^MSA_API [^(]*?\b(\w+)\(", hdr, flags=re.M))
+    assert declared == set(M.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in (OK, NULL, SHAPE, RANGE, ALIGN, WS, UNSUP, -7):
+        assert M.status_string(code).startswith("MSA_")
+
+
+def test_dims_validation(L):
+    c = _cache()
+    for bad in (M.Dims(8, 16, 128, 128, 128, 16, 0.08), M.Dims(4, 8, 128, 128, 128, 16, 0.08),
+                M.Dims(4, 16, 64, 128, 128, 16, 0.08), M.Dims(4, 16, 128, 64, 128, 16, 0.08),
+                M.Dims(4, 16, 128, 128, 64, 16, 0.08), M.Dims(4, 16, 128, 128, 128, 0, 0.08),
+                M.Dims(4, 16, 128, 128, 128, 65, 0.08), M.Dims(4, 16, 128, 128, 128, 16, 0.0),
+                M.Dims(4, 16, 128, 128, 128, 16, float("nan"))):
+        rc = L.msa_select(ctypes.byref(bad), ctypes.byref(c), A, A, A, 1, 100, A, A, A, 1 << 30, None)
+        assert rc == UNSUP
+    # DSA needs block 1 and 1 <= top_k <= 4096
+    d = M.msa_dims()
+    assert L.dsa_select(ctypes.byref(d), ctypes.byref(c), A, A, A, 1, 100, A, A, A, 1 << 30, None) == UNSUP
+    assert L.msa_select(None, ctypes.byref(c), A, A, A, 1, 100, A, A, A, 1 << 30, None) == NULL
+
+
+def test_null_misaligned_and_range(L):
+    d = M.msa_dims()
+    c = _cache()
+    args = lambda **kw: [kw.get("idx_q", A), kw.get("stream", A), kw.get("pos", A), kw.get("n_q", 1),
+                         kw.get("max_pos", 100), kw.get("sel", A), kw.get("n_sel", A), kw.get("ws", A),
+                         kw.get("wsb", 1 << 30), None]
+    sel = lambda **kw: L.msa_select(ctypes.byref(d), ctypes.byref(kw.pop("cache", c)), *args(**kw))
+    assert sel(idx_q=None) == NULL
+    assert sel(sel=None) == NULL
+    assert sel(cache=_cache(idx=None)) == NULL
+    assert sel(idx_q=MIS) == ALIGN
+    assert sel(n_sel=MIS) == ALIGN
+    assert sel(max_pos=4096) == RANGE          # == cap
+    assert sel(max_pos=-1) == RANGE
+    assert sel(n_q=-1) == SHAPE
+    assert sel(cache=_cache(cap=0)) == SHAPE
+    assert sel(cache=_cache(n_stream=0)) == SHAPE
+    assert sel(ws=None) == NULL
+    need = M.workspace_bytes(d, M.MSA_OP_SELECT, 1, 100)
+    assert sel(wsb=need - 1) == WS
+    assert sel(n_q=0) == OK                    # empty call, nothing launched
+    assert sel(n_q=0, ws=None) == OK
+
+
+def test_prefill_range_checks(L):
+    d = M.msa_dims()
+    c = _cache(cap=1000, n_stream=2)
+    f = lambda stream, pos0, n: L.msa_select_prefill(ctypes.byref(d), ctypes.byref(c), A, stream, pos0, n,
+                                                     A, A, A, 1 << 30, None)
+    assert f(2, 0, 10) == RANGE
+    assert f(-1, 0, 10) == RANGE
+    assert f(0, -1, 10) == RANGE
+    assert f(0, 991, 10) == RANGE              # last position 1000 == cap
+    assert f(0, 990, 0) == OK
+    assert f(0, 0, -5) == SHAPE
+    g = lambda n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 990, n, A, A, A, 1 << 30,
+                                       None)
+    assert g(11) == RANGE
+    assert g(0) == OK
+
+
+def test_append_validation(L):
+    d = M.msa_dims()
+    c = _cache(idx=None)
+    f = lambda *src, n=1, max_pos=5: L.msa_index_append(ctypes.byref(d), ctypes.byref(c), A, A, n,
+                                                       max_pos, *src, None)
+    assert f(A, None, None) == NULL            # idx source but no idx cache
+    assert f(None, MIS, None) == ALIGN
+    assert f(None, A, A, n=0) == OK
+    assert f(None, A, A, max_pos=4096) == RANGE
+    dd = M.dsa_dims()
+    cd = _cache(dsa=None)
+    assert L.dsa_index_append(ctypes.byref(dd), ctypes.byref(cd), A, A, 1, 5, A, None, None, None) == NULL
+
+
+def test_topk_block_limit(L):
+    d = M.msa_dims()
+    # 4096 blocks of 128 is the most a top-k wave ranks
+    assert L.msa_topk_blocks(ctypes.byref(d), A, 4097, A, 1, 4096 * 128, A, A, None) == UNSUP
+    assert L.msa_topk_blocks(ctypes.byref(d), A, 10, A, 1, 4096, A, A, None) == SHAPE   # stride < nblk
+    assert L.msa_topk_blocks(ctypes.byref(d), A, 33, A, 0, 4095, A, A, None) == OK
+
+
+def test_workspace_sizes(L):
+    d = M.msa_dims()
+    # select: n_q * 4 groups * nblk floats, 256-byte aligned
+    assert M.workspace_bytes(d, M.MSA_OP_SELECT, 32, 32767) == 32 * 4 * 256 * 4
+    assert M.workspace_bytes(d, M.MSA_OP_SELECT, 1, 0) == 256
+    assert M.workspace_bytes(d, M.MSA_OP_SELECT_PREFILL, 4096, 32767) == 4096 * 4 * 256 * 4
+    # attention partials: per (query, group, split) 16 heads x (128 + 2) floats
+    n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
+    assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 0   # no split at 4096 queries
+    dd = M.dsa_dims()
+    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
+    with pytest.raises(M.MsaError):
+        M.workspace_bytes(d, M.DSA_OP_SELECT, 16, 65535)   # DSA op needs DSA dims

@@ -1,0 +1,86 @@
+"""GPU parity of the DSA lightning-indexer variant (Hadamard key rotation into
+the fp16 cache, token top-k selection, attention over the kept tokens)
+against the fp64 oracle, through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_msa_amd as M
+import oracle
+import workloads as W
+from _gpu_common import DEV, GAP_REL, GpuWorkload, check_attention, dev, dev_bits, host_bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_token_selection(g_sel, g_nsel, o_sel, o_nsel, scores, pos, top_k):
+    equal = np.zeros(len(pos), bool)
+    for i in range(len(pos)):
+        k = min(top_k, pos[i] + 1)
+        assert g_nsel[i] == o_nsel[i] == k
+        ids = g_sel[i, :k]
+        assert np.all(np.diff(ids) > 0) and ids.min() >= 0 and ids.max() <= pos[i]
+        assert np.all(g_sel[i, k:] == -1)
+        a, b = set(ids.tolist()), set(o_sel[i, :k].tolist())
+        if a == b:
+            equal[i] = True
+            continue
+        t = scores[i, :pos[i] + 1]
+        thr = GAP_REL * np.abs(t).max()
+        boundary = t[o_sel[i, :k]].min()
+        for x in a ^ b:
+            assert abs(t[x] - boundary) < thr, f"query {i}: token {x} outside the near-tie band"
+    return equal
+
+
+def _dsa_parity(wl: W.Workload):
+    log(f"[dsa] {wl.name}: streams={wl.n_stream} cap={wl.cap} n_q={wl.n_q} top_k={wl.top_k}")
+    dims = M.dsa_dims(wl.top_k, W.SCALE)
+    gw = GpuWorkload(wl)
+    gw.append_own_rows()             # rotates every key into the fp16 cache
+    torch.cuda.synchronize()
+    # rotation parity: bit-exact (exact fp64 transform, one RNE rounding)
+    o_rot = oracle.dsa_rotate(gw.host["dsa_k"])
+    g_rot = host_bits(gw.dsa_k)
+    n_bad = int((g_rot != o_rot).sum())
+    assert n_bad == 0, f"{n_bad} rotated key elements differ"
+    q_idx = dev_bits(gw.qs["q_idx"], torch.float16)
+    sel = torch.empty((wl.n_q, wl.top_k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty(wl.n_q, dtype=torch.int32, device=DEV)
+    M.dsa_select(dims, gw.cache, q_idx, gw.stream, gw.pos, wl.max_pos, sel, n_sel,
+                 gw.ws(dims, M.DSA_OP_SELECT))
+    torch.cuda.synchronize()
+    o_sel, o_nsel, scores = oracle.dsa_select(o_rot, gw.qs["stream"], gw.qs["pos"], gw.qs["q_idx"],
+                                              top_k=wl.top_k, want_scores=True)
+    equal = _check_token_selection(sel.cpu().numpy(), n_sel.cpu().numpy(), o_sel, o_nsel, scores,
+                                   gw.qs["pos"], wl.top_k)
+    log(f"  selection: {equal.sum()} of {len(equal)} queries identical")
+    o_out = oracle.sparse_attend(gw.host["k"], gw.host["v"], gw.qs["stream"], gw.qs["pos"], gw.qs["q"],
+                                 o_sel, unit=1, scale=W.SCALE, shared_across_groups=True)
+
+    def attend(sel_dev):
+        out = torch.empty((wl.n_q, 64, 128), dtype=torch.float32, device=DEV)
+        M.dsa_attend_decode(dims, gw.cache, gw.q, gw.stream, gw.pos, wl.max_pos, sel_dev, out,
+                            gw.ws(dims, M.DSA_OP_ATTEND_DECODE))
+        return out.cpu().numpy()
+
+    wa, wr = check_attention(attend(dev(o_sel)), o_out)
+    log(f"  attention on the oracle selection: max-abs {wa:.3e}, rel-L2 {wr:.3e}")
+    check_attention(attend(sel), o_out, mask_qg=np.repeat(equal[:, None], 4, 1))
+
+
+def test_dsa_small_ragged():
+    # ragged cap; positions below and above top_k; a short context (p + 1 <= top_k)
+    wl = W.Workload("dsa_small", "dsa_decode", 3, 3000, (0, 1, 2, 0, 1), (2999, 63, 1500, 64, 0),
+                    top_k=64)
+    _dsa_parity(wl)
+
+
+def test_dsa_dense_when_context_fits():
+    wl = W.Workload("dsa_dense", "dsa_decode", 2, 2048, (0, 1), (2047, 1000), top_k=2048)
+    _dsa_parity(wl)
+
+
+def test_dsa_full_16x64k():
+    _dsa_parity(W.CONFIGS["dsa_16x64k"])
