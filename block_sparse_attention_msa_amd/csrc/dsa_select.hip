@@ -26,9 +26,12 @@ constexpr int kSelThreads = 1024;
 __device__ __forceinline__ float dot8_f16(const u32x4& q, const u32x4& k) {
     float d = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, q[e]), __builtin_bit_cast(half2_t, k[e]), d,
-                                   false);
+    for (int e = 0; e < 4; ++e) {
+        // copy the element out first: a bit-cast of a vector-element lvalue
+        // reads element 0 whatever the index
+        const uint32_t qe = q[e], ke = k[e];
+        d = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qe), __builtin_bit_cast(half2_t, ke), d, false);
+    }
     return d;
 }
 

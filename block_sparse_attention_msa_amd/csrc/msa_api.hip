@@ -78,12 +78,12 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
     MSA_TRY(check_dims(dims, mode));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_new, max_pos, cache));
+    if (n_new == 0) return MSA_OK;
     MSA_TRY(check_ptrs({d_stream, d_pos}));
     if (d_idx_k_new) MSA_TRY(check_ptrs({d_idx_k_new, cache->idx_k}));
     if (d_key_new) MSA_TRY(check_ptrs({d_key_new, cache->dsa_k}));
     if (d_k_new) MSA_TRY(check_ptrs({d_k_new, cache->k}));
     if (d_v_new) MSA_TRY(check_ptrs({d_v_new, cache->v}));
-    if (n_new == 0) return MSA_OK;
     return hip_status(msa::launch_append(cache->idx_k, cache->dsa_k, cache->k, cache->v, cache->cap,
                                          d_stream, d_pos, n_new, d_idx_k_new, d_key_new, d_k_new,
                                          d_v_new, static_cast<hipStream_t>(hip_stream)));
@@ -150,9 +150,9 @@ msa_status msa_block_scores(const msa_dims* dims, const msa_cache* cache, const 
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_stream, d_pos, d_bs}));
     if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
-    if (n_q == 0) return MSA_OK;
     return hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q,
                                                       nblk_of(max_pos), d_bs, nblk_stride,
                                                       static_cast<hipStream_t>(hip_stream)));
@@ -164,10 +164,10 @@ msa_status msa_topk_blocks(const msa_dims* dims, const float* d_bs, int64_t nblk
     MSA_TRY(check_dims(dims, Mode::Msa));
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
     if (max_pos < 0) return MSA_ERR_OUT_OF_RANGE;
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({d_bs, d_pos, d_sel, d_n_sel}));
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
-    if (n_q == 0) return MSA_OK;
     return hip_status(msa::launch_topk_blocks(d_bs, nblk_stride, d_pos, n_q, nblk_of(max_pos), dims->top_k,
                                               d_sel, d_n_sel, static_cast<hipStream_t>(hip_stream)));
 }
@@ -179,9 +179,9 @@ msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float*
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
-    if (n_q == 0) return MSA_OK;
     MSA_TRY(check_ptrs({d_ws}));
     if (ws_bytes < select_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -200,8 +200,8 @@ msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_bs}));
-    if (n_q == 0) return MSA_OK;
     const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
     if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
     return hip_status(msa::launch_block_scores_prefill(view(cache), d_idx_q, stream, pos0, n_q,
@@ -217,8 +217,8 @@ msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cache, cons
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_sel, d_n_sel}));
-    if (n_q == 0) return MSA_OK;
     const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({d_ws}));
@@ -241,8 +241,8 @@ msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_stream, d_pos, d_sel, d_out}));
-    if (n_q == 0) return MSA_OK;
     const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, kBlock);
     if (need) {
         MSA_TRY(check_ptrs({d_ws}));
@@ -261,8 +261,8 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out}));
-    if (n_q == 0) return MSA_OK;
     const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, kBlock);
     if (need) {
         MSA_TRY(check_ptrs({d_ws}));
@@ -280,9 +280,9 @@ msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16
     MSA_TRY(check_dims(dims, Mode::Dsa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->dsa_k, d_q_idx, d_stream, d_pos, d_sel, d_n_sel}));
     if (n_q > 65535) return MSA_ERR_UNSUPPORTED;
-    if (n_q == 0) return MSA_OK;
     MSA_TRY(check_ptrs({d_ws}));
     if (ws_bytes < msa::dsa_select_ws_bytes(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(msa::launch_dsa_select(cache->dsa_k, cache->cap, d_q_idx, d_stream, d_pos, n_q,
@@ -297,8 +297,8 @@ msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
     MSA_TRY(check_dims(dims, Mode::Dsa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_stream, d_pos, d_sel, d_out}));
-    if (n_q == 0) return MSA_OK;
     const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, 1);
     if (need) {
         MSA_TRY(check_ptrs({d_ws}));
