@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="decode step only (for profiling)")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for rocprofv3 counter runs: one plain 1 GiB device copy (calibration of the "
+                         "byte counters), then 3 decode steps; prints no result line")
     return ap.parse_args()
 
 
@@ -140,6 +143,18 @@ def main():
         M.msa_attend_decode(dims, cache, q, stream, pos, p, sel, out, ws_att)
         if e: e[4].record()
 
+    if args.profile_pass:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)            # reads 1 GiB and writes 1 GiB
+        torch.cuda.synchronize()
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        log("[bench] profile pass done")
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -164,7 +179,11 @@ def main():
     log(f"[bench] decode step {ms_per_step * 1e3:.1f} us: append {t_append * 1e3:.1f} scan {t_scan * 1e3:.1f} "
         f"topk {t_topk * 1e3:.1f} attend {t_att * 1e3:.1f} us; scan {scan_gbps:.0f} GB/s, attend {att_gbps:.0f} GB/s")
 
+    copy_gbps = measure_copy_bandwidth(torch, dev)
+    log(f"[bench] device copy {copy_gbps:.0f} GB/s (read + write)")
     extra = {
+        "device_copy_GBps": round(copy_gbps, 1),
+        "indexer_frac_of_copy": round(scan_gbps / copy_gbps, 4),
         "decode_us": {"append": round(t_append * 1e3, 2), "indexer_scan": round(t_scan * 1e3, 2),
                       "topk": round(t_topk * 1e3, 2), "attend": round(t_att * 1e3, 2)},
         "indexer_GBps": round(scan_gbps, 1),
@@ -229,6 +248,24 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_copy_bandwidth(torch, dev, n_bytes=1 << 30, iters=10):
+    """Plain device-to-device copy (read + write bytes / time): the
+    practical HBM ceiling the roofline fractions can be compared with."""
+    src = torch.empty(n_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / iters * 1e-3
+    del src, dst
+    return 2 * n_bytes / t / 1e9
 
 
 def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10):

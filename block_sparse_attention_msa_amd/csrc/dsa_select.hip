@@ -8,8 +8,8 @@
 //
 // Kernel 1 streams the fp16 key cache once with 128-bit loads (a 16-lane DPP
 // row per 256-byte key row, v_dot2 on fp16 pairs) and writes the f32 scores.
-// Kernel 2 is an exact radix select on order-preserving u32 keys: four 8-bit
-// digit passes find the k-th largest key T, then an order-preserving
+// Kernel 2 is an exact radix select on order-preserving u32 keys: three digit
+// passes (12, 12, 8 bits) find the k-th largest key T, then an order-preserving
 // compaction writes every key > T and the lowest-id keys == T, so the output
 // is already in ascending id order and unique.
 #include "common.hpp"
@@ -96,12 +96,19 @@ __device__ int block_inclusive_scan(int v, int* wave_sums) {
     return v;
 }
 
+// Digits of the radix select, most significant first: 12 + 12 + 8 bits.
+// Wide first digits spread the (exponent-concentrated) f32 scores over many
+// histogram bins, which keeps LDS atomic collisions rare.
+constexpr int kDigitBits[3] = {12, 12, 8};
+constexpr int kBins = 4096;
+constexpr int kBinsPerThread = kBins / kSelThreads;   // 4
+
 __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __restrict__ scores,
                                                                int64_t stride,
                                                                const int32_t* __restrict__ q_pos,
                                                                int top_k, int32_t* __restrict__ sel,
                                                                int32_t* __restrict__ n_sel) {
-    __shared__ int hist[256];
+    __shared__ int hist[kBins];
     __shared__ int wave_sums[kSelThreads / 64];
     __shared__ uint32_t s_digit;
     __shared__ int s_remaining;
@@ -115,31 +122,52 @@ __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __re
         if (tid == 0) n_sel[i] = n;
         return;
     }
-    // ---- radix select of the k-th largest key (k = top_k here)
+    // ---- radix select of the top_k-th largest key T
     uint32_t prefix = 0, mask = 0;
-    int remaining = top_k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
+    int remaining = top_k;      // keys still to take among those matching the prefix
+    int shift = 32;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int bits = kDigitBits[pass];
+        shift -= bits;
+        const uint32_t dmask = (1u << bits) - 1;
+        for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
         __syncthreads();
         for (int j = tid; j < n; j += kSelThreads) {
             const uint32_t key = ordered_key(t[j]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
         }
         __syncthreads();
-        // digits from the top: thread d' counts bin 255 - d'
-        const int cnt = tid < 256 ? hist[255 - tid] : 0;
-        const int incl = block_inclusive_scan(cnt, wave_sums);
-        if (tid < 256 && incl >= remaining && incl - cnt < remaining) {
-            s_digit = 255u - tid;
-            s_remaining = remaining - (incl - cnt);
+        // thread tid owns descending bins d' = 4*tid .. 4*tid + 3 (digit = nb - 1 - d')
+        const int nb = 1 << bits;
+        int c[kBinsPerThread];
+        int csum = 0;
+#pragma unroll
+        for (int e = 0; e < kBinsPerThread; ++e) {
+            const int dd = kBinsPerThread * tid + e;
+            c[e] = dd < nb ? hist[nb - 1 - dd] : 0;
+            csum += c[e];
+        }
+        const int incl = block_inclusive_scan(csum, wave_sums);
+        if (incl >= remaining && incl - csum < remaining) {
+            int before = incl - csum;
+#pragma unroll
+            for (int e = 0; e < kBinsPerThread; ++e) {
+                if (before + c[e] >= remaining) {
+                    s_digit = static_cast<uint32_t>(nb - 1 - (kBinsPerThread * tid + e));
+                    s_remaining = remaining - before;
+                    break;
+                }
+                before += c[e];
+            }
         }
         __syncthreads();
         prefix |= s_digit << shift;
-        mask |= 255u << shift;
+        mask |= dmask << shift;
         remaining = s_remaining;
         __syncthreads();
     }
-    const uint32_t T = prefix;          // the k-th largest key; `remaining` keys equal to it are kept
+    const uint32_t T = prefix;          // the top_k-th largest key; `remaining` keys equal to it are kept
     // ---- order-preserving compaction over contiguous per-thread ranges
     const int R = (n + kSelThreads - 1) / kSelThreads;
     const int j0 = min(tid * R, n), j1 = min(j0 + R, n);

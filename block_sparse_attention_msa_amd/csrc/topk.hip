@@ -18,17 +18,42 @@
 namespace msa {
 namespace {
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int mask) {
-    const uint32_t lo = xor_lane_u32(static_cast<uint32_t>(x), mask);
-    const uint32_t hi = xor_lane_u32(static_cast<uint32_t>(x >> 32), mask);
+__device__ __forceinline__ uint64_t make_u64(uint32_t lo, uint32_t hi) {
     return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const uint32_t lo = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x)), CTRL, 0xf, 0xf, false));
+    const uint32_t hi = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(x >> 32)), CTRL, 0xf, 0xf, false));
+    return make_u64(lo, hi);
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum over the 64 lanes, delivered to every lane: DPP inside each
+// 16-lane row, then the gfx950 row swaps (v_permlane16_swap pairs rows 0/1
+// and 2/3, v_permlane32_swap pairs the two halves of the wave).
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const uint64_t y = shfl_xor_u64(x, m);
-        x = y > x ? y : x;
+    x = max_u64(x, dpp_u64<kDppQuadXor1>(x));
+    x = max_u64(x, dpp_u64<kDppQuadXor2>(x));
+    x = max_u64(x, dpp_u64<kDppRowHalfMirror>(x));
+    x = max_u64(x, dpp_u64<kDppRowMirror>(x));
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x),
+                                                         false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x >> 32),
+                                                         static_cast<uint32_t>(x >> 32), false, false);
+        x = max_u64(make_u64(lo[0], hi[0]), make_u64(lo[1], hi[1]));
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x),
+                                                         false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x >> 32),
+                                                         static_cast<uint32_t>(x >> 32), false, false);
+        x = max_u64(make_u64(lo[0], hi[0]), make_u64(lo[1], hi[1]));
     }
     return x;
 }
