@@ -151,6 +151,12 @@ int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
+// Prefill: tiles of consecutive queries sweep the union of their selected
+// blocks (no workspace).
+hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
+                                 int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
+                                 float scale, float* out, hipStream_t s);
+
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
 hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,
                              const int32_t* stream, const int32_t* pos, int64_t n_q,

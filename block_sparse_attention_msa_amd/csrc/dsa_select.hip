@@ -8,10 +8,10 @@
 //
 // Kernel 1 streams the fp16 key cache once with 128-bit loads (a 16-lane DPP
 // row per 256-byte key row, v_dot2 on fp16 pairs) and writes the f32 scores.
-// Kernel 2 is an exact radix select on order-preserving u32 keys: three digit
-// passes (12, 12, 8 bits) find the k-th largest key T, then an order-preserving
-// compaction writes every key > T and the lowest-id keys == T, so the output
-// is already in ascending id order and unique.
+// Kernel 2 is an exact radix select on order-preserving u32 keys (digits of
+// 12, 12 and 8 bits) that finds the k-th largest key T, then an order-
+// preserving compaction writes every key > T and the lowest-id keys == T, so
+// the output is already in ascending id order and unique.
 #include "common.hpp"
 
 namespace msa {
@@ -103,15 +103,74 @@ constexpr int kDigitBits[3] = {12, 12, 8};
 constexpr int kBins = 4096;
 constexpr int kBinsPerThread = kBins / kSelThreads;   // 4
 
+// One workgroup of 1024 threads per query, three streaming passes over the
+// query's scores (16-byte loads, coalesced across the workgroup):
+//  1. histogram of the top 12 key bits -> the digit d1 of the top_k-th
+//     largest key T, and how many keys equal to T's prefix are still needed;
+//  2. the keys whose top 12 bits equal d1 (the boundary bin, typically ~1% of
+//     the keys) are copied with their ids into an LDS candidate list, whose
+//     remaining 12 + 8 bits are resolved there;
+//  3. an order-preserving compaction in rounds of 4096 consecutive keys emits
+//     every key > T and the lowest-id keys == T, ascending.
+// A boundary bin larger than the LDS list (heavily tied scores) takes the
+// general path, which re-reads the scores for the last two digits.
+constexpr int kCandCap = 4096;
+
+template <typename F>
+__device__ __forceinline__ void for_each_score(const float* t, int n, F&& f) {
+    // j = 4 * (tid + 1024 * r) + c: 16-byte loads, consecutive threads adjacent
+    for (int base = 4 * threadIdx.x; base < n; base += 4 * kSelThreads) {
+        if (base + 3 < n) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(t + base);
+            f(base, ordered_key(x.x)); f(base + 1, ordered_key(x.y));
+            f(base + 2, ordered_key(x.z)); f(base + 3, ordered_key(x.w));
+        } else {
+            for (int j = base; j < n; ++j) f(j, ordered_key(t[j]));
+        }
+    }
+}
+
+// Finds the digit (bits `bits` wide) of the rank-`remaining` largest among
+// the histogram counts; returns it through s_digit / s_remaining.
+__device__ __forceinline__ void pick_digit(const int* hist, int bits, int remaining, int* wave_sums,
+                                           uint32_t* s_digit, int* s_remaining) {
+    const int nb = 1 << bits;
+    int c[kBinsPerThread];
+    int csum = 0;
+#pragma unroll
+    for (int e = 0; e < kBinsPerThread; ++e) {
+        const int dd = kBinsPerThread * threadIdx.x + e;    // descending bin order
+        c[e] = dd < nb ? hist[nb - 1 - dd] : 0;
+        csum += c[e];
+    }
+    const int incl = block_inclusive_scan(csum, wave_sums);
+    if (incl >= remaining && incl - csum < remaining) {
+        int before = incl - csum;
+#pragma unroll
+        for (int e = 0; e < kBinsPerThread; ++e) {
+            if (before + c[e] >= remaining) {
+                *s_digit = static_cast<uint32_t>(nb - 1 - (kBinsPerThread * threadIdx.x + e));
+                *s_remaining = remaining - before;
+                break;
+            }
+            before += c[e];
+        }
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __restrict__ scores,
                                                                int64_t stride,
                                                                const int32_t* __restrict__ q_pos,
                                                                int top_k, int32_t* __restrict__ sel,
                                                                int32_t* __restrict__ n_sel) {
     __shared__ int hist[kBins];
+    __shared__ uint32_t cand_key[kCandCap];
+    __shared__ int32_t cand_id[kCandCap];
     __shared__ int wave_sums[kSelThreads / 64];
     __shared__ uint32_t s_digit;
     __shared__ int s_remaining;
+    __shared__ int s_ncand;
     const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
     const int n = q_pos[i] + 1;
@@ -122,73 +181,117 @@ __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __re
         if (tid == 0) n_sel[i] = n;
         return;
     }
-    // ---- radix select of the top_k-th largest key T
-    uint32_t prefix = 0, mask = 0;
-    int remaining = top_k;      // keys still to take among those matching the prefix
-    int shift = 32;
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-        const int bits = kDigitBits[pass];
-        shift -= bits;
-        const uint32_t dmask = (1u << bits) - 1;
-        for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
-        __syncthreads();
-        for (int j = tid; j < n; j += kSelThreads) {
-            const uint32_t key = ordered_key(t[j]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
-        }
-        __syncthreads();
-        // thread tid owns descending bins d' = 4*tid .. 4*tid + 3 (digit = nb - 1 - d')
-        const int nb = 1 << bits;
-        int c[kBinsPerThread];
-        int csum = 0;
-#pragma unroll
-        for (int e = 0; e < kBinsPerThread; ++e) {
-            const int dd = kBinsPerThread * tid + e;
-            c[e] = dd < nb ? hist[nb - 1 - dd] : 0;
-            csum += c[e];
-        }
-        const int incl = block_inclusive_scan(csum, wave_sums);
-        if (incl >= remaining && incl - csum < remaining) {
-            int before = incl - csum;
-#pragma unroll
-            for (int e = 0; e < kBinsPerThread; ++e) {
-                if (before + c[e] >= remaining) {
-                    s_digit = static_cast<uint32_t>(nb - 1 - (kBinsPerThread * tid + e));
-                    s_remaining = remaining - before;
-                    break;
-                }
-                before += c[e];
+    // ---- pass 1: top 12 bits over all keys
+    for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
+    if (tid == 0) s_ncand = 0;
+    __syncthreads();
+    for_each_score(t, n, [&](int, uint32_t key) { atomicAdd(&hist[key >> 20], 1); });
+    __syncthreads();
+    pick_digit(hist, 12, top_k, wave_sums, &s_digit, &s_remaining);
+    const uint32_t d1 = s_digit;
+    int remaining = s_remaining;
+    const int bin_count = hist[d1];
+    uint32_t prefix = d1 << 20, mask = 0xfff00000u;
+    __syncthreads();
+    if (bin_count <= kCandCap) {
+        // ---- pass 2: gather the boundary bin, resolve the low 20 bits in LDS
+        for_each_score(t, n, [&](int j, uint32_t key) {
+            if ((key & mask) == prefix) {
+                const int slot = atomicAdd(&s_ncand, 1);
+                cand_key[slot] = key;
+                cand_id[slot] = j;
             }
+        });
+        __syncthreads();
+        const int nc = s_ncand;
+#pragma unroll
+        for (int pass = 1; pass < 3; ++pass) {
+            const int bits = kDigitBits[pass];
+            const int shift = pass == 1 ? 8 : 0;
+            const uint32_t dmask = (1u << bits) - 1;
+            for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
+            __syncthreads();
+            for (int c = tid; c < nc; c += kSelThreads) {
+                const uint32_t key = cand_key[c];
+                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+            }
+            __syncthreads();
+            pick_digit(hist, bits, remaining, wave_sums, &s_digit, &s_remaining);
+            prefix |= s_digit << shift;
+            mask |= dmask << shift;
+            remaining = s_remaining;
+            __syncthreads();
         }
-        __syncthreads();
-        prefix |= s_digit << shift;
-        mask |= dmask << shift;
-        remaining = s_remaining;
-        __syncthreads();
+    } else {
+        // ---- general path: the last two digits over all keys
+#pragma unroll
+        for (int pass = 1; pass < 3; ++pass) {
+            const int bits = kDigitBits[pass];
+            const int shift = pass == 1 ? 8 : 0;
+            const uint32_t dmask = (1u << bits) - 1;
+            for (int b = tid; b < kBins; b += kSelThreads) hist[b] = 0;
+            __syncthreads();
+            for_each_score(t, n, [&](int, uint32_t key) {
+                if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+            });
+            __syncthreads();
+            pick_digit(hist, bits, remaining, wave_sums, &s_digit, &s_remaining);
+            prefix |= s_digit << shift;
+            mask |= dmask << shift;
+            remaining = s_remaining;
+            __syncthreads();
+        }
     }
     const uint32_t T = prefix;          // the top_k-th largest key; `remaining` keys equal to it are kept
-    // ---- order-preserving compaction over contiguous per-thread ranges
-    const int R = (n + kSelThreads - 1) / kSelThreads;
-    const int j0 = min(tid * R, n), j1 = min(j0 + R, n);
-    int n_gt = 0, n_eq = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = ordered_key(t[j]);
-        n_gt += key > T;
-        n_eq += key == T;
-    }
-    const int eq_before = block_inclusive_scan(n_eq, wave_sums) - n_eq;
-    const int take_eq = max(0, min(n_eq, remaining - eq_before));
-    const int mine = n_gt + take_eq;
-    int w = block_inclusive_scan(mine, wave_sums) - mine;
-    int taken = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = ordered_key(t[j]);
-        if (key > T || (key == T && taken < take_eq)) {
-            if (w < top_k) out[w] = j;     // exactly top_k keys qualify; the bound is defensive
-            ++w;
-            taken += key == T;
+    // ---- pass 3: order-preserving compaction, 4096 consecutive keys per round
+    int written = 0, eq_seen = 0;       // running totals over the rounds (uniform)
+    for (int base = 0; base < n; base += 4 * kSelThreads) {
+        const int j = base + 4 * tid;
+        uint32_t key[4] = {0, 0, 0, 0};
+        bool in[4];
+        if (j + 3 < n) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(t + j);
+            key[0] = ordered_key(x.x); key[1] = ordered_key(x.y);
+            key[2] = ordered_key(x.z); key[3] = ordered_key(x.w);
+        } else {
+            for (int c = 0; c < 4; ++c)
+                if (j + c < n) key[c] = ordered_key(t[j + c]);
         }
+        int n_eq = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            in[c] = j + c < n;
+            n_eq += in[c] && key[c] == T;
+        }
+        const int eq_incl = block_inclusive_scan(n_eq, wave_sums);
+        int eq_rank = eq_seen + eq_incl - n_eq;      // equal keys before this thread's four
+        bool take[4];
+        int n_take = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool eq = in[c] && key[c] == T;
+            take[c] = (in[c] && key[c] > T) || (eq && eq_rank < remaining);
+            eq_rank += eq;
+            n_take += take[c];
+        }
+        const int take_incl = block_inclusive_scan(n_take, wave_sums);
+        int w = written + take_incl - n_take;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (take[c]) {
+                if (w < top_k) out[w] = j + c;      // exactly top_k keys qualify; the bound is defensive
+                ++w;
+            }
+        }
+        // round totals: the last thread's inclusive values, via the scan's LDS
+        if (tid == kSelThreads - 1) {
+            wave_sums[0] = eq_incl;
+            wave_sums[1] = take_incl;
+        }
+        __syncthreads();
+        eq_seen += wave_sums[0];
+        written += wave_sums[1];
+        __syncthreads();
     }
     if (tid == 0) n_sel[i] = top_k;
 }

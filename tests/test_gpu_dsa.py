@@ -34,10 +34,10 @@ def _check_token_selection(g_sel, g_nsel, o_sel, o_nsel, scores, pos, top_k):
     return equal
 
 
-def _dsa_parity(wl: W.Workload):
+def _dsa_parity(wl: W.Workload, host=None):
     log(f"[dsa] {wl.name}: streams={wl.n_stream} cap={wl.cap} n_q={wl.n_q} top_k={wl.top_k}")
     dims = M.dsa_dims(wl.top_k, W.SCALE)
-    gw = GpuWorkload(wl)
+    gw = GpuWorkload(wl, host)
     gw.append_own_rows()             # rotates every key into the fp16 cache
     torch.cuda.synchronize()
     # rotation parity: bit-exact (exact fp64 transform, one RNE rounding)
@@ -80,6 +80,15 @@ def test_dsa_small_ragged():
 def test_dsa_dense_when_context_fits():
     wl = W.Workload("dsa_dense", "dsa_decode", 2, 2048, (0, 1), (2047, 1000), top_k=2048)
     _dsa_parity(wl)
+
+
+def test_dsa_all_scores_tied():
+    # every key identical: all scores tie, the lowest ids win; the boundary
+    # bin holds every key, more than the candidate list keeps in LDS
+    wl = W.Workload("dsa_ties", "dsa_decode", 1, 6000, (0, 0), (5999, 4500), top_k=100)
+    host = W.caches(wl)
+    host["dsa_k"][:] = host["dsa_k"][0, 0]
+    _dsa_parity(wl, host)
 
 
 def test_dsa_full_16x64k():

@@ -195,6 +195,14 @@ def test_prefill_from_position_zero():
     _prefill_parity(W.prefill_workload("pf_zero", 700, 0, 700))
 
 
+@pytest.mark.parametrize("top_k", [7, 64])
+def test_prefill_second_stream_cache_edge(top_k):
+    # stream 1 of 2; the last queries' local block runs past the cache end
+    wl = W.Workload(f"pf_edge{top_k}", "msa_prefill", 2, 1000, tuple([1] * 100),
+                    tuple(range(900, 1000)), idx_dist="normal_scaled", top_k=top_k)
+    _prefill_parity(wl)
+
+
 def test_prefill_full_4096_at_32k_sampled():
     wl = W.CONFIGS["prefill_4096_at_32k"]
     rng = np.random.default_rng(0)
