@@ -194,8 +194,7 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
             float cm = x[0];
 #pragma unroll
             for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
-            cm = fmaxf(cm, xor_lane(cm, 16));
-            cm = fmaxf(cm, xor_lane(cm, 32));
+            cm = max_xor32(max_xor16(cm));
             const float m_new = fmaxf(m_run, cm);      // finite: the chunk has a visible key
             const float alpha = exp2f(m_run - m_new);  // 0 on the first chunk (m_run = -inf)
             float pr[8];
@@ -205,8 +204,7 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
                 pr[j] = exp2f(x[j] - m_new);
                 rs += pr[j];
             }
-            rs += xor_lane(rs, 16);
-            rs += xor_lane(rs, 32);
+            rs = sum_xor32(sum_xor16(rs));
             l_run = l_run * alpha + rs;
             m_run = m_new;
 #pragma unroll

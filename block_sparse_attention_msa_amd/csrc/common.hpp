@@ -57,14 +57,25 @@ __device__ __forceinline__ float row16_max(float x) {
     return x;
 }
 
-// Cross-row exchange (lane ^ 16, lane ^ 32) through the LDS permute unit.
-__device__ __forceinline__ float xor_lane(float x, int mask) {
-    int lane = __lane_id();
-    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+// All-lane reductions across rows with the gfx950 row-swap permutes:
+// v_permlane16_swap pairs rows 0/1 and 2/3, v_permlane32_swap the two wave
+// halves, so op(result[0], result[1]) combines lane l with lane l ^ 16
+// (resp. l ^ 32) in every lane.
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ uint32_t xor_lane_u32(uint32_t x, int mask) {
-    int lane = __lane_id();
-    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, static_cast<int>(x)));
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Order-preserving map of a finite or infinite f32 onto u32 (+0 and -0 map
@@ -150,12 +161,6 @@ struct AttendArgs {
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-
-// Prefill: tiles of consecutive queries sweep the union of their selected
-// blocks (no workspace).
-hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
-                                 int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
-                                 float scale, float* out, hipStream_t s);
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
 hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,

@@ -110,24 +110,39 @@ constexpr int kBinsPerThread = kBins / kSelThreads;   // 4
 //  2. the keys whose top 12 bits equal d1 (the boundary bin, typically ~1% of
 //     the keys) are copied with their ids into an LDS candidate list, whose
 //     remaining 12 + 8 bits are resolved there;
-//  3. an order-preserving compaction in rounds of 4096 consecutive keys emits
+//  3. an order-preserving compaction in rounds of 16384 consecutive keys emits
 //     every key > T and the lowest-id keys == T, ascending.
 // A boundary bin larger than the LDS list (heavily tied scores) takes the
 // general path, which re-reads the scores for the last two digits.
 constexpr int kCandCap = 4096;
 
+// Visits every score j < n as (j, ordered key).  Each thread issues four
+// 16-byte loads per batch (j = 4 * (tid + 1024 * r) + c, coalesced across the
+// workgroup) before using any of them.
+constexpr int kBatch = 4;
+
 template <typename F>
 __device__ __forceinline__ void for_each_score(const float* t, int n, F&& f) {
-    // j = 4 * (tid + 1024 * r) + c: 16-byte loads, consecutive threads adjacent
-    for (int base = 4 * threadIdx.x; base < n; base += 4 * kSelThreads) {
-        if (base + 3 < n) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(t + base);
-            f(base, ordered_key(x.x)); f(base + 1, ordered_key(x.y));
-            f(base + 2, ordered_key(x.z)); f(base + 3, ordered_key(x.w));
-        } else {
-            for (int j = base; j < n; ++j) f(j, ordered_key(t[j]));
+    const int full = n & ~3;
+    for (int base = 4 * threadIdx.x; base < full; base += 4 * kSelThreads * kBatch) {
+        f32x4 x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = base + 4 * kSelThreads * u;
+            x[u] = j < full ? *reinterpret_cast<const f32x4*>(t + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int j = base + 4 * kSelThreads * u;
+            if (j < full) {
+                f(j, ordered_key(x[u].x));
+                f(j + 1, ordered_key(x[u].y));
+                f(j + 2, ordered_key(x[u].z));
+                f(j + 3, ordered_key(x[u].w));
+            }
         }
     }
+    if (static_cast<int>(threadIdx.x) < n - full) f(full + threadIdx.x, ordered_key(t[full + threadIdx.x]));
 }
 
 // Finds the digit (bits `bits` wide) of the rank-`remaining` largest among
@@ -243,42 +258,48 @@ __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __re
         }
     }
     const uint32_t T = prefix;          // the top_k-th largest key; `remaining` keys equal to it are kept
-    // ---- pass 3: order-preserving compaction, 4096 consecutive keys per round
+    // ---- pass 3: order-preserving compaction; thread tid takes 16 consecutive
+    // keys of each round of 16384
+    constexpr int kPer = 16;
     int written = 0, eq_seen = 0;       // running totals over the rounds (uniform)
-    for (int base = 0; base < n; base += 4 * kSelThreads) {
-        const int j = base + 4 * tid;
-        uint32_t key[4] = {0, 0, 0, 0};
-        bool in[4];
-        if (j + 3 < n) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(t + j);
-            key[0] = ordered_key(x.x); key[1] = ordered_key(x.y);
-            key[2] = ordered_key(x.z); key[3] = ordered_key(x.w);
-        } else {
-            for (int c = 0; c < 4; ++c)
-                if (j + c < n) key[c] = ordered_key(t[j + c]);
+    for (int base = 0; base < n; base += kPer * kSelThreads) {
+        const int j = base + kPer * tid;
+        uint32_t key[kPer];
+#pragma unroll
+        for (int v = 0; v < kPer / 4; ++v) {
+            const int jj = j + 4 * v;
+            if (jj + 3 < n) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(t + jj);
+                key[4 * v] = ordered_key(x.x);
+                key[4 * v + 1] = ordered_key(x.y);
+                key[4 * v + 2] = ordered_key(x.z);
+                key[4 * v + 3] = ordered_key(x.w);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) key[4 * v + c] = jj + c < n ? ordered_key(t[jj + c]) : 0u;
+            }
         }
         int n_eq = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            in[c] = j + c < n;
-            n_eq += in[c] && key[c] == T;
-        }
+        for (int c = 0; c < kPer; ++c) n_eq += (j + c < n) && key[c] == T;
         const int eq_incl = block_inclusive_scan(n_eq, wave_sums);
-        int eq_rank = eq_seen + eq_incl - n_eq;      // equal keys before this thread's four
-        bool take[4];
+        int eq_rank = eq_seen + eq_incl - n_eq;      // equal keys before this thread's keys
+        uint32_t take = 0;
         int n_take = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bool eq = in[c] && key[c] == T;
-            take[c] = (in[c] && key[c] > T) || (eq && eq_rank < remaining);
+        for (int c = 0; c < kPer; ++c) {
+            const bool in = j + c < n;
+            const bool eq = in && key[c] == T;
+            const bool tk = (in && key[c] > T) || (eq && eq_rank < remaining);
             eq_rank += eq;
-            n_take += take[c];
+            take |= static_cast<uint32_t>(tk) << c;
+            n_take += tk;
         }
         const int take_incl = block_inclusive_scan(n_take, wave_sums);
         int w = written + take_incl - n_take;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (take[c]) {
+        for (int c = 0; c < kPer; ++c) {
+            if ((take >> c) & 1) {
                 if (w < top_k) out[w] = j + c;      // exactly top_k keys qualify; the bound is defensive
                 ++w;
             }
