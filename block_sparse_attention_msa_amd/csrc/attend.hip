@@ -11,7 +11,9 @@
 //    heads of a group are the N = 16 side of v_mfma_f32_16x16x32_bf16, so a
 //    group's heads share every K/V byte that is read.
 //  * Keys are read straight from the cache by block (or token) id in chunks of
-//    32: nothing is gathered or materialised.  Each chunk computes
+//    32: nothing is gathered or materialised.  Each wave software-pipelines its
+//    chunks: the next chunk's K loads are issued before the current chunk is
+//    computed, and a chunk's V loads before its score MFMAs.  Each chunk computes
 //    S^T = K Q^T (keys x heads), so every lane already holds P^T in the layout
 //    the second MFMA (O^T = V^T P^T) wants; V is transposed once through a
 //    per-wave LDS tile with 8-byte writes.
@@ -24,7 +26,6 @@ namespace msa {
 namespace {
 
 constexpr int kAttWaves = 4;
-constexpr int kPair = 2;                         // chunks a wave loads at once
 constexpr int kVtPitch = kChunk + 4;             // bf16 per transposed-V row (one dim)
 constexpr int kPartFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;   // acc + (m, l)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -41,6 +42,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
+
+struct ChunkBuf {
+    bf16x8 kA[2][4];      // K operand of the chunk's two 16-key tiles
+    int vrow[2][4];       // cache rows of the V values this lane transposes
+    uint32_t valid;       // bit kk: key kk of the chunk is visible
+};
+
+// Largest id list one split stages: 4096 DSA tokens (or 64 MSA blocks).
+constexpr int kMaxSplitEntries = 4096;
 
 struct KernelArgs {
     AttendArgs a;
@@ -71,7 +81,8 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     const int l4 = lane >> 4;
 
     __shared__ LdsAttend lds;
-    __shared__ int32_t ids[kAttWaves][kPair * kChunk];
+    __shared__ int32_t ids[kAttWaves][kChunk];
+    __shared__ int32_t sel_s[kMaxSplitEntries];   // this split's selected ids
 
     const int64_t s = a.stream ? a.stream[i] : a.stream0;
     const int p = a.pos ? a.pos[i] : a.pos0 + static_cast<int>(i);
@@ -80,6 +91,14 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     const uint16_t* kg = a.k + (s * a.cap * kGroups + g) * kHeadDim;   // row t at + t*kGroups*kHeadDim
     const uint16_t* vg = a.v + (s * a.cap * kGroups + g) * kHeadDim;
     constexpr int64_t kRow = kGroups * kHeadDim;
+
+    const int c_begin = sp * ka.chunks_per_split;
+    const int c_end = min(c_begin + ka.chunks_per_split, ka.n_chunks);
+    // stage the split's ids once: blocks c/4 (MSA) or tokens 32c.. (DSA)
+    const int e_begin = kTokenIds ? c_begin * kChunk : c_begin / 4;
+    const int e_end = kTokenIds ? min(c_end * kChunk, a.sel_len) : (c_end + 3) / 4;
+    for (int e = e_begin + static_cast<int>(threadIdx.x); e < e_end; e += 256) sel_s[e - e_begin] = sel[e];
+    __syncthreads();
 
     // Q^T operand: B[k = dim][n = head]; lane: head l16, dims 32*ks + 8*l4 + 0..7
     bf16x8 qb[4];
@@ -94,147 +113,148 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     f32x4 acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int c_begin = sp * ka.chunks_per_split;
-    const int c_end = min(c_begin + ka.chunks_per_split, ka.n_chunks);
     uint16_t* vt = lds.vt[wave];
 
-    // Each wave takes kPair consecutive chunks at a time and issues all their
-    // K/V loads before computing, so 32 KiB per wave are in flight.
-    for (int c0 = c_begin + kPair * wave; c0 < c_end; c0 += kPair * kAttWaves) {
-        // token id of key (lane & 31) of chunk c0 + (lane >> 5); -1: padding or not visible
-        int tok = -1;
-        {
-            const int c = c0 + (lane >> 5);
-            const int kk = lane & 31;
-            if (c < c_end) {
-                if (kTokenIds) {
-                    const int e = c * kChunk + kk;
-                    tok = e < a.sel_len ? sel[e] : -1;
-                } else {
-                    const int blk = sel[c >> 2];
-                    tok = (blk < 0 || blk > p / kBlock) ? -1 : blk * kBlock + (c & 3) * kChunk + kk;
-                }
+    // Issue the K loads of chunk c into `buf` and note its V rows (nothing is
+    // waited on here).
+    auto fetch = [&](int c, ChunkBuf& buf) {
+        int tok = -1;                    // key `lane` of the chunk; -1: padding or not visible
+        if (lane < kChunk) {
+            if (kTokenIds) {
+                const int e = c * kChunk + lane;
+                tok = e < a.sel_len ? sel_s[e - e_begin] : -1;
+            } else {
+                const int blk = sel_s[(c >> 2) - e_begin];
+                tok = (blk < 0 || blk > p / kBlock) ? -1 : blk * kBlock + (c & 3) * kChunk + lane;
             }
             if (tok > p) tok = -1;
             ids[wave][lane] = tok;
         }
-        const uint64_t valid2 = __ballot(tok >= 0);
-        if (valid2 == 0) continue;                 // wave-uniform
+        buf.valid = static_cast<uint32_t>(__ballot(lane < kChunk && tok >= 0));
+        if (buf.valid == 0) return;      // wave-uniform
         wave_lds_sync();
-
-        // issue every load of the pair first
-        bf16x8 kA[kPair][2][4];
-        u32x4 vr[kPair][2][4];
 #pragma unroll
-        for (int h2 = 0; h2 < kPair; ++h2) {
-            const int32_t* cid = ids[wave] + kChunk * h2;
+        for (int t = 0; t < 2; ++t) {    // K operand: A = K (m = key, k = dim)
+            int row = ids[wave][16 * t + l16];
+            row = row < 0 ? p : row;     // masked later; any valid row is safe to read
+            const uint16_t* kr = kg + row * kRow + 8 * l4;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {      // K operand: A = K (m = key, k = dim)
-                int row = cid[16 * t + l16];
-                row = row < 0 ? p : row;       // masked below; any valid row is safe to read
-                const uint16_t* kr = kg + row * kRow + 8 * l4;
+            for (int ks = 0; ks < 4; ++ks) buf.kA[t][ks] = *reinterpret_cast<const bf16x8*>(kr + 32 * ks);
+        }
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) kA[h2][t][ks] = *reinterpret_cast<const bf16x8*>(kr + 32 * ks);
-            }
+        for (int h = 0; h < 2; ++h) {    // V rows: keys 4*qd + u (qd = l4, 4 + l4)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {      // V: keys 4*qd + u, dims 8*l16 + 0..7 (qd = l4, 4 + l4)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    int row = cid[4 * (l4 + 4 * h) + u];
-                    row = row < 0 ? p : row;   // weight is exactly 0; the value only needs to be finite
-                    vr[h2][h][u] = *reinterpret_cast<const u32x4*>(vg + row * kRow + 8 * l16);
-                }
+            for (int u = 0; u < 4; ++u) {
+                const int row = ids[wave][4 * (l4 + 4 * h) + u];
+                buf.vrow[h][u] = row < 0 ? p : row;   // weight is exactly 0; the value only needs to be finite
             }
         }
+        wave_lds_sync();                 // ids is rewritten by the next fetch
+    };
 
+    // Online-softmax update with the chunk held in `buf`.
+    auto compute = [&](ChunkBuf& buf) {
+        const uint32_t valid = buf.valid;
+        if (valid == 0) return;          // wave-uniform
+        // V loads first: their latency overlaps the score MFMAs and the softmax
+        u32x4 vr[2][4];
 #pragma unroll
-        for (int h2 = 0; h2 < kPair; ++h2) {
-            const uint32_t valid = static_cast<uint32_t>(valid2 >> (kChunk * h2));
-            if (valid == 0) continue;          // wave-uniform
-
-            // S^T = K Q^T; lane gets keys 16t + 4*l4 + r of head l16
-            f32x4 st[2];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < 4; ++u)
+                vr[h][u] = *reinterpret_cast<const u32x4*>(vg + buf.vrow[h][u] * kRow + 8 * l16);
+        // S^T = K Q^T; lane gets keys 16t + 4*l4 + r of head l16
+        f32x4 st[2];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) st[t] = mfma_16x16x32_bf16(kA[h2][t][ks], qb[ks], st[t]);
-            }
-
-            // transpose V into vt[dim][key] (8-byte writes of 4 consecutive keys)
+        for (int t = 0; t < 2; ++t) {
+            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int key0 = 4 * (l4 + 4 * h);
-#pragma unroll
-                for (int m2 = 0; m2 < 4; ++m2) {       // dims 8*l16 + 2*m2, +1
-                    const uint32_t w0 = vr[h2][h][0][m2], w1 = vr[h2][h][1][m2];
-                    const uint32_t w2 = vr[h2][h][2][m2], w3 = vr[h2][h][3][m2];
-                    // even dim: low halves; odd dim: high halves
-                    const uint32_t e01 = __builtin_amdgcn_perm(w1, w0, 0x05040100);
-                    const uint32_t e23 = __builtin_amdgcn_perm(w3, w2, 0x05040100);
-                    const uint32_t o01 = __builtin_amdgcn_perm(w1, w0, 0x07060302);
-                    const uint32_t o23 = __builtin_amdgcn_perm(w3, w2, 0x07060302);
-                    const int d = 8 * l16 + 2 * m2;
-                    *reinterpret_cast<uint2*>(vt + d * kVtPitch + key0) = make_uint2(e01, e23);
-                    *reinterpret_cast<uint2*>(vt + (d + 1) * kVtPitch + key0) = make_uint2(o01, o23);
-                }
-            }
-
-            // online softmax over this chunk for head l16
-            float x[8];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int kk = 16 * t + 4 * l4 + r;
-                    x[4 * t + r] = ((valid >> kk) & 1) ? st[t][r] * qk_scale : -INFINITY;
-                }
-            }
-            float cm = x[0];
-#pragma unroll
-            for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
-            cm = max_xor32(max_xor16(cm));
-            const float m_new = fmaxf(m_run, cm);      // finite: the chunk has a visible key
-            const float alpha = exp2f(m_run - m_new);  // 0 on the first chunk (m_run = -inf)
-            float pr[8];
-            float rs = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                pr[j] = exp2f(x[j] - m_new);
-                rs += pr[j];
-            }
-            rs = sum_xor32(sum_xor16(rs));
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-
-            // P^T operand (B: k = key, n = head); k-slot 8*l4 + j holds key
-            // 4*l4 + j (j < 4) or 16 + 4*l4 + (j - 4)
-            u32x4 pw;
-            pw[0] = pack_bf16x2(pr[0], pr[1]);
-            pw[1] = pack_bf16x2(pr[2], pr[3]);
-            pw[2] = pack_bf16x2(pr[4], pr[5]);
-            pw[3] = pack_bf16x2(pr[6], pr[7]);
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-
-            wave_lds_sync();
-            // O^T += V^T P^T; A = V^T[m = dim 16*dt + l16][k-slot as above]
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const uint16_t* row = vt + (16 * dt + l16) * kVtPitch;
-                const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * l4);
-                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 + 4 * l4);
-                u32x4 vw;
-                vw[0] = lo.x;
-                vw[1] = lo.y;
-                vw[2] = hi.x;
-                vw[3] = hi.y;
-                acc[dt] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pb, acc[dt]);
-            }
-            wave_lds_sync();                       // vt is rewritten by the next chunk
+            for (int ks = 0; ks < 4; ++ks) st[t] = mfma_16x16x32_bf16(buf.kA[t][ks], qb[ks], st[t]);
         }
+        // transpose V into vt[dim][key] (8-byte writes of 4 consecutive keys)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int key0 = 4 * (l4 + 4 * h);
+#pragma unroll
+            for (int m2 = 0; m2 < 4; ++m2) {       // dims 8*l16 + 2*m2, +1
+                const uint32_t w0 = vr[h][0][m2], w1 = vr[h][1][m2];
+                const uint32_t w2 = vr[h][2][m2], w3 = vr[h][3][m2];
+                // even dim: low halves; odd dim: high halves
+                const uint32_t e01 = __builtin_amdgcn_perm(w1, w0, 0x05040100);
+                const uint32_t e23 = __builtin_amdgcn_perm(w3, w2, 0x05040100);
+                const uint32_t o01 = __builtin_amdgcn_perm(w1, w0, 0x07060302);
+                const uint32_t o23 = __builtin_amdgcn_perm(w3, w2, 0x07060302);
+                const int d = 8 * l16 + 2 * m2;
+                *reinterpret_cast<uint2*>(vt + d * kVtPitch + key0) = make_uint2(e01, e23);
+                *reinterpret_cast<uint2*>(vt + (d + 1) * kVtPitch + key0) = make_uint2(o01, o23);
+            }
+        }
+        // online softmax over this chunk for head l16
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kk = 16 * t + 4 * l4 + r;
+                x[4 * t + r] = ((valid >> kk) & 1) ? st[t][r] * qk_scale : -INFINITY;
+            }
+        }
+        float cm = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
+        cm = max_xor32(max_xor16(cm));
+        const float m_new = fmaxf(m_run, cm);      // finite: the chunk has a visible key
+        const float alpha = exp2f(m_run - m_new);  // 0 on the first chunk (m_run = -inf)
+        float pr[8];
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            pr[j] = exp2f(x[j] - m_new);
+            rs += pr[j];
+        }
+        rs = sum_xor32(sum_xor16(rs));
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+        // P^T operand (B: k = key, n = head); k-slot 8*l4 + j holds key
+        // 4*l4 + j (j < 4) or 16 + 4*l4 + (j - 4)
+        u32x4 pw;
+        pw[0] = pack_bf16x2(pr[0], pr[1]);
+        pw[1] = pack_bf16x2(pr[2], pr[3]);
+        pw[2] = pack_bf16x2(pr[4], pr[5]);
+        pw[3] = pack_bf16x2(pr[6], pr[7]);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+        wave_lds_sync();
+        // O^T += V^T P^T; A = V^T[m = dim 16*dt + l16][k-slot as above]
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint16_t* row = vt + (16 * dt + l16) * kVtPitch;
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * l4);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 + 4 * l4);
+            u32x4 vw;
+            vw[0] = lo.x;
+            vw[1] = lo.y;
+            vw[2] = hi.x;
+            vw[3] = hi.y;
+            acc[dt] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pb, acc[dt] * alpha);
+        }
+        wave_lds_sync();                           // vt is rewritten by the next chunk
+    };
+
+    // Software pipeline over this wave's chunks c_begin + wave + kAttWaves*n:
+    // the K loads of the next chunk are in flight while the current one computes.
+    ChunkBuf bufA, bufB;
+    int c = c_begin + wave;
+    if (c < c_end) fetch(c, bufA);
+    while (c < c_end) {
+        int cn = c + kAttWaves;
+        if (cn < c_end) fetch(cn, bufB);
+        compute(bufA);
+        c = cn;
+        if (c >= c_end) break;
+        cn = c + kAttWaves;
+        if (cn < c_end) fetch(cn, bufA);
+        compute(bufB);
+        c = cn;
     }
 
     // ---- merge the four waves (lane holds O^T[dim 16*dt + 4*l4 + r][head l16])
@@ -317,9 +337,10 @@ int num_chunks(int sel_len, int unit) {
 int attend_num_splits(int64_t n_q, int sel_len, int unit) {
     const int64_t pairs = n_q * kGroups;
     const int n_chunks = num_chunks(sel_len, unit);
-    // aim for >= 1024 workgroups, with a chunk pair for every wave of a split
-    int64_t want = (1024 + pairs - 1) / pairs;
-    const int64_t cap = n_chunks / (kAttWaves * kPair) > 0 ? n_chunks / (kAttWaves * kPair) : 1;
+    // aim for >= 512 workgroups (measured best on the 32-stream decode), with
+    // two chunks for every wave of a split
+    int64_t want = (512 + pairs - 1) / pairs;
+    const int64_t cap = n_chunks / (2 * kAttWaves) > 0 ? n_chunks / (2 * kAttWaves) : 1;
     if (want > cap) want = cap;
     if (want > 16) want = 16;
     if (want < 1) want = 1;

@@ -7,7 +7,7 @@
 // This file holds the decode form; the prefill form (matrix cores) is in
 // prefill_scores.hip.
 //
-// Decode: one workgroup per (query, key block).  The F32 index-key cache is
+// Decode: one workgroup per (query, two key blocks).  The F32 index-key cache is
 // streamed once with 128-bit loads; each 16-lane DPP row of a wavefront owns
 // one group's 512-byte slice of a token row, so a token's four group scores
 // come out of one DPP row reduction each and no scores are materialised.
@@ -22,8 +22,10 @@ constexpr int kRowF4 = kGroups * kIdxDim / 4;   // 128 float4 per token row
 // ---------------------------------------------------------------------------
 // Decode scan
 // ---------------------------------------------------------------------------
-constexpr int kScanWaves = 4;
-constexpr int kScanTokensPerWave = kBlock / kScanWaves;   // 32
+constexpr int kScanBlocksPerWg = 2;                       // key blocks per workgroup
+constexpr int kScanWavesPerBlock = 4;
+constexpr int kScanWaves = kScanBlocksPerWg * kScanWavesPerBlock;   // 8 waves, 512 threads
+constexpr int kScanTokensPerWave = kBlock / kScanWavesPerBlock;     // 32
 constexpr int kScanUnroll = 8;
 
 __device__ __forceinline__ float dot8(const f32x4& q0, const f32x4& q1, const f32x4& a,
@@ -39,54 +41,62 @@ __device__ __forceinline__ float dot8(const f32x4& q0, const f32x4& q1, const f3
     return d;
 }
 
-__global__ __launch_bounds__(256) void block_scores_decode_kernel(
+// One workgroup per (query, pair of key blocks); four waves per block, 32
+// tokens each.  Index keys are read once with non-temporal 128-bit loads
+// (they are streamed, never re-read), 16 KiB per wave in flight.
+__global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
     const float* __restrict__ idx_k, int64_t cap, const float* __restrict__ idx_q,
     const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
-    float* __restrict__ bs, int64_t nblk_stride) {
+    float* __restrict__ bs, int64_t nblk_stride, int nblk) {
     const int64_t i = blockIdx.x;
-    const int b = blockIdx.y;
+    const int b0 = blockIdx.y * kScanBlocksPerWg;
     const int p = q_pos[i];
     const int loc = p / kBlock;
-    float* out = bs + i * kGroups * nblk_stride + b;
-    if (b > loc) {
-        if (threadIdx.x < kGroups) out[threadIdx.x * nblk_stride] = -INFINITY;
-        return;
-    }
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;     // the DPP row of this lane = its group
     const int c = lane & 15;     // lane's 16-byte column within the group's first/second half
-    const f32x4* qrow = reinterpret_cast<const f32x4*>(idx_q + i * kGroups * kIdxDim);
-    const f32x4 q0 = qrow[g * 32 + c];
-    const f32x4 q1 = qrow[g * 32 + 16 + c];
-    const f32x4* rows = reinterpret_cast<const f32x4*>(
-        idx_k + (static_cast<int64_t>(q_stream[i]) * cap + static_cast<int64_t>(b) * kBlock) *
-                    (kGroups * kIdxDim)) + g * 32 + c;
-    const int t_begin = wave * kScanTokensPerWave;
-    const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);
+    const int b = b0 + wave / kScanWavesPerBlock;   // this wave's key block
     float m = -INFINITY;
-    int t = t_begin;
-    for (; t + kScanUnroll <= t_end; t += kScanUnroll) {
-        f32x4 a[kScanUnroll], bb[kScanUnroll];
+    if (b < nblk && b <= loc) {
+        const f32x4* qrow = reinterpret_cast<const f32x4*>(idx_q + i * kGroups * kIdxDim);
+        const f32x4 q0 = qrow[g * 32 + c];
+        const f32x4 q1 = qrow[g * 32 + 16 + c];
+        const f32x4* rows = reinterpret_cast<const f32x4*>(
+            idx_k + (static_cast<int64_t>(q_stream[i]) * cap + static_cast<int64_t>(b) * kBlock) *
+                        (kGroups * kIdxDim)) + g * 32 + c;
+        const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
+        const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+        int t = t_begin;
+        for (; t + kScanUnroll <= t_end; t += kScanUnroll) {
+            f32x4 a[kScanUnroll], bb[kScanUnroll];
 #pragma unroll
-        for (int u = 0; u < kScanUnroll; ++u) {
-            a[u] = __builtin_nontemporal_load(rows + (t + u) * kRowF4);
-            bb[u] = __builtin_nontemporal_load(rows + (t + u) * kRowF4 + 16);
+            for (int u = 0; u < kScanUnroll; ++u) {
+                a[u] = __builtin_nontemporal_load(rows + (t + u) * kRowF4);
+                bb[u] = __builtin_nontemporal_load(rows + (t + u) * kRowF4 + 16);
+            }
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; ++u) m = fmaxf(m, row16_sum(dot8(q0, q1, a[u], bb[u])));
         }
-#pragma unroll
-        for (int u = 0; u < kScanUnroll; ++u) m = fmaxf(m, row16_sum(dot8(q0, q1, a[u], bb[u])));
-    }
-    for (; t < t_end; ++t) {
-        const f32x4 a = rows[t * kRowF4];
-        const f32x4 bb = rows[t * kRowF4 + 16];
-        m = fmaxf(m, row16_sum(dot8(q0, q1, a, bb)));
+        for (; t < t_end; ++t) {
+            const f32x4 a = rows[t * kRowF4];
+            const f32x4 bb = rows[t * kRowF4 + 16];
+            m = fmaxf(m, row16_sum(dot8(q0, q1, a, bb)));
+        }
     }
     __shared__ float red[kScanWaves][kGroups];
     if (c == 0) red[wave][g] = m;
     __syncthreads();
-    if (threadIdx.x < kGroups) {
-        const int gg = threadIdx.x;
-        out[gg * nblk_stride] = fmaxf(fmaxf(red[0][gg], red[1][gg]), fmaxf(red[2][gg], red[3][gg]));
+    if (threadIdx.x < kGroups * kScanBlocksPerWg) {
+        const int gg = threadIdx.x % kGroups;
+        const int bl = threadIdx.x / kGroups;
+        const int bb2 = b0 + bl;
+        if (bb2 < nblk) {
+            float r = -INFINITY;    // stays -inf for blocks past the query's own block
+#pragma unroll
+            for (int w = 0; w < kScanWavesPerBlock; ++w) r = fmaxf(r, red[bl * kScanWavesPerBlock + w][gg]);
+            bs[(i * kGroups + gg) * nblk_stride + bb2] = r;
+        }
     }
 }
 
@@ -95,8 +105,9 @@ __global__ __launch_bounds__(256) void block_scores_decode_kernel(
 hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
                                       int64_t nblk_stride, hipStream_t s) {
-    hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), nblk), dim3(256),
-                       0, s, c.idx_k, c.cap, idx_q, stream, pos, bs, nblk_stride);
+    const unsigned ny = static_cast<unsigned>((nblk + kScanBlocksPerWg - 1) / kScanBlocksPerWg);
+    hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
+                       0, s, c.idx_k, c.cap, idx_q, stream, pos, bs, nblk_stride, nblk);
     return hipGetLastError();
 }
 
