@@ -209,3 +209,46 @@ def test_prefill_full_4096_at_32k_sampled():
     edges = [0, 1, 127, 128, 129, 255, 256, 2047, 2048, 4094, 4095]
     sample = sorted(set(edges) | set(rng.choice(wl.n_q, 37, replace=False).tolist()))
     _prefill_parity(wl, sample=sample)
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """A captured decode step (append, select, attend) replayed several times,
+    with eager work and synchronisations in between, reproduces the eager
+    result bit for bit every time (no memset nodes are recorded)."""
+    wl = W.decode_workload("graph", 4, 3000)
+    dims = M.msa_dims(16, W.SCALE)
+    gw = GpuWorkload(wl)
+    h, qs = gw.host, gw.qs
+    s_np, p_np = qs["stream"], qs["pos"]
+    new_idx = dev(h["idx_k"][s_np, p_np])
+    from _gpu_common import dev_bits
+    new_k = dev_bits(h["k"][s_np, p_np], torch.bfloat16)
+    new_v = dev_bits(h["v"][s_np, p_np], torch.bfloat16)
+    idx_q = dev(qs["idx_q"])
+    sel = torch.empty((4, 4, 16), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty((4, 4), dtype=torch.int32, device=DEV)
+    out = torch.empty((4, 64, 128), dtype=torch.float32, device=DEV)
+    ws_s = gw.ws(dims, M.MSA_OP_SELECT)
+    ws_a = gw.ws(dims, M.MSA_OP_ATTEND_DECODE)
+
+    def step():
+        M.msa_index_append(dims, gw.cache, gw.stream, gw.pos, wl.max_pos, new_idx, new_k, new_v)
+        M.msa_select(dims, gw.cache, idx_q, gw.stream, gw.pos, wl.max_pos, sel, n_sel, ws_s)
+        M.msa_attend_decode(dims, gw.cache, gw.q, gw.stream, gw.pos, wl.max_pos, sel, out, ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel = out.clone(), sel.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        sel.fill_(-7)
+        ws_a.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sel, ref_sel), f"replay {r}: selection differs"
+        assert torch.equal(out, ref_out), f"replay {r}: output differs"
+        _ = (out * 2).sum().item()      # eager work between replays
