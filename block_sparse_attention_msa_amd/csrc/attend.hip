@@ -57,7 +57,6 @@ struct KernelArgs {
     int n_split;
     int n_chunks;          // chunks of 32 keys per (query, group)
     int chunks_per_split;
-    int range_blocks;      // > 0: split sp takes the blocks [sp, sp + 1) * range_blocks
 };
 
 union LdsAttend {
@@ -72,25 +71,10 @@ union LdsAttend {
 template <bool kTokenIds>
 __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     const AttendArgs& a = ka.a;
-    int sp, g;
-    int64_t i;
-    if (ka.range_blocks == 0) {
-        const int64_t wg = blockIdx.x;             // ((query * kGroups) + group) * n_split + split
-        sp = static_cast<int>(wg % ka.n_split);
-        g = static_cast<int>((wg / ka.n_split) % kGroups);
-        i = wg / (static_cast<int64_t>(ka.n_split) * kGroups);
-    } else {
-        // Workgroups are handed to the 8 XCDs round-robin by id; XCD x works
-        // through the (group, block range) pairs x, x + 8, ... one at a time,
-        // every query of the chunk for each, so its L2 holds one group's range.
-        const int x = static_cast<int>(blockIdx.x % 8);
-        const int64_t kk = blockIdx.x / 8;
-        const int pair = x + 8 * static_cast<int>(kk / a.n_q);   // = group * n_split + range
-        if (pair >= kGroups * ka.n_split) return;
-        i = kk % a.n_q;
-        g = pair / ka.n_split;
-        sp = pair % ka.n_split;
-    }
+    const int64_t wg = blockIdx.x;                 // ((query * kGroups) + group) * n_split + split
+    const int sp = static_cast<int>(wg % ka.n_split);
+    const int g = static_cast<int>((wg / ka.n_split) % kGroups);
+    const int64_t i = wg / (static_cast<int64_t>(ka.n_split) * kGroups);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int l16 = lane & 15;
@@ -108,21 +92,8 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     const uint16_t* vg = a.v + (s * a.cap * kGroups + g) * kHeadDim;
     constexpr int64_t kRow = kGroups * kHeadDim;
 
-    int c_begin = sp * ka.chunks_per_split;
-    int c_end = min(c_begin + ka.chunks_per_split, ka.n_chunks);
-    if (!kTokenIds && ka.range_blocks > 0) {
-        // the selected ids are ascending (-1 padding last): this range's
-        // entries are a contiguous run
-        const int lo = sp * ka.range_blocks, hi = lo + ka.range_blocks;
-        int eb = 0, ee = 0;
-        for (int e = 0; e < a.sel_len; ++e) {
-            const int blk = sel[e];
-            eb += (blk >= 0 && blk < lo);
-            ee += (blk >= 0 && blk < hi);
-        }
-        c_begin = 4 * eb;
-        c_end = 4 * ee;
-    }
+    const int c_begin = sp * ka.chunks_per_split;
+    const int c_end = min(c_begin + ka.chunks_per_split, ka.n_chunks);
     // stage the split's ids once: blocks c/4 (MSA) or tokens 32c.. (DSA)
     const int e_begin = kTokenIds ? c_begin * kChunk : c_begin / 4;
     const int e_end = kTokenIds ? min(c_end * kChunk, a.sel_len) : (c_end + 3) / 4;
@@ -344,8 +315,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
     for (int sp = 0; sp < n_split; ++sp) {
         const float* part = part0 + sp * kPartFloats;
         const float ms = part[kHeadsPerGroup * kHeadDim + 2 * hh];
-        if (ms == -INFINITY) continue;             // no key of this (query, group) in the split
-        const float wt = exp2f(ms - M);
+        const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
         L += wt * part[kHeadsPerGroup * kHeadDim + 2 * hh + 1];
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0);
         const f32x4 a1 = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0 + 4);
@@ -383,38 +353,13 @@ size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit) {
     return static_cast<size_t>(n_q) * kGroups * n_split * kPartFloats * sizeof(float);
 }
 
-int prefill_num_ranges(int32_t max_pos) {
-    const int nblk = max_pos / kBlock + 1;
-    // one range per 64 blocks (4 MiB of one group's K/V): about an L2
-    return nblk <= 64 ? 1 : (nblk + 63) / 64;
-}
-
-size_t prefill_attend_ws_bytes(int64_t n_q, int32_t max_pos) {
-    const int r = prefill_num_ranges(max_pos);
-    if (r == 1) return 0;
-    return static_cast<size_t>(n_q) * kGroups * r * kPartFloats * sizeof(float);
-}
-
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     KernelArgs ka;
     ka.a = a;
+    ka.n_split = attend_num_splits(a.n_q, a.sel_len, a.unit);
     ka.n_chunks = num_chunks(a.sel_len, a.unit);
-    const bool ranged = a.unit == kBlock && a.stream == nullptr;   // prefill: one stream, pos0 + i
-    const int32_t max_pos = a.pos0 + static_cast<int>(a.n_q) - 1;
-    const int nblk = max_pos / kBlock + 1;
-    if (ranged && prefill_num_ranges(max_pos) > 1) {
-        ka.n_split = prefill_num_ranges(max_pos);
-        ka.range_blocks = (nblk + ka.n_split - 1) / ka.n_split;
-        ka.chunks_per_split = ka.n_chunks;
-    } else {
-        ka.n_split = ranged ? 1 : attend_num_splits(a.n_q, a.sel_len, a.unit);
-        ka.range_blocks = 0;
-        ka.chunks_per_split = (ka.n_chunks + ka.n_split - 1) / ka.n_split;
-    }
-    const unsigned n_wg = ka.range_blocks > 0
-                              ? static_cast<unsigned>(8 * ((kGroups * ka.n_split + 7) / 8) * a.n_q)
-                              : static_cast<unsigned>(a.n_q * kGroups * ka.n_split);
-    const dim3 grid(n_wg);
+    ka.chunks_per_split = (ka.n_chunks + ka.n_split - 1) / ka.n_split;
+    const dim3 grid(static_cast<unsigned>(a.n_q * kGroups * ka.n_split));
     if (a.unit == kBlock)
         hipLaunchKernelGGL(attend_kernel<false>, grid, dim3(256), 0, s, ka);
     else

@@ -160,10 +160,6 @@ struct AttendArgs {
 };
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
-// Prefill (stream == NULL): the selected blocks of each (query, group) are
-// split by block-id range, one range per 64 blocks, and the partials merged.
-int prefill_num_ranges(int32_t max_pos);
-size_t prefill_attend_ws_bytes(int64_t n_q, int32_t max_pos);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);

@@ -118,9 +118,8 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
             if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;
             return select_ws(n_q, max_pos);
         case MSA_OP_ATTEND_DECODE:
-            return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
         case MSA_OP_ATTEND_PREFILL:
-            return align256(msa::prefill_attend_ws_bytes(n_q, max_pos));
+            return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
         case DSA_OP_SELECT:
             return align256(msa::dsa_select_ws_bytes(n_q, max_pos));
         case DSA_OP_ATTEND_DECODE:
@@ -264,7 +263,7 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out}));
-    const size_t need = msa::prefill_attend_ws_bytes(n_q, static_cast<int32_t>(pos0 + n_q - 1));
+    const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, kBlock);
     if (need) {
         MSA_TRY(check_ptrs({d_ws}));
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
