@@ -84,8 +84,8 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     __shared__ int32_t ids[kAttWaves][kChunk];
     __shared__ int32_t sel_s[kMaxSplitEntries];   // this split's selected ids
 
-    const int64_t s = a.stream ? a.stream[i] : a.stream0;
-    const int p = a.pos ? a.pos[i] : a.pos0 + static_cast<int>(i);
+    const int64_t s = a.stream[i];
+    const int p = a.pos[i];
     const int32_t* sel = a.sel + i * static_cast<int64_t>(a.sel_len) * (kTokenIds ? 1 : kGroups) +
                          g * a.sel_g_stride;
     const uint16_t* kg = a.k + (s * a.cap * kGroups + g) * kHeadDim;   // row t at + t*kGroups*kHeadDim

@@ -145,10 +145,8 @@ struct AttendArgs {
     const uint16_t* v;
     int64_t cap;
     const uint16_t* q;
-    const int32_t* stream;   // per query, or NULL with stream0 for prefill
-    const int32_t* pos;      // per query, or NULL with pos0 for prefill
-    int32_t stream0;
-    int32_t pos0;
+    const int32_t* stream;   // per query
+    const int32_t* pos;      // per query
     int64_t n_q;
     const int32_t* sel;
     int sel_len;             // entries per (query, group)
@@ -161,6 +159,11 @@ struct AttendArgs {
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// Prefill attention for the consecutive positions pos0 .. pos0 + n_q - 1 of
+// one stream (MSA blocks).
+hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
+                                 int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
+                                 float scale, float* out, hipStream_t s);
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
 hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,

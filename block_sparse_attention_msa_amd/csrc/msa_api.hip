@@ -118,8 +118,9 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
             if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;
             return select_ws(n_q, max_pos);
         case MSA_OP_ATTEND_DECODE:
-        case MSA_OP_ATTEND_PREFILL:
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
+        case MSA_OP_ATTEND_PREFILL:
+            return 0;
         case DSA_OP_SELECT:
             return align256(msa::dsa_select_ws_bytes(n_q, max_pos));
         case DSA_OP_ATTEND_DECODE:
@@ -248,7 +249,7 @@ msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
         MSA_TRY(check_ptrs({d_ws}));
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
     }
-    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, 0, 0, n_q, d_sel,
+    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, n_q, d_sel,
                       dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
@@ -263,14 +264,11 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out}));
-    const size_t need = msa::attend_ws_bytes(n_q, dims->top_k, kBlock);
-    if (need) {
-        MSA_TRY(check_ptrs({d_ws}));
-        if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    }
-    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, nullptr, nullptr, stream, pos0, n_q, d_sel,
-                      dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws};
-    return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
+    (void)d_ws;
+    (void)ws_bytes;
+    return hip_status(msa::launch_prefill_attend(cache->k, cache->v, cache->cap, d_q, stream, pos0, n_q, d_sel,
+                                                 dims->top_k, dims->scale, d_out,
+                                                 static_cast<hipStream_t>(hip_stream)));
 }
 
 msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q_idx,
@@ -304,7 +302,7 @@ msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
         MSA_TRY(check_ptrs({d_ws}));
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
     }
-    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, 0, 0, n_q, d_sel,
+    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, n_q, d_sel,
                       dims->top_k, 0, 1, dims->scale, d_out, d_ws};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
 }

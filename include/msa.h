@@ -226,9 +226,10 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
  * Prefill form of msa_attend_decode ([MSA-PR] Implementation, batch path:
  * block-level mask of the selection combined with the causal mask): n_q
  * consecutive queries at positions pos0 .. pos0 + n_q - 1 of `stream`.
- * Same arguments and output as msa_attend_decode.  Workspace:
- * MSA_OP_ATTEND_PREFILL (0 bytes once n_q * n_group >= 1024, when every
- * (query, group) runs in one workgroup; d_ws may then be NULL).
+ * Same arguments and output as msa_attend_decode.  Cache rows up to
+ * pos0 + n_q - 1 must be written (the chunk's own keys included).  Needs no
+ * workspace (MSA_OP_ATTEND_PREFILL is 0 bytes): d_ws and ws_bytes are
+ * ignored and may be NULL / 0.
  */
 MSA_API msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
                               int32_t stream, int32_t pos0, int64_t n_q, const int32_t* d_sel,

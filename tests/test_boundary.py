@@ -136,7 +136,8 @@ def test_workspace_sizes(L):
     # attention partials: per (query, group, split) 16 heads x (128 + 2) floats
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 0   # no split at 4096 queries
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 0   # prefill attention needs none
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 1, 100) == 0
     dd = M.dsa_dims()
     assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
     with pytest.raises(M.MsaError):
