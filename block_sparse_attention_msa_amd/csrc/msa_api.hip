@@ -263,6 +263,7 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
+    if (nblk_of(static_cast<int32_t>(pos0 + n_q - 1)) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out}));
     (void)d_ws;
     (void)ws_bytes;

@@ -103,6 +103,11 @@ def test_prefill_range_checks(L):
                                        None)
     assert g(11) == RANGE
     assert g(0) == OK
+    # more than 4096 blocks of 128 keys are beyond prefill attention's block masks
+    big = _cache(cap=4097 * 128, n_stream=1)
+    h = lambda pos0, n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(big), A, 0, pos0, n, A, A, A, 0, None)
+    assert h(4096 * 128 - 8, 8) != UNSUP      # last block 4095: accepted (fails later only for want of a GPU)
+    assert h(4096 * 128 - 8, 9) == UNSUP
 
 
 def test_append_validation(L):
