@@ -13,7 +13,9 @@ of the two is reported when the replay reproduces the eager output.
 Also measured in the same run and reported under "extra": the indexer scan
 and decode attention GB/s, the 4096-query prefill chunk at positions
 28672..32767 (append + MFMA block scores + top-16 + block-sparse attention,
-prefill tok/s), and the DSA lightning-indexer decode (16 streams x 65536).
+prefill tok/s; plus the attention alone on a selection shared by every 16
+consecutive queries, the overlap real text shows), and the DSA
+lightning-indexer decode (16 streams x 65536).
 
 `roofline` is the dominant kernel (the decode indexer scan): algorithmic bytes
 per launch / mean launch time from HIP events recorded on the stream the
@@ -346,6 +348,31 @@ def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10):
         att_flop += keys * 64 * 128 * 4
     log(f"[bench] prefill: append {seg[0] * 1e3:.1f} select {seg[1] * 1e3:.1f} attend {seg[2] * 1e3:.1f} us "
         f"-> {n_q / (total * 1e-3):.0f} tok/s")
+
+    # The same attention call on a selection where every 16 consecutive queries
+    # share their 15 non-local blocks (drawn uniformly from the blocks before
+    # the chunk): the independent Gaussian indexer inputs above give
+    # neighbouring queries almost disjoint selections, real text gives them
+    # largely shared ones.  Same keys per query, so the same FLOP count.
+    rng = np.random.default_rng(20260101)
+    n_tile = n_q // 16
+    shared = np.stack([np.stack([rng.choice(pos0 // 128, 15, replace=False) for _ in range(4)])
+                       for _ in range(n_tile)])                      # [tile][group][15]
+    loc_ids = (np.arange(pos0, pos0 + n_q) // 128).astype(np.int64)
+    sel_sh = np.concatenate([np.repeat(shared, 16, axis=0), np.broadcast_to(loc_ids[:, None, None], (n_q, 4, 1))],
+                            axis=2)
+    sel_sh = tens(np.sort(sel_sh, axis=2).astype(np.int32))
+    M.msa_attend_prefill(dims, cache, q, 0, pos0, sel_sh, out, ws_att)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        M.msa_attend_prefill(dims, cache, q, 0, pos0, sel_sh, out, ws_att)
+    e1.record()
+    torch.cuda.synchronize()
+    t_sh = e0.elapsed_time(e1) / iters
+    log(f"[bench] prefill attention, selections shared by each 16 consecutive queries: {t_sh * 1e3:.1f} us "
+        f"({att_flop / (t_sh * 1e-3) / 1e12:.0f} TFLOP/s)")
     return {
         "prefill_tok_s": round(n_q / (total * 1e-3), 1),
         "prefill_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
@@ -354,6 +381,8 @@ def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10):
         "prefill_indexer_frac_fp32_mfma": round(idx_flop / (seg[1] * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
         "prefill_attend_TFLOPs": round(att_flop / (seg[2] * 1e-3) / 1e12, 2),
         "prefill_attend_frac_bf16_mfma": round(att_flop / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "prefill_attend_shared16_us": round(t_sh * 1e3, 2),
+        "prefill_attend_shared16_frac_bf16_mfma": round(att_flop / (t_sh * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
     }
 
 

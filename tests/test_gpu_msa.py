@@ -203,6 +203,32 @@ def test_prefill_second_stream_cache_edge(top_k):
     _prefill_parity(wl)
 
 
+def test_prefill_attention_shared_selection():
+    # every 16 consecutive queries share their 15 non-local blocks (the overlap
+    # real text shows), so most staged blocks serve many queries at once
+    wl = W.prefill_workload("pf_shared", 3000, 2500, 300)
+    log(f"[msa prefill] {wl.name}: shared selections")
+    dims = M.msa_dims(16, W.SCALE)
+    gw = GpuWorkload(wl)
+    gw.append_own_rows()
+    n_q, pos0 = wl.n_q, wl.pos[0]
+    rng = np.random.default_rng(7)
+    loc = np.arange(pos0, pos0 + n_q) // 128
+    sel = np.empty((n_q, 4, 16), np.int32)
+    for t0 in range(0, n_q, 16):
+        for g in range(4):
+            others = rng.choice(pos0 // 128, 15, replace=False)
+            for i in range(t0, min(t0 + 16, n_q)):
+                sel[i, g] = np.sort(np.append(others, loc[i]))
+    out = torch.empty((n_q, 64, 128), dtype=torch.float32, device=DEV)
+    M.msa_attend_prefill(dims, gw.cache, gw.q, wl.stream[0], pos0, dev(sel), out, None)
+    torch.cuda.synchronize()
+    o_out = oracle.sparse_attend(gw.host["k"], gw.host["v"], gw.qs["stream"], gw.qs["pos"], gw.qs["q"], sel,
+                                 unit=128, scale=W.SCALE)
+    wa, wr = check_attention(out.cpu().numpy(), o_out)
+    log(f"  attention: max-abs {wa:.3e}, rel-L2 {wr:.3e}")
+
+
 def test_prefill_full_4096_at_32k_sampled():
     wl = W.CONFIGS["prefill_4096_at_32k"]
     rng = np.random.default_rng(0)
