@@ -160,10 +160,11 @@ int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 // Prefill attention for the consecutive positions pos0 .. pos0 + n_q - 1 of
-// one stream (MSA blocks).
+// one stream (MSA blocks); ws holds the per-tile step lists.
+size_t prefill_attend_ws_bytes(int64_t n_q, int top_k);
 hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
                                  int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
-                                 float scale, float* out, hipStream_t s);
+                                 float scale, float* out, void* ws, hipStream_t s);
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
 hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,

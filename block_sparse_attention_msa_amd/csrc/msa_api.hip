@@ -120,7 +120,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
         case MSA_OP_ATTEND_DECODE:
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
         case MSA_OP_ATTEND_PREFILL:
-            return 0;
+            return align256(msa::prefill_attend_ws_bytes(n_q, dims->top_k));
         case DSA_OP_SELECT:
             return align256(msa::dsa_select_ws_bytes(n_q, max_pos));
         case DSA_OP_ATTEND_DECODE:
@@ -264,11 +264,10 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     if (nblk_of(static_cast<int32_t>(pos0 + n_q - 1)) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
-    MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out}));
-    (void)d_ws;
-    (void)ws_bytes;
+    MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out, d_ws}));
+    if (ws_bytes < msa::prefill_attend_ws_bytes(n_q, dims->top_k)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(msa::launch_prefill_attend(cache->k, cache->v, cache->cap, d_q, stream, pos0, n_q, d_sel,
-                                                 dims->top_k, dims->scale, d_out,
+                                                 dims->top_k, dims->scale, d_out, d_ws,
                                                  static_cast<hipStream_t>(hip_stream)));
 }
 

@@ -5,52 +5,144 @@
 // (causal inside the query's own block); prefill and decode rank the same
 // block scores, so the selection semantics are those of decode.
 //
-// Design (gfx950).  A workgroup takes a tile of 16 consecutive queries of one
-// group and sweeps the UNION of their selected blocks in ascending block
-// order.  Each block's K and V (128 keys x 256 B each) are copied straight
-// from HBM into LDS with global_load_lds_dwordx4 -- no registers -- into one
-// of two buffers, so the next block streams in while the current one is
-// consumed by every query of the tile that selected it.  Rows are stored
-// with their 16-byte segments permuted by the row index, so the K operand
-// reads (16 rows, same columns) and the V reads are free of bank conflicts.
-// V stays row-major: ds_read_b64_tr_b16 hands each lane four consecutive keys
-// of one dim, which is the layout the P.V matrix-core operand wants.  Eight
-// waves each own two queries; their online-softmax states and 16-head x
-// 128-dim accumulators stay in registers for the whole sweep.
+// Design (gfx950).  A workgroup owns a tile of 32 consecutive queries of one
+// group and sweeps the union of their selected blocks in ascending block
+// order, so each block's K and V are fetched once per tile (and, since every
+// workgroup of an XCD sweeps the same group upward at the same time, mostly
+// from that XCD's L2).  A small pre-kernel turns the selections into each
+// tile's step list: one step per union block and up to kPb of the tile's
+// queries that selected it (a block chosen by more queries, e.g. the shared
+// local block, becomes several steps).
+//
+// Every step is spread evenly over all eight waves, whatever queries it
+// holds: for S = Q K^T wave w takes keys 16w .. 16w+15 of the block for every
+// query of the step and writes its bf16 probabilities to LDS; for O += P V
+// wave w owns output dims 16w .. 16w+15 of all 32 queries of the tile, so the
+// 16-head x 128-dim accumulators of the whole tile live in registers, one
+// 16 x 16 slice per wave and query.  The softmax needs no exchange of maxima:
+// each (query, head) uses one fixed reference for the whole sweep (its score
+// against its own key, always selected), and a block whose probabilities
+// would pass 2^64 is recomputed against a raised reference (rare).  Row sums
+// come from the matrix cores (a ones operand against the same bf16
+// probabilities), so the normalisation sums exactly the weights applied.
+// K, V and the step's queries are copied HBM -> LDS with global_load_lds (no
+// registers): V one step ahead into a second buffer, K and Q while the
+// previous step's products run.  Two barriers per step.
 #include "common.hpp"
 
 namespace msa {
 namespace {
 
 constexpr int kPaWaves = 8;
-constexpr int kSlots = 2;                   // queries per wave
-constexpr int kTileQ = kSlots * kPaWaves;   // queries per workgroup
 constexpr int kPaThreads = 64 * kPaWaves;
-constexpr int kRowBytes = kHeadDim * 2;     // one group's K or V row: 256 B = 16 segments
-constexpr int kBufBytes = kBlock * kRowBytes;   // 32 KiB per block for K (and for V)
-constexpr int kStageSlots = kBlock * kRowBytes / 16 / kPaWaves;   // 16-byte slots per wave and operand
+constexpr int kTq = 32;                     // queries per tile (one mask bit each)
+constexpr int kPb = 6;                      // queries per step
+constexpr int kRowBytes = kHeadDim * 2;     // one group's K or V row, one head's Q row: 256 B
+constexpr int kBufBytes = kBlock * kRowBytes;        // 32 KiB: K (or V) of one block
+constexpr int kQBytes = kHeadsPerGroup * kRowBytes;  // 4 KiB: one query's 16 heads
 constexpr float kLog2eP = 1.4426950408889634f;
-constexpr int kRing = 3;                    // operand register ring depth (steps)
-constexpr float kSlack = 8.f;              // lazy-rescale threshold, log2 units
+constexpr int kStepsThreads = 256;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // Rows are stored with their 16 segments permuted by seg ^ f(row & 15), f a
-// 4-bit rotate: f is one-to-one on 16 consecutive rows (the K operand reads
-// 16 rows at one segment) and f >> 1 is one-to-one on 8 consecutive rows (the
+// 4-bit rotate: f is one-to-one on 16 consecutive rows (operand reads of 16
+// rows at one segment) and f >> 1 is one-to-one on 8 consecutive rows (the
 // transposing V reads take a 32-byte pair of segments from each of 8 rows per
 // half-wave), so neither read pattern has bank conflicts.
 __device__ __forceinline__ int rowperm(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 // Byte offset of 16-byte segment `seg` of row `row` in a staged buffer.
 __device__ __forceinline__ int swz(int row, int seg) { return row * kRowBytes + ((seg ^ rowperm(row)) << 4); }
 
+// Workgroup barrier that orders LDS accesses only: this wave's LDS reads and
+// writes complete (lgkmcnt 0) before it arrives, while copies into LDS still
+// in flight (global_load_lds, counted by vmcnt) are not waited for.  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // vmcnt 63, expcnt 7, lgkmcnt 0
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
+
+// ---------------------------------------------------------------------------
+// Step lists.  Workgroup (tile, g): entry = {block id, mask of tile queries},
+// ascending block order, at most kPb mask bits per entry.
+// ---------------------------------------------------------------------------
+struct StepArgs {
+    const int32_t* sel;
+    int top_k;
+    int pos0;
+    int64_t n_q;
+    int nblk;
+    int max_steps;
+    int32_t* counts;
+    u32x2* steps;
+};
+
+__global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a) {
+    const int g = blockIdx.x % kGroups;
+    const int64_t q_first = static_cast<int64_t>(blockIdx.x / kGroups) * kTq;
+    const int n_tq = static_cast<int>(min<int64_t>(kTq, a.n_q - q_first));
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    extern __shared__ uint32_t qmask[];        // [nblk]
+    __shared__ int wave_sums[kStepsThreads / 64];
+
+    for (int b = threadIdx.x; b < a.nblk; b += kStepsThreads) qmask[b] = 0u;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n_tq * a.top_k; e += kStepsThreads) {
+        const int t = e / a.top_k;
+        const int64_t qi = q_first + t;
+        const int blk = a.sel[(qi * kGroups + g) * a.top_k + e % a.top_k];
+        const int loc = (a.pos0 + static_cast<int>(qi)) / kBlock;
+        if (blk >= 0 && blk <= loc) atomicOr(&qmask[blk], 1u << t);
+    }
+    __syncthreads();
+    // steps per block, exclusive scan over the workgroup in block order
+    const int per = (a.nblk + kStepsThreads - 1) / kStepsThreads;
+    const int b0 = threadIdx.x * per, b1 = min(b0 + per, a.nblk);
+    int cnt = 0;
+    for (int b = b0; b < b1; ++b) cnt += (__builtin_popcount(qmask[b]) + kPb - 1) / kPb;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wave_sums[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_sums[w];
+    int pos = before + incl - cnt;
+    u32x2* out = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
+    for (int b = b0; b < b1; ++b) {
+        uint32_t m = qmask[b];
+        while (m != 0u) {
+            uint32_t sub = 0u;
+            for (int i = 0; i < kPb && m != 0u; ++i) {
+                const uint32_t low = m & (~m + 1u);
+                sub |= low;
+                m ^= low;
+            }
+            out[pos++] = u32x2{static_cast<uint32_t>(b), sub};
+        }
+    }
+    if (threadIdx.x == kStepsThreads - 1) a.counts[blockIdx.x] = before + incl;
+}
+
+// ---------------------------------------------------------------------------
+// Attention sweep.
+// ---------------------------------------------------------------------------
 struct PaArgs {
     const uint16_t* k;
     const uint16_t* v;
@@ -60,303 +152,394 @@ struct PaArgs {
     int32_t pos0;
     int64_t n_q;
     int64_t last_row;
-    const int32_t* sel;
-    int top_k;
-    int nblk;
-    int n_tiles;
+    int max_steps;
+    const int32_t* counts;
+    const u32x2* steps;
     float scale;
     float* out;
 };
 
 __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a) {
-    // workgroup id -> (group, tile); with 8 XCDs fed round-robin, each XCD
-    // serves one group
     const int g = blockIdx.x % kGroups;
-    const int tile = blockIdx.x / kGroups;
-    if (tile >= a.n_tiles) return;
+    const int64_t q_first = static_cast<int64_t>(blockIdx.x / kGroups) * kTq;
+    const int n_tq = a.n_q - q_first < kTq ? static_cast<int>(a.n_q - q_first) : kTq;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15;
     const int l4 = lane >> 4;
-    const int64_t q_first = static_cast<int64_t>(tile) * kTileQ;
-    const int n_tq = static_cast<int>(min<int64_t>(kTileQ, a.n_q - q_first));
+    const int n_steps = a.counts[blockIdx.x];
+    const u32x2* steps = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
 
-    // two staging buffers, each K then V of one block; separate objects so
-    // the compiler can tell reads of one from the loads into the other
-    __shared__ __attribute__((aligned(16))) char kv0[2][kBufBytes];
-    __shared__ __attribute__((aligned(16))) char kv1[2][kBufBytes];
-    __shared__ int wave_sums[kPaWaves];
-    __shared__ int s_nu;
-    extern __shared__ uint32_t dyn[];          // qmask[nblk], then ulist[nblk] (16-bit ids)
-    uint32_t* qmask = dyn;
-    uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn + a.nblk);
+    // Separate objects, so that reads of one are not made to wait for copies
+    // in flight into another.
+    __shared__ __attribute__((aligned(16))) char kbuf[kBufBytes];
+    __shared__ __attribute__((aligned(16))) char vbuf0[kBufBytes];
+    __shared__ __attribute__((aligned(16))) char vbuf1[kBufBytes];
+    __shared__ __attribute__((aligned(16))) char qbuf[kPb][kQBytes];
+    __shared__ __attribute__((aligned(16))) char pbuf[kPb][kQBytes];
+    __shared__ __attribute__((aligned(16))) float pmax[kPb][kHeadsPerGroup][kPaWaves];
+    __shared__ float rnew[kPb][kHeadsPerGroup];    // redo: raised reference of the step's queries
+    __shared__ float alph[kPb][kHeadsPerGroup];    // redo: accumulator factor
+    __shared__ float m_ref[kTq][kHeadsPerGroup];   // reference of each (query, head), log2 units
+    __shared__ float l_fin[kTq][kHeadsPerGroup];
+    __shared__ int redo_flag;
 
-    // ---- which tile queries selected which block
-    for (int b = threadIdx.x; b < a.nblk; b += kPaThreads) qmask[b] = 0u;
-    __syncthreads();
-    for (int e = threadIdx.x; e < n_tq * a.top_k; e += kPaThreads) {
-        const int t = e / a.top_k;
-        const int64_t qi = q_first + t;
-        const int blk = a.sel[(qi * kGroups + g) * a.top_k + e % a.top_k];
-        const int loc = (a.pos0 + static_cast<int>(qi)) / kBlock;
-        if (blk >= 0 && blk <= loc) atomicOr(&qmask[blk], 1u << t);
-    }
-    __syncthreads();
-    // ---- compact the union in ascending block order
-    {
-        const int per = (a.nblk + kPaThreads - 1) / kPaThreads;
-        const int b0 = threadIdx.x * per, b1 = min(b0 + per, a.nblk);
-        int cnt = 0;
-        for (int b = b0; b < b1; ++b) cnt += qmask[b] != 0u;
-        int incl = cnt;                        // inclusive scan over the workgroup
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
-        if (lane == 63) wave_sums[wave] = incl;
-        __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; ++w) before += wave_sums[w];
-        int pos = before + incl - cnt;
-        for (int b = b0; b < b1; ++b)
-            if (qmask[b] != 0u) ulist[pos++] = static_cast<uint16_t>(b);
-        if (threadIdx.x == kPaThreads - 1) s_nu = before + incl;
-        __syncthreads();
-    }
-    const int n_union = s_nu;
-
-    // ---- per-slot query state: wave owns tile queries kSlots * wave + s
-    const int64_t s_base = static_cast<int64_t>(a.stream) * a.cap * kGroups;
-    bf16x8 qb[kSlots][4];
-    f32x4 acc[kSlots][8];
-    float m_run[kSlots], l_run[kSlots];
-    int pq[kSlots];
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        const int t = kSlots * wave + s;
-        const int64_t qi = min<int64_t>(q_first + t, a.n_q - 1);
-        pq[s] = a.pos0 + static_cast<int>(q_first + t);
-        const uint16_t* qrow = a.q + (qi * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + l16) * kHeadDim;
-#pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) qb[s][ks4] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks4 + 8 * l4);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[s] = -INFINITY;
-        l_run[s] = 0.f;
-    }
     const float qk_scale = a.scale * kLog2eP;
+    const int64_t s_base = static_cast<int64_t>(a.stream) * a.cap * kGroups;
+    const int64_t q_base = (q_first * kGroups + g) * kHeadsPerGroup * kHeadDim;   // query q_first's 16 heads
+    constexpr int64_t kQStride = int64_t(kGroups) * kHeadsPerGroup * kHeadDim;     // next query
 
-    // Lane offsets of the operand reads inside a staged buffer.  The row
-    // permutation depends on row & 15 only, so chunk and tile offsets (whole
-    // multiples of 16 rows) are added as constants.
-    int koff[4];                                  // K: row l16, segment 4*ks4 + l4
+    // Softmax reference of (query t, head h): its score against its own key,
+    // which every selection holds (the local block is always selected).  Any
+    // finite reference gives the same softmax; this one keeps the query's
+    // largest probability at or above 1, and a block whose probabilities
+    // would pass 2^kOverflow raises it (the step is redone, see below).
+    {
+        const int t = threadIdx.x >> 4, h = threadIdx.x & 15;
+        float r = 0.f;
+        if (t < n_tq) {
+            const uint16_t* qr = a.q + q_base + t * kQStride + h * kHeadDim;
+            const uint16_t* kr = a.k + (s_base + static_cast<int64_t>(a.pos0 + q_first + t) * kGroups + g) * kHeadDim;
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll 4
+            for (int d = 0; d < kHeadDim; d += 8) {
+                const u32x4 qa = *reinterpret_cast<const u32x4*>(qr + d);
+                const u32x4 ka = *reinterpret_cast<const u32x4*>(kr + d);
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) koff[ks4] = swz(l16, 4 * ks4 + l4);
-    int voff[8];                                  // V: row 4*l4 + l16/4, dims 16*dt + 4*(l16%4)
+                for (int j = 0; j < 4; ++j) {
+                    s0 = __builtin_fmaf(__uint_as_float(qa[j] << 16), __uint_as_float(ka[j] << 16), s0);
+                    s1 = __builtin_fmaf(__uint_as_float(qa[j] & 0xffff0000u), __uint_as_float(ka[j] & 0xffff0000u), s1);
+                }
+            }
+            r = (s0 + s1) * qk_scale;
+        }
+        m_ref[t][h] = r;
+        if (threadIdx.x == 0) redo_flag = 0;
+    }
+    // O^T slices (dims 16w + 4*l4 + r, head l16) of all tile queries, and the
+    // row sums of the queries t with t % 8 == w (every row of the tile holds
+    // the same sum)
+    f32x4 acc[kTq];
+    f32x4 lacc[kTq / kPaWaves];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) voff[dt] = swz(4 * l4 + (l16 >> 2), 2 * dt + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+    for (int t = 0; t < kTq; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kTq / kPaWaves; ++k) lacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-    // Direct-to-LDS staging of block b into `dst` (K, then V): 2048 16-byte
-    // slots each; the wave's instruction j fills slots kStageSlots * wave +
-    // 64 * j + lane, i.e. row slot / 16 at permuted position slot % 16, which
-    // receives the row's segment (slot % 16) ^ f(row).
-    uint32_t soff[kStageSlots / 64];              // lane's source offset (elements) within a block
+    // Lane offsets inside staged buffers (the row permutation depends on
+    // row & 15 only, so multiples of 16 rows are added as constants).
+    int koff[4];                                // K rows 16w + l16, dims 32*ks4 + 8*l4 ..
+    int qoff[4];                                // Q rows (heads) l16, same dims
 #pragma unroll
-    for (int j = 0; j < kStageSlots / 64; ++j) {
-        const int slot = kStageSlots * wave + 64 * j + lane;
+    for (int ks4 = 0; ks4 < 4; ++ks4) {
+        koff[ks4] = swz(16 * wave + l16, 4 * ks4 + l4);
+        qoff[ks4] = swz(l16, 4 * ks4 + l4);
+    }
+    // V: row 4*l4 + l16/4 (+ 32c, + 16), dims 16w + 4*(l16 % 4) .. +3
+    const int voff = swz(4 * l4 + (l16 >> 2), 2 * wave + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+    // P exchange: chunk c = keys 32c .. 32c+31 is written by waves 2c (keys
+    // 32c + 4*l4 + r) and 2c+1 (keys 32c + 16 + 4*l4 + r) and read as the
+    // 8-key B operand of lane (l16, l4) of every wave.
+    const int pw_off = (((wave >> 1) * 4 + l4) * 16 + l16) * 16 + (wave & 1) * 8;
+    const int pr_off = (l4 * 16 + l16) * 16;   // + 1 KiB per chunk
+
+    // Copies.  Slot s (16 bytes) of a staged 256-byte-row buffer holds
+    // segment (s % 16) ^ f(row) of row s / 16.  One call issues instruction j
+    // (of 4) of this wave's share of a K or V block.
+    const int last_row = static_cast<int>(a.last_row);       // positions are int32
+    uint32_t soff[4];                                          // lane's source offset (elements) in a block
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int slot = 256 * wave + 64 * j + lane;
         const int row = slot >> 4;
         soff[j] = static_cast<uint32_t>(row * kGroups * kHeadDim + 8 * ((slot & 15) ^ rowperm(row)));
     }
-    auto stage = [&](int b, char (*dst)[kBufBytes]) {
-        const int64_t row0 = static_cast<int64_t>(b) * kBlock;
-        const int64_t base = (s_base + row0 * kGroups + g) * kHeadDim;
-        const uint16_t* kbase = a.k + base;
-        const uint16_t* vbase = a.v + base;
-        if (row0 + kBlock - 1 <= a.last_row) {        // wave-uniform: the whole block is written
-#pragma unroll
-            for (int j = 0; j < kStageSlots / 64; ++j) {
-                __builtin_amdgcn_global_load_lds(kbase + soff[j], LDS_PTR(void, &dst[0][(kStageSlots * wave + 64 * j) * 16]),
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vbase + soff[j], LDS_PTR(void, &dst[1][(kStageSlots * wave + 64 * j) * 16]),
-                                                 16, 0, 0);
-            }
-        } else {
-            // rows past the chunk's last key are clamped to it: they are
-            // masked for every query, and a written row keeps P.V finite
-            const int last = static_cast<int>(a.last_row - row0);
-#pragma unroll
-            for (int j = 0; j < kStageSlots / 64; ++j) {
-                const int row = (kStageSlots * wave + 64 * j + lane) >> 4;
-                const uint32_t o = soff[j] - static_cast<uint32_t>((row - min(row, last)) * kGroups * kHeadDim);
-                __builtin_amdgcn_global_load_lds(kbase + o, LDS_PTR(void, &dst[0][(kStageSlots * wave + 64 * j) * 16]),
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vbase + o, LDS_PTR(void, &dst[1][(kStageSlots * wave + 64 * j) * 16]),
-                                                 16, 0, 0);
-            }
+    auto stage_row_j = [&](const uint16_t* cache, int b, char* dst, int j) {
+        const int row0 = b * kBlock;
+        const uint16_t* src = cache + (s_base + static_cast<int64_t>(row0) * kGroups + g) * kHeadDim;
+        uint32_t o = soff[j];
+        if (row0 + kBlock - 1 > last_row) {                   // wave-uniform: the chunk's last block
+            // rows past the chunk's last key are read from that key's row:
+            // they are masked for every query
+            const int row = (256 * wave + 64 * j + lane) >> 4;
+            o -= static_cast<uint32_t>((row - min(row, last_row - row0)) * kGroups * kHeadDim);
+        }
+        __builtin_amdgcn_global_load_lds(src + o, LDS_PTR(void, dst + (256 * wave + 64 * j) * 16), 16, 0, 0);
+    };
+    // Q of query t into slot p: instruction j (of 4) is issued by wave (4p + j) % 8.
+    auto stage_q = [&](int p, int t) {
+        const int j = (wave - 4 * p) & 7;
+        if (j < 4) {
+            const int slot = 64 * j + lane;
+            const int row = slot >> 4;
+            const int seg = (slot & 15) ^ rowperm(row);
+            __builtin_amdgcn_global_load_lds(a.q + q_base + t * kQStride + row * kHeadDim + 8 * seg,
+                                             LDS_PTR(void, &qbuf[p][64 * j * 16]), 16, 0, 0);
         }
     };
 
-    // Consume the block staged in `src`: every tile query of this wave that
-    // selected block b attends over its 128 keys with one softmax update.
-    // Both products run as steps of four LDS reads and a few independent MFMAs;
-    // reads are issued kRing - 1 steps ahead into a kRing-deep register ring,
-    // so at most 4 * kRing are in flight (the LDS counter counts to 15) and
-    // each step waits only for its own.  Scheduling barriers keep that order.
-    auto consume = [&](int b, unsigned bmask, const char (*src)[kBufBytes]) {
-        const unsigned my = (bmask >> (kSlots * wave)) & ((1u << kSlots) - 1);
-        if (my == 0) return;                            // wave-uniform
-        const char* kb = src[0];
-        const char* vb = src[1];
-        // S step i: 16-key tiles e = 4*(i&1) + t, dims 32*(i>>1) + 8*l4 ..
-        auto load_ks = [&](int i, bf16x8 (&o)[4]) {
+    // This wave's S^T tile (keys 16w + 4*l4 + r, head l16) of query p of the
+    // step, from K in kbuf and Q in qbuf[p]; keys past the query masked.
+    auto load_q = [&](int p, bf16x8 (&qop)[4]) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                o[t] = *reinterpret_cast<const bf16x8*>(kb + 16 * (4 * (i & 1) + t) * kRowBytes + koff[i >> 1]);
-        };
-        // P.V step i: chunk c = i>>2, dim tiles dt = 2*(i&3) + u.  Transposing
-        // reads: within each 16-lane row, lane j addresses row key0 + j/4,
-        // dims d0 + 4*(j%4) .. +3, and receives V[key0 + 0..3][d0 + j], with
-        // key0 = 32c + 4*l4 for k-slots 0..3 and 32c + 16 + 4*l4 for 4..7
-        auto load_vs = [&](int i, bf16x8 (&o)[2]) {
-            const int c = i >> 2;
+        for (int ks4 = 0; ks4 < 4; ++ks4) qop[ks4] = *reinterpret_cast<const bf16x8*>(qbuf[p] + qoff[ks4]);
+    };
+    auto score_q = [&](const bf16x8 (&kop)[4], const bf16x8 (&qop)[4], int qpos, int b) {
+        f32x4 s0 = mfma_16x16x32_bf16(kop[0], qop[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 s1 = mfma_16x16x32_bf16(kop[1], qop[1], f32x4{0.f, 0.f, 0.f, 0.f});
+        s0 = mfma_16x16x32_bf16(kop[2], qop[2], s0);
+        s1 = mfma_16x16x32_bf16(kop[3], qop[3], s1);
+        f32x4 s = s0 + s1;
+        const int key0 = b * kBlock + 16 * wave + 4 * l4;
+        if (b * kBlock + kBlock - 1 > qpos) {                 // the query's own block: causal mask
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int dt = 2 * (i & 3) + u;
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(v4i16, vb + kChunk * c * kRowBytes + voff[dt]));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(v4i16, vb + (kChunk * c + 16) * kRowBytes + voff[dt]));
-                o[u] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
-                                               0, 1, 2, 3, 4, 5, 6, 7);
+            for (int r = 0; r < 4; ++r)
+                if (key0 + r > qpos) s[r] = -INFINITY;
+        }
+        return s;
+    };
+    auto score = [&](const bf16x8 (&kop)[4], int p, int qpos, int b) {
+        bf16x8 qop[4];
+        load_q(p, qop);
+        return score_q(kop, qop, qpos, b);
+    };
+    // P = 2^(scale' s - ref) for this wave's keys -> bf16 into pbuf[p];
+    // returns the largest exponent.
+    auto write_p = [&](const f32x4& s, int p, float ref) {
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(s[r], qk_scale, -ref);
+        const uint32_t w01 = pack2_bf16(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
+        const uint32_t w23 = pack2_bf16(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
+        *reinterpret_cast<u32x2*>(pbuf[p] + pw_off) = u32x2{w01, w23};
+        return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    };
+    // Probabilities above 2^kOverflow could leave the f32 / bf16 range in the
+    // sums: such a step is recomputed against a raised reference.
+    constexpr float kOverflow = 64.f;
+
+    // One step: block b, tile queries `mask` (at most kPb), V in vcur; the
+    // next step's V goes to vnext.
+    auto step = [&](int i, const char* vcur, char* vnext) {
+        const u32x2 e = steps[i];
+        const int b = static_cast<int>(e[0]);
+        const uint32_t mask = e[1];
+        const int np = __builtin_popcount(mask);
+        const bool more = i + 1 < n_steps;
+        const u32x2 en = steps[more ? i + 1 : i];
+        const int bn = static_cast<int>(en[0]);
+        const int qpos0 = a.pos0 + static_cast<int>(q_first);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                                        // B0: this step's K, Q, V are in LDS
+
+        // ---- S, P for this wave's 16 keys, every query of the step; the
+        // next step's V is copied meanwhile
+        bf16x8 kop[4];
+#pragma unroll
+        for (int ks4 = 0; ks4 < 4; ++ks4) kop[ks4] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks4]);
+        if (more) {
+            stage_row_j(a.v, bn, vnext, 0);
+            stage_row_j(a.v, bn, vnext, 1);
+        }
+        float xmax = -INFINITY;
+        {
+            // two queries per iteration, so that their read / product /
+            // exponent chains overlap
+            uint32_t m = mask;
+            int p = 0;
+            for (; p + 1 < np; p += 2) {
+                const int t0 = __builtin_ctz(m);
+                m &= m - 1u;
+                const int t1 = __builtin_ctz(m);
+                m &= m - 1u;
+                const float r0 = m_ref[t0][l16], r1 = m_ref[t1][l16];
+                bf16x8 q0[4], q1[4];
+                load_q(p, q0);
+                load_q(p + 1, q1);
+                const f32x4 s0 = score_q(kop, q0, qpos0 + t0, b);
+                const f32x4 s1 = score_q(kop, q1, qpos0 + t1, b);
+                xmax = fmaxf(xmax, fmaxf(write_p(s0, p, r0), write_p(s1, p + 1, r1)));
             }
-        };
-#pragma unroll
-        for (int s = 0; s < kSlots; ++s) {
-            if (!((my >> s) & 1)) continue;             // wave-uniform
-            const int kmax = pq[s] - b * kBlock;        // last visible key offset, >= 0
-            // S^T = K Q^T: st[e] holds keys 16e + 4*l4 + r, head l16.  Keys
-            // past the query are computed and then masked: every staged row
-            // holds finite values.
-            f32x4 st[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-            bf16x8 kr[kRing][4];
-#pragma unroll
-            for (int i = 0; i < kRing - 1; ++i) load_ks(i, kr[i]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i + kRing - 1 < 8) load_ks(i + kRing - 1, kr[(i + kRing - 1) % kRing]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    st[4 * (i & 1) + t] = mfma_16x16x32_bf16(kr[i % kRing][t], qb[s][i >> 1], st[4 * (i & 1) + t]);
-                __builtin_amdgcn_sched_barrier(0);
+            if (p < np) {
+                const int t = __builtin_ctz(m);
+                xmax = fmaxf(xmax, write_p(score(kop, p, qpos0 + t, b), p, m_ref[t][l16]));
             }
-            bf16x8 vr[kRing][2];
+        }
+        if (more) {
+            stage_row_j(a.v, bn, vnext, 2);
+            stage_row_j(a.v, bn, vnext, 3);
+        }
+        if (__builtin_amdgcn_ballot_w64(xmax > kOverflow) != 0 && lane == 0) redo_flag = 1;
+        lds_barrier();                                          // B1: P is in LDS; K, Q free
+
+        const bool redo = redo_flag != 0;                       // workgroup-uniform, rare
+        if (redo) {
+            // Raise the reference of the step's queries to max(ref, block
+            // max) and recompute P (K and Q are still in place); the
+            // accumulators are scaled by 2^(old - new) below.
+            bf16x8 kre[4];
 #pragma unroll
-            for (int i = 0; i < kRing - 1; ++i) load_vs(i, vr[i]);
-            // Mask keys past the query (only its own block has any), then the
-            // block max of the raw scores; the scale is positive.
-            if (kmax < kBlock - 1) {                    // wave-uniform
-                const int rel = kmax - 4 * l4;          // compared with constants: no index registers
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (16 * e + r > rel) st[e][r] = -INFINITY;
+            for (int ks4 = 0; ks4 < 4; ++ks4) kre[ks4] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks4]);
+            uint32_t m = mask;
+            for (int p = 0; p < np; ++p) {
+                const int t = __builtin_ctz(m);
+                m &= m - 1u;
+                const f32x4 s = score(kre, p, qpos0 + t, b);
+                const float mx = max_xor32(max_xor16(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
+                if (lane < 16) pmax[p][l16][wave] = mx;
             }
-            float mx = st[0][0];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[e][r]);
-            mx = max_xor32(max_xor16(mx)) * qk_scale;   // key 0 is visible: finite
-            // Lazy rescaling: the reference max m_run moves only when a block
-            // max exceeds it by more than kSlack (log2 units), so probabilities
-            // stay below 2^kSlack and most blocks skip rescaling the
-            // accumulators.  The result is the same softmax.
-            if (__builtin_amdgcn_ballot_w64(mx > m_run[s] + kSlack) != 0) {   // wave-uniform
-                const float m_new = fmaxf(m_run[s], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);   // 0 on the first block
-                l_run[s] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[s][dt] = acc[s][dt] * alpha;
-                m_run[s] = m_new;
-            }
-            // P^T as the B operand of P.V: k-slot 8*l4 + j of chunk c is key
-            // 32c + 4*l4 + j (j < 4) or 32c + 16 + 4*l4 + j - 4 (j >= 4)
-            bf16x8 pb[kBlock / kChunk];
-            float rs = 0.f;
-#pragma unroll
-            for (int c = 0; c < kBlock / kChunk; ++c) {
-                float pr[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    pr[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[2 * c + j / 4][j % 4], qk_scale, -m_run[s]));
-                    rs += pr[j];
+            lds_barrier();
+            m = mask;
+            for (int p = 0; p < np; ++p) {
+                const int t = __builtin_ctz(m);
+                m &= m - 1u;
+                const f32x4 m0 = *reinterpret_cast<const f32x4*>(&pmax[p][l16][0]);
+                const f32x4 m1 = *reinterpret_cast<const f32x4*>(&pmax[p][l16][4]);
+                const float mb = fmaxf(fmaxf(fmaxf(m0[0], m0[1]), fmaxf(m0[2], m0[3])),
+                                       fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3]))) * qk_scale;
+                const float old = m_ref[t][l16];
+                const float ref = fmaxf(old, mb);
+                write_p(score(kre, p, qpos0 + t, b), p, ref);
+                if (wave == 0 && lane < 16) {
+                    rnew[p][l16] = ref;
+                    alph[p][l16] = __builtin_amdgcn_exp2f(old - ref);
                 }
-                u32x4 pw;
-                pw[0] = pack2_bf16(pr[0], pr[1]);
-                pw[1] = pack2_bf16(pr[2], pr[3]);
-                pw[2] = pack2_bf16(pr[4], pr[5]);
-                pw[3] = pack2_bf16(pr[6], pr[7]);
-                pb[c] = __builtin_bit_cast(bf16x8, pw);
             }
-            l_run[s] += sum_xor32(sum_xor16(rs));
-            // O^T += V^T P^T
+            lds_barrier();
+            if (wave == 0 && lane < 16) {                       // read again only after the next B0
+                m = mask;
+                for (int p = 0; p < np; ++p) {
+                    const int t = __builtin_ctz(m);
+                    m &= m - 1u;
+                    m_ref[t][l16] = rnew[p][l16];
+                }
+            }
+            if (threadIdx.x == 0) redo_flag = 0;                // next read after the next step's B1
+        }
+
+        // ---- O^T += V^T P^T for this wave's 16 dims, every query of the
+        // step, and the row sums of its own queries; the next step's K and Q
+        // are copied meanwhile
+        bf16x8 vop[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i + kRing - 1 < 16) load_vs(i + kRing - 1, vr[(i + kRing - 1) % kRing]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < 4; ++c) {
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(v4i16, vcur + kChunk * c * kRowBytes + voff));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDS_PTR(v4i16, vcur + (kChunk * c + 16) * kRowBytes + voff));
+            vop[c] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        if (more) {
 #pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    acc[s][2 * (i & 3) + u] =
-                        mfma_16x16x32_bf16(vr[i % kRing][u], pb[i >> 2], acc[s][2 * (i & 3) + u]);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j) stage_row_j(a.k, bn, kbuf, j);
+            uint32_t mn = en[1];
+            for (int p = 0; mn != 0u; ++p) {
+                stage_q(p, __builtin_ctz(mn));
+                mn &= mn - 1u;
+            }
+        }
+        {
+            // the next query's P operand is read as soon as this one's
+            // products have been issued
+            bf16x8 pt[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pt[c] = *reinterpret_cast<const bf16x8*>(pbuf[0] + pr_off + 1024 * c);
+            int p = 0;
+#pragma unroll
+            for (int t = 0; t < kTq; ++t) {
+                if ((mask >> t) & 1u) {                         // wave-uniform
+                    const bool own = (t % kPaWaves) == wave;
+                    if (redo) {
+                        const float al = alph[p][l16];
+                        acc[t] = acc[t] * al;
+                        if (own) lacc[t / kPaWaves] = lacc[t / kPaWaves] * al;
+                    }
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[t] = mfma_16x16x32_bf16(vop[c], pt[c], acc[t]);
+                    if (own) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) lacc[t / kPaWaves] = mfma_16x16x32_bf16(ones, pt[c], lacc[t / kPaWaves]);
+                    }
+                    ++p;
+                    if (p < np) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) pt[c] = *reinterpret_cast<const bf16x8*>(pbuf[p] + pr_off + 1024 * c);
+                    }
+                }
             }
         }
     };
 
-    // The block ids and masks are read before the loads are issued: LDS reads
-    // that the compiler cannot tell apart from the staging buffers would
-    // otherwise wait for the loads in flight.
-    int b_cur = n_union > 0 ? static_cast<int>(ulist[0]) : 0;
-    if (n_union > 0) stage(b_cur, kv0);
-    for (int u = 0; u < n_union; u += 2) {
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        int b_next = u + 1 < n_union ? static_cast<int>(ulist[u + 1]) : 0;
-        unsigned m_cur = qmask[b_cur];
-        if (u + 1 < n_union) stage(b_next, kv1);
-        consume(b_cur, m_cur, kv0);
-        if (u + 1 >= n_union) break;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        b_cur = u + 2 < n_union ? static_cast<int>(ulist[u + 2]) : 0;
-        m_cur = qmask[b_next];
-        if (u + 2 < n_union) stage(b_cur, kv0);
-        consume(b_next, m_cur, kv1);
+    if (n_steps > 0) {
+        const u32x2 e0 = steps[0];
+        const int b0 = static_cast<int>(e0[0]);
+        uint32_t m = e0[1];
+        for (int j = 0; j < 4; ++j) {
+            stage_row_j(a.k, b0, kbuf, j);
+            stage_row_j(a.v, b0, vbuf0, j);
+        }
+        for (int p = 0; m != 0u; ++p) {
+            stage_q(p, __builtin_ctz(m));
+            m &= m - 1u;
+        }
     }
+    for (int i = 0; i < n_steps; i += 2) {
+        step(i, vbuf0, vbuf1);
+        if (i + 1 >= n_steps) break;
+        step(i + 1, vbuf1, vbuf0);
+    }
+    // row sums to LDS (lane (l16, 0) of the owner wave holds head l16's)
+#pragma unroll
+    for (int k = 0; k < kTq / kPaWaves; ++k)
+        if (lane < 16) l_fin[k * kPaWaves + wave][l16] = lacc[k][0];
+    __syncthreads();
 
-    // ---- normalise and write: lane holds O^T[dim 16*dt + 4*l4 + r][head l16]
+    // ---- normalise and write: lane holds O^T[dim 16w + 4*l4 + r][head l16]
+    float* dst = a.out + q_base + static_cast<int64_t>(l16) * kHeadDim + 16 * wave + 4 * l4;
 #pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-        const int t = kSlots * wave + s;
-        if (t >= n_tq) continue;
-        const int64_t qi = q_first + t;
-        const float inv = 1.f / l_run[s];
-        float* dst = a.out + (qi * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + l16) * kHeadDim + 4 * l4;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[s][dt] * inv;
+    for (int t = 0; t < kTq; ++t) {
+        if (t < n_tq) {
+            const float inv = 1.f / l_fin[t][l16];
+            *reinterpret_cast<f32x4*>(dst + t * kQStride) = acc[t] * inv;
+        }
     }
 }
 
+int64_t n_tiles_of(int64_t n_q) { return (n_q + kTq - 1) / kTq; }
+
 }  // namespace
+
+size_t prefill_attend_ws_bytes(int64_t n_q, int top_k) {
+    const int64_t n_wg = n_tiles_of(n_q) * kGroups;
+    const size_t counts = (static_cast<size_t>(n_wg) * sizeof(int32_t) + 255) & ~size_t(255);
+    return counts + static_cast<size_t>(n_wg) * kTq * top_k * sizeof(u32x2);
+}
 
 hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
                                  int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
-                                 float scale, float* out, hipStream_t s) {
+                                 float scale, float* out, void* ws, hipStream_t s) {
+    const int64_t n_wg = n_tiles_of(n_q) * kGroups;
+    const size_t counts_bytes = (static_cast<size_t>(n_wg) * sizeof(int32_t) + 255) & ~size_t(255);
+    int32_t* counts = static_cast<int32_t*>(ws);
+    u32x2* steps = reinterpret_cast<u32x2*>(static_cast<char*>(ws) + counts_bytes);
+    const int nblk = (pos0 + static_cast<int>(n_q) - 1) / kBlock + 1;
+
+    StepArgs sa;
+    sa.sel = sel;
+    sa.top_k = top_k;
+    sa.pos0 = pos0;
+    sa.n_q = n_q;
+    sa.nblk = nblk;
+    sa.max_steps = kTq * top_k;
+    sa.counts = counts;
+    sa.steps = steps;
+    hipLaunchKernelGGL(prefill_steps_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(kStepsThreads),
+                       static_cast<size_t>(nblk) * sizeof(uint32_t), s, sa);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
     PaArgs a;
     a.k = k;
     a.v = v;
@@ -366,15 +549,12 @@ hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t c
     a.pos0 = pos0;
     a.n_q = n_q;
     a.last_row = pos0 + n_q - 1;
-    a.sel = sel;
-    a.top_k = top_k;
-    a.nblk = (pos0 + static_cast<int>(n_q) - 1) / kBlock + 1;
-    a.n_tiles = static_cast<int>((n_q + kTileQ - 1) / kTileQ);
+    a.max_steps = kTq * top_k;
+    a.counts = counts;
+    a.steps = steps;
     a.scale = scale;
     a.out = out;
-    const unsigned n_wg = static_cast<unsigned>(a.n_tiles) * kGroups;
-    const size_t lds = static_cast<size_t>(a.nblk) * (sizeof(uint32_t) + sizeof(uint16_t));
-    hipLaunchKernelGGL(prefill_attend_kernel, dim3(n_wg), dim3(kPaThreads), lds, s, a);
+    hipLaunchKernelGGL(prefill_attend_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(kPaThreads), 0, s, a);
     return hipGetLastError();
 }
 

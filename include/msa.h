@@ -227,9 +227,11 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
  * block-level mask of the selection combined with the causal mask): n_q
  * consecutive queries at positions pos0 .. pos0 + n_q - 1 of `stream`.
  * Same arguments and output as msa_attend_decode.  Cache rows up to
- * pos0 + n_q - 1 must be written (the chunk's own keys included).  Needs no
- * workspace (MSA_OP_ATTEND_PREFILL is 0 bytes): d_ws and ws_bytes are
- * ignored and may be NULL / 0.
+ * pos0 + n_q - 1 must be written (the chunk's own keys included).
+ * Workspace: msa_workspace_bytes(dims, MSA_OP_ATTEND_PREFILL, n_q, max_pos)
+ * bytes at d_ws (16-byte aligned; MSA_ERR_WORKSPACE_TOO_SMALL otherwise):
+ * per tile of 32 consecutive queries and group, the ascending list of the
+ * blocks their selections hold, built on the device before the sweep.
  */
 MSA_API msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
                               int32_t stream, int32_t pos0, int64_t n_q, const int32_t* d_sel,

@@ -108,6 +108,12 @@ def test_prefill_range_checks(L):
     h = lambda pos0, n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(big), A, 0, pos0, n, A, A, A, 0, None)
     assert h(4096 * 128 - 8, 8) != UNSUP      # last block 4095: accepted (fails later only for want of a GPU)
     assert h(4096 * 128 - 8, 9) == UNSUP
+    # the step lists need workspace
+    c1 = _cache(cap=1000, n_stream=1)
+    need = M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 10, 99)
+    w = lambda ws, n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c1), A, 0, 90, 10, A, A, ws, n, None)
+    assert w(None, need) == NULL
+    assert w(A, need - 1) == WS
 
 
 def test_append_validation(L):
@@ -141,8 +147,11 @@ def test_workspace_sizes(L):
     # attention partials: per (query, group, split) 16 heads x (128 + 2) floats
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 0   # prefill attention needs none
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 1, 100) == 0
+    # prefill attention: per (32-query tile, group) a step count (256-byte
+    # aligned array) and up to 32 * top_k 8-byte step entries
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 2048 + 512 * 32 * 16 * 8
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 1, 100) == 256 + 4 * 32 * 16 * 8
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 33, 100) == 256 + 8 * 32 * 16 * 8
     dd = M.dsa_dims()
     assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
     with pytest.raises(M.MsaError):

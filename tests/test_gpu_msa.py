@@ -10,7 +10,7 @@ import torch
 import block_sparse_attention_msa_amd as M
 import oracle
 import workloads as W
-from _gpu_common import (DEV, GpuWorkload, check_attention, check_selection, dev, host_bits, log)
+from _gpu_common import (DEV, GpuWorkload, check_attention, check_selection, dev, dev_bits, host_bits, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -221,9 +221,38 @@ def test_prefill_attention_shared_selection():
             for i in range(t0, min(t0 + 16, n_q)):
                 sel[i, g] = np.sort(np.append(others, loc[i]))
     out = torch.empty((n_q, 64, 128), dtype=torch.float32, device=DEV)
-    M.msa_attend_prefill(dims, gw.cache, gw.q, wl.stream[0], pos0, dev(sel), out, None)
+    M.msa_attend_prefill(dims, gw.cache, gw.q, wl.stream[0], pos0, dev(sel), out, gw.ws(dims, M.MSA_OP_ATTEND_PREFILL))
     torch.cuda.synchronize()
     o_out = oracle.sparse_attend(gw.host["k"], gw.host["v"], gw.qs["stream"], gw.qs["pos"], gw.qs["q"], sel,
+                                 unit=128, scale=W.SCALE)
+    wa, wr = check_attention(out.cpu().numpy(), o_out)
+    log(f"  attention: max-abs {wa:.3e}, rel-L2 {wr:.3e}")
+
+
+@pytest.mark.parametrize("q_scale", [6.0, 40.0])
+def test_prefill_attention_large_score_range(q_scale):
+    # Queries scaled up so that block maxima run far above each query's first
+    # reference: x6 moves the running reference, x40 also pushes scaled
+    # probabilities past the overflow bound, so steps are recomputed.
+    wl = W.prefill_workload(f"pf_big{int(q_scale)}", 3000, 2500, 200)
+    log(f"[msa prefill] {wl.name}: queries scaled by {q_scale}")
+    dims = M.msa_dims(16, W.SCALE)
+    gw = GpuWorkload(wl)
+    gw.append_own_rows()
+    q32 = (gw.qs["q"].astype(np.uint32) << 16).view(np.float32) * np.float32(q_scale)
+    qb = W.to_bf16_bits(q32)
+    q_dev = dev_bits(qb, torch.bfloat16)
+    n_q, pos0 = wl.n_q, wl.pos[0]
+    rng = np.random.default_rng(11)
+    sel = np.empty((n_q, 4, 16), np.int32)
+    for i in range(n_q):
+        loc = (pos0 + i) // 128
+        for g in range(4):
+            sel[i, g] = np.sort(np.append(rng.choice(loc, 15, replace=False), loc))
+    out = torch.empty((n_q, 64, 128), dtype=torch.float32, device=DEV)
+    M.msa_attend_prefill(dims, gw.cache, q_dev, wl.stream[0], pos0, dev(sel), out, gw.ws(dims, M.MSA_OP_ATTEND_PREFILL))
+    torch.cuda.synchronize()
+    o_out = oracle.sparse_attend(gw.host["k"], gw.host["v"], gw.qs["stream"], gw.qs["pos"], qb, sel,
                                  unit=128, scale=W.SCALE)
     wa, wr = check_attention(out.cpu().numpy(), o_out)
     log(f"  attention: max-abs {wa:.3e}, rel-L2 {wr:.3e}")
