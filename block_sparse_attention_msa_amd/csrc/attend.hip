@@ -7,69 +7,82 @@
 // the same over the kept token ids.
 //
 // Design (gfx950):
-//  * One workgroup of four wavefronts per (query, group, split).  The 16 query
-//    heads of a group are the N = 16 side of v_mfma_f32_16x16x32_bf16, so a
-//    group's heads share every K/V byte that is read.
-//  * Keys are read straight from the cache by block (or token) id in chunks of
-//    32: nothing is gathered or materialised.  Each wave software-pipelines its
-//    chunks: the next chunk's K loads are issued before the current chunk is
-//    computed, and a chunk's V loads before its score MFMAs.  Each chunk computes
-//    S^T = K Q^T (keys x heads), so every lane already holds P^T in the layout
-//    the second MFMA (O^T = V^T P^T) wants; V is transposed once through a
-//    per-wave LDS tile with 8-byte writes.
-//  * Online softmax in the log2 domain; the four waves of a workgroup merge in
-//    LDS; splits write (m, l, acc) partials that a second kernel combines in a
-//    fixed order, so results are deterministic.
+//  * One workgroup of four wavefronts per (query, group, split), sized so the
+//    grid is about one workgroup per compute unit.  A split owns a run of
+//    128-key units: selected blocks (MSA) or 128 kept token ids (DSA).  The 16
+//    query heads of a group are the N = 16 side of v_mfma_f32_16x16x32_bf16,
+//    so a group's heads share every K/V byte that is read.
+//  * Units stream HBM -> LDS with global_load_lds (no registers) into a ring
+//    of two: the next unit's 64 KiB are in flight while the current one is
+//    computed, nothing is gathered into a separate buffer.  Rows are stored
+//    with their 16-byte segments permuted by the row index, so K operand reads
+//    and the transposing V reads (ds_read_b64_tr_b16, which hand each lane
+//    four consecutive keys of one dim) are free of bank conflicts.
+//  * Wave w takes keys 32w .. 32w+31 of every unit: S^T = K Q^T (keys x
+//    heads) leaves P^T in the layout O^T = V^T P^T wants.  Online softmax in
+//    the log2 domain per wave; the four waves merge in LDS; splits write
+//    (m, l, acc) partials that a second kernel combines in a fixed order, so
+//    results are deterministic.
 #include "common.hpp"
 
 namespace msa {
 namespace {
 
 constexpr int kAttWaves = 4;
-constexpr int kVtPitch = kChunk + 4;             // bf16 per transposed-V row (one dim)
+constexpr int kAttThreads = 64 * kAttWaves;
+constexpr int kUnit = 128;                        // keys per streamed unit
+constexpr int kRowBytes = kHeadDim * 2;           // one group's K or V row: 256 B
+constexpr int kUnitBytes = kUnit * kRowBytes;     // 32 KiB of K (and of V) per unit
+constexpr int kCopiesPerUnit = kUnitBytes / 16 / kAttThreads;   // 16-byte copies per thread, K or V
 constexpr int kPartFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;   // acc + (m, l)
 constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = static_cast<__bf16>(lo);
-    const __bf16 b = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-
-struct ChunkBuf {
-    bf16x8 kA[2][4];      // K operand of the chunk's two 16-key tiles
-    int vrow[2][4];       // cache rows of the V values this lane transposes
-    uint32_t valid;       // bit kk: key kk of the chunk is visible
-};
-
 // Largest id list one split stages: 4096 DSA tokens (or 64 MSA blocks).
 constexpr int kMaxSplitEntries = 4096;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// Segment permutation of a staged row (see the design note).
+__device__ __forceinline__ int rowperm(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int seg) { return row * kRowBytes + ((seg ^ rowperm(row)) << 4); }
+
+// Barrier ordering LDS accesses only: copies into LDS still in flight
+// (counted by vmcnt) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // vmcnt 63, expcnt 7, lgkmcnt 0
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr unsigned waitcnt_vm(int n) {
+    return static_cast<unsigned>((n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+static_assert(waitcnt_vm(0) == 0x0F70 && waitcnt_vm(16) == 0x4F70, "gfx9 s_waitcnt layout");
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 
 struct KernelArgs {
     AttendArgs a;
     int n_split;
-    int n_chunks;          // chunks of 32 keys per (query, group)
-    int chunks_per_split;
+    int n_units;           // units per (query, group)
+    int units_per_split;
 };
 
-union LdsAttend {
-    uint16_t vt[kAttWaves][kHeadDim * kVtPitch];       // transposed V tiles
-    struct {
-        float acc[kAttWaves][kHeadsPerGroup][kHeadDim];
-        float m[kAttWaves][kHeadsPerGroup];
-        float l[kAttWaves][kHeadsPerGroup];
-    } merge;
-};
-
-template <bool kTokenIds>
-__global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
+// kMaxUnits: the units a split streams.  The unit loop is fully unrolled and
+// every copy and wait in it is unconditional (units past the split's valid
+// ones are copied from a valid row and fully masked), so the compiler can
+// tell which ring buffer every copy in flight targets and reads of the other
+// buffer never wait for it.
+template <bool kTokenIds, int kMaxUnits>
+__global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     const AttendArgs& a = ka.a;
     const int64_t wg = blockIdx.x;                 // ((query * kGroups) + group) * n_split + split
     const int sp = static_cast<int>(wg % ka.n_split);
@@ -80,9 +93,16 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
     const int l16 = lane & 15;
     const int l4 = lane >> 4;
 
-    __shared__ LdsAttend lds;
-    __shared__ int32_t ids[kAttWaves][kChunk];
-    __shared__ int32_t sel_s[kMaxSplitEntries];   // this split's selected ids
+    // ring of two units; separate objects, so that reads of one are not made
+    // to wait for the copies in flight into the other
+    __shared__ __attribute__((aligned(16))) char kbuf0[kUnitBytes];
+    __shared__ __attribute__((aligned(16))) char kbuf1[kUnitBytes];
+    __shared__ __attribute__((aligned(16))) char vbuf0[kUnitBytes];
+    __shared__ __attribute__((aligned(16))) char vbuf1[kUnitBytes];
+    __shared__ int32_t sel_s[kMaxSplitEntries];    // this split's ids
+    __shared__ float mrg_m[kAttWaves][kHeadsPerGroup];
+    __shared__ float mrg_l[kAttWaves][kHeadsPerGroup];
+    __shared__ int n_valid_s;
 
     const int64_t s = a.stream[i];
     const int p = a.pos[i];
@@ -90,197 +110,192 @@ __global__ __launch_bounds__(256) void attend_kernel(KernelArgs ka) {
                          g * a.sel_g_stride;
     const uint16_t* kg = a.k + (s * a.cap * kGroups + g) * kHeadDim;   // row t at + t*kGroups*kHeadDim
     const uint16_t* vg = a.v + (s * a.cap * kGroups + g) * kHeadDim;
-    constexpr int64_t kRow = kGroups * kHeadDim;
+    constexpr int kRow = kGroups * kHeadDim;
 
-    const int c_begin = sp * ka.chunks_per_split;
-    const int c_end = min(c_begin + ka.chunks_per_split, ka.n_chunks);
-    // stage the split's ids once: blocks c/4 (MSA) or tokens 32c.. (DSA)
-    const int e_begin = kTokenIds ? c_begin * kChunk : c_begin / 4;
-    const int e_end = kTokenIds ? min(c_end * kChunk, a.sel_len) : (c_end + 3) / 4;
-    for (int e = e_begin + static_cast<int>(threadIdx.x); e < e_end; e += 256) sel_s[e - e_begin] = sel[e];
-    __syncthreads();
-
+    // this split's units and their ids (ascending, -1 padding at the end)
+    const int u_begin = sp * ka.units_per_split;
+    const int u_end = min(u_begin + ka.units_per_split, ka.n_units);
+    const int e_begin = kTokenIds ? u_begin * kUnit : u_begin;
+    const int e_end = kTokenIds ? min(u_end * kUnit, a.sel_len) : u_end;
     // Q^T operand: B[k = dim][n = head]; lane: head l16, dims 32*ks + 8*l4 + 0..7
+    // (loaded with the ids, before any copy into LDS is in flight)
     bf16x8 qb[4];
     {
         const uint16_t* qrow = a.q + (i * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + l16) * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * l4);
     }
+    if (threadIdx.x == 0) n_valid_s = 0;
+    __syncthreads();
+    for (int e = e_begin + static_cast<int>(threadIdx.x); e < e_begin + (u_end - u_begin) * (kTokenIds ? kUnit : 1);
+         e += kAttThreads) {
+        int id = e < e_end ? sel[e] : -1;
+        if (kTokenIds ? (id > p) : (id > p / kBlock)) id = -1;
+        sel_s[e - e_begin] = id;
+        // units are valid up to the first unit whose first id is padding
+        if (id >= 0 && (kTokenIds ? ((e - e_begin) % kUnit == 0) : true))
+            atomicMax(&n_valid_s, (e - e_begin) / (kTokenIds ? kUnit : 1) + 1);
+    }
+    __syncthreads();
+    const int n_units = n_valid_s;                  // the split size guarantees n_valid_s <= kMaxUnits
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));      // the query operand has arrived
     const float qk_scale = a.scale * kLog2e;
+
+    // Copies of unit u into (kd, vd): slot c = 256*j + thread holds segment
+    // (c % 16) ^ f(row) of row c / 16; rows whose key is padding or past the
+    // query read the query's own row (finite, masked below).
+    auto stage = [&](int u, char* kd, char* vd) {
+#pragma unroll
+        for (int j = 0; j < kCopiesPerUnit; ++j) {
+            const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
+            const int row = c >> 4;
+            const int seg = (c & 15) ^ rowperm(row);
+            int tok = p;
+            if (u < n_units) tok = kTokenIds ? sel_s[u * kUnit + row] : sel_s[u] * kBlock + row;
+            if (tok < 0 || tok > p) tok = p;
+            const int64_t off = static_cast<int64_t>(tok) * kRow + 8 * seg;
+            __builtin_amdgcn_global_load_lds(kg + off, LDS_PTR(void, kd + (kAttThreads * j + 64 * wave) * 16), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vg + off, LDS_PTR(void, vd + (kAttThreads * j + 64 * wave) * 16), 16, 0, 0);
+        }
+    };
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint16_t* vt = lds.vt[wave];
+    // lane offsets: K rows 32w + 16t + l16; V rows 32w + 4*l4 + l16/4 (+16)
+    int koff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[ks] = swz(32 * wave + l16, 4 * ks + l4);
 
-    // Issue the K loads of chunk c into `buf` and note its V rows (nothing is
-    // waited on here).
-    auto fetch = [&](int c, ChunkBuf& buf) {
-        int tok = -1;                    // key `lane` of the chunk; -1: padding or not visible
-        if (lane < kChunk) {
-            if (kTokenIds) {
-                const int e = c * kChunk + lane;
-                tok = e < a.sel_len ? sel_s[e - e_begin] : -1;
-            } else {
-                const int blk = sel_s[(c >> 2) - e_begin];
-                tok = (blk < 0 || blk > p / kBlock) ? -1 : blk * kBlock + (c & 3) * kChunk + lane;
+    // Online-softmax update with keys 32w .. 32w+31 of unit u.  The unit's
+    // K and V operands are read first; `release` runs once they are in
+    // registers (the ring buffer may then be refilled) and before the math.
+    auto compute = [&](int u, const char* kb, const char* vb, auto&& release) {
+        // validity of this lane's keys 32w + 16t + 4*l4 + r
+        uint32_t valid = 0;
+        if (u < n_units)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = 32 * wave + 16 * t + 4 * l4 + r;
+                const int tok = kTokenIds ? sel_s[u * kUnit + key] : sel_s[u] * kBlock + key;
+                if (tok >= 0 && tok <= p) valid |= 1u << (4 * t + r);
             }
-            if (tok > p) tok = -1;
-            ids[wave][lane] = tok;
-        }
-        buf.valid = static_cast<uint32_t>(__ballot(lane < kChunk && tok >= 0));
-        if (buf.valid == 0) return;      // wave-uniform
-        wave_lds_sync();
+        const bool any = __builtin_amdgcn_ballot_w64(valid != 0) != 0;   // wave-uniform
+        // K operands (lane: keys 32w + 16t + l16) and V^T operands
+        bf16x8 kA[2][4];
+        bf16x8 va[8];
+        if (any) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {    // K operand: A = K (m = key, k = dim)
-            int row = ids[wave][16 * t + l16];
-            row = row < 0 ? p : row;     // masked later; any valid row is safe to read
-            const uint16_t* kr = kg + row * kRow + 8 * l4;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) buf.kA[t][ks] = *reinterpret_cast<const bf16x8*>(kr + 32 * ks);
-        }
+                for (int ks = 0; ks < 4; ++ks)
+                    kA[t][ks] = *reinterpret_cast<const bf16x8*>(kb + 16 * t * kRowBytes + koff[ks]);
+            // dim tile dt: keys 32w + 4*l4 + 0..3 and 32w + 16 + 4*l4 + 0..3
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {    // V rows: keys 4*qd + u (qd = l4, 4 + l4)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int row = ids[wave][4 * (l4 + 4 * h) + u];
-                buf.vrow[h][u] = row < 0 ? p : row;   // weight is exactly 0; the value only needs to be finite
+            for (int dt = 0; dt < 8; ++dt) {
+                const int vo = swz(4 * l4 + (l16 >> 2), 2 * dt + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(v4i16, vb + 32 * wave * kRowBytes + vo));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    LDS_PTR(v4i16, vb + (32 * wave + 16) * kRowBytes + vo));
+                va[dt] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
             }
         }
-        wave_lds_sync();                 // ids is rewritten by the next fetch
-    };
-
-    // Online-softmax update with the chunk held in `buf`.
-    auto compute = [&](ChunkBuf& buf) {
-        const uint32_t valid = buf.valid;
-        if (valid == 0) return;          // wave-uniform
-        // V loads first: their latency overlaps the score MFMAs and the softmax
-        u32x4 vr[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                vr[h][u] = *reinterpret_cast<const u32x4*>(vg + buf.vrow[h][u] * kRow + 8 * l16);
-        // S^T = K Q^T; lane gets keys 16t + 4*l4 + r of head l16
+        release();
+        if (!any) return;                          // nothing of this wave's keys is visible
+        // S^T = K Q^T; lane gets keys 32w + 16t + 4*l4 + r of head l16
         f32x4 st[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) st[t] = mfma_16x16x32_bf16(buf.kA[t][ks], qb[ks], st[t]);
+            for (int ks = 0; ks < 4; ++ks) st[t] = mfma_16x16x32_bf16(kA[t][ks], qb[ks], st[t]);
         }
-        // transpose V into vt[dim][key] (8-byte writes of 4 consecutive keys)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int key0 = 4 * (l4 + 4 * h);
-#pragma unroll
-            for (int m2 = 0; m2 < 4; ++m2) {       // dims 8*l16 + 2*m2, +1
-                const uint32_t w0 = vr[h][0][m2], w1 = vr[h][1][m2];
-                const uint32_t w2 = vr[h][2][m2], w3 = vr[h][3][m2];
-                // even dim: low halves; odd dim: high halves
-                const uint32_t e01 = __builtin_amdgcn_perm(w1, w0, 0x05040100);
-                const uint32_t e23 = __builtin_amdgcn_perm(w3, w2, 0x05040100);
-                const uint32_t o01 = __builtin_amdgcn_perm(w1, w0, 0x07060302);
-                const uint32_t o23 = __builtin_amdgcn_perm(w3, w2, 0x07060302);
-                const int d = 8 * l16 + 2 * m2;
-                *reinterpret_cast<uint2*>(vt + d * kVtPitch + key0) = make_uint2(e01, e23);
-                *reinterpret_cast<uint2*>(vt + (d + 1) * kVtPitch + key0) = make_uint2(o01, o23);
-            }
-        }
-        // online softmax over this chunk for head l16
         float x[8];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kk = 16 * t + 4 * l4 + r;
-                x[4 * t + r] = ((valid >> kk) & 1) ? st[t][r] * qk_scale : -INFINITY;
-            }
-        }
+            for (int r = 0; r < 4; ++r)
+                x[4 * t + r] = ((valid >> (4 * t + r)) & 1) ? st[t][r] * qk_scale : -INFINITY;
         float cm = x[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) cm = fmaxf(cm, x[j]);
         cm = max_xor32(max_xor16(cm));
-        const float m_new = fmaxf(m_run, cm);      // finite: the chunk has a visible key
-        const float alpha = exp2f(m_run - m_new);  // 0 on the first chunk (m_run = -inf)
+        const float m_new = fmaxf(m_run, cm);      // finite: the wave has a visible key
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 on the first unit
         float pr[8];
         float rs = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            pr[j] = exp2f(x[j] - m_new);
+            pr[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
             rs += pr[j];
         }
         rs = sum_xor32(sum_xor16(rs));
         l_run = l_run * alpha + rs;
         m_run = m_new;
         // P^T operand (B: k = key, n = head); k-slot 8*l4 + j holds key
-        // 4*l4 + j (j < 4) or 16 + 4*l4 + (j - 4)
+        // 4*l4 + j (j < 4) or 16 + 4*l4 + (j - 4) of this wave's 32
         u32x4 pw;
         pw[0] = pack_bf16x2(pr[0], pr[1]);
         pw[1] = pack_bf16x2(pr[2], pr[3]);
         pw[2] = pack_bf16x2(pr[4], pr[5]);
         pw[3] = pack_bf16x2(pr[6], pr[7]);
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        wave_lds_sync();
-        // O^T += V^T P^T; A = V^T[m = dim 16*dt + l16][k-slot as above]
+        // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const uint16_t* row = vt + (16 * dt + l16) * kVtPitch;
-            const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * l4);
-            const uint2 hi = *reinterpret_cast<const uint2*>(row + 16 + 4 * l4);
-            u32x4 vw;
-            vw[0] = lo.x;
-            vw[1] = lo.y;
-            vw[2] = hi.x;
-            vw[3] = hi.y;
-            acc[dt] = mfma_16x16x32_bf16(__builtin_bit_cast(bf16x8, vw), pb, acc[dt] * alpha);
-        }
-        wave_lds_sync();                           // vt is rewritten by the next chunk
+        for (int dt = 0; dt < 8; ++dt) acc[dt] = mfma_16x16x32_bf16(va[dt], pb, acc[dt] * alpha);
     };
 
-    // Software pipeline over this wave's chunks c_begin + wave + kAttWaves*n:
-    // the K loads of the next chunk are in flight while the current one computes.
-    ChunkBuf bufA, bufB;
-    int c = c_begin + wave;
-    if (c < c_end) fetch(c, bufA);
-    while (c < c_end) {
-        int cn = c + kAttWaves;
-        if (cn < c_end) fetch(cn, bufB);
-        compute(bufA);
-        c = cn;
-        if (c >= c_end) break;
-        cn = c + kAttWaves;
-        if (cn < c_end) fetch(cn, bufA);
-        compute(bufB);
-        c = cn;
+    // Two-unit ring: unit u + 1 streams in while unit u is computed.  Every
+    // thread issues 2 * kCopiesPerUnit copies per unit, so waiting until at
+    // most that many are outstanding means unit u has landed.  Only copies
+    // into LDS are in flight in the loop.
+    static_assert(kMaxUnits % 2 == 0, "units alternate between the two ring buffers");
+    stage(0, kbuf0, vbuf0);
+    stage(1, kbuf1, vbuf1);
+    auto step = [&](int u, const char* kb, const char* vb, char* kn, char* vn) {
+        if (u + 1 < kMaxUnits) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerUnit));   // compile-time
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        lds_barrier();                             // unit u is in LDS
+        compute(u, kb, vb, [&]() {
+            lds_barrier();                         // every wave has its operands: refill the buffers
+            if (u + 2 < kMaxUnits) stage(u + 2, kn, vn);
+        });
+    };
+#pragma unroll
+    for (int u = 0; u < kMaxUnits; u += 2) {
+        step(u, kbuf0, vbuf0, kbuf0, vbuf0);
+        step(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
     }
 
     // ---- merge the four waves (lane holds O^T[dim 16*dt + 4*l4 + r][head l16])
     __syncthreads();
+    float* mrg = reinterpret_cast<float*>(kbuf0);  // [wave][head][dim]
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(&lds.merge.acc[wave][l16][16 * dt + 4 * l4]) = acc[dt];
+        *reinterpret_cast<f32x4*>(&mrg[(wave * kHeadsPerGroup + l16) * kHeadDim + 16 * dt + 4 * l4]) = acc[dt];
     if (lane < 16) {
-        lds.merge.m[wave][lane] = m_run;
-        lds.merge.l[wave][lane] = l_run;
+        mrg_m[wave][lane] = m_run;
+        mrg_l[wave][lane] = l_run;
     }
     __syncthreads();
     const int hh = threadIdx.x >> 4;          // head of this thread
     const int d0 = 8 * (threadIdx.x & 15);    // its 8 dims
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, lds.merge.m[w][hh]);
+    for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, mrg_m[w][hh]);
     float L = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kAttWaves; ++w) {
-        const float mw = lds.merge.m[w][hh];
-        const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        L += wt * lds.merge.l[w][hh];
+        const float mw = mrg_m[w][hh];
+        const float wt = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        L += wt * mrg_l[w][hh];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += wt * lds.merge.acc[w][hh][d0 + e];
+        for (int e = 0; e < 8; ++e) o[e] += wt * mrg[(w * kHeadsPerGroup + hh) * kHeadDim + d0 + e];
     }
     if (ka.n_split == 1) {
         const float inv = 1.f / L;
@@ -328,21 +343,23 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
 }
 
-int num_chunks(int sel_len, int unit) {
-    return unit == kBlock ? sel_len * (kBlock / kChunk) : (sel_len + kChunk - 1) / kChunk;
+int num_units(int sel_len, int unit) {
+    return unit == kBlock ? sel_len : (sel_len + kUnit - 1) / kUnit;
 }
+
+constexpr int kUnitsPerSplitMax = 8;
 
 }  // namespace
 
 int attend_num_splits(int64_t n_q, int sel_len, int unit) {
     const int64_t pairs = n_q * kGroups;
-    const int n_chunks = num_chunks(sel_len, unit);
-    // aim for >= 512 workgroups (measured best on the 32-stream decode), with
-    // two chunks for every wave of a split
-    int64_t want = (512 + pairs - 1) / pairs;
-    const int64_t cap = n_chunks / (2 * kAttWaves) > 0 ? n_chunks / (2 * kAttWaves) : 1;
-    if (want > cap) want = cap;
-    if (want > 16) want = 16;
+    const int n_units = num_units(sel_len, unit);
+    // about one workgroup per compute unit (256), each streaming >= 1 unit,
+    // and at most kUnitsPerSplitMax units per split
+    int64_t want = (256 + pairs - 1) / pairs;
+    if (want > n_units) want = n_units;
+    const int64_t least = (n_units + kUnitsPerSplitMax - 1) / kUnitsPerSplitMax;
+    if (want < least) want = least;
     if (want < 1) want = 1;
     return static_cast<int>(want);
 }
@@ -357,13 +374,20 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     KernelArgs ka;
     ka.a = a;
     ka.n_split = attend_num_splits(a.n_q, a.sel_len, a.unit);
-    ka.n_chunks = num_chunks(a.sel_len, a.unit);
-    ka.chunks_per_split = (ka.n_chunks + ka.n_split - 1) / ka.n_split;
+    ka.n_units = num_units(a.sel_len, a.unit);
+    ka.units_per_split = (ka.n_units + ka.n_split - 1) / ka.n_split;
     const dim3 grid(static_cast<unsigned>(a.n_q * kGroups * ka.n_split));
-    if (a.unit == kBlock)
-        hipLaunchKernelGGL(attend_kernel<false>, grid, dim3(256), 0, s, ka);
-    else
-        hipLaunchKernelGGL(attend_kernel<true>, grid, dim3(256), 0, s, ka);
+    // instantiations for splits of up to 2, 4 and 8 units
+    const int nu = ka.units_per_split;
+    if (a.unit == kBlock) {
+        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<false, 2>), grid, dim3(kAttThreads), 0, s, ka);
+        else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<false, 4>), grid, dim3(kAttThreads), 0, s, ka);
+        else hipLaunchKernelGGL((attend_kernel<false, kUnitsPerSplitMax>), grid, dim3(kAttThreads), 0, s, ka);
+    } else {
+        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<true, 2>), grid, dim3(kAttThreads), 0, s, ka);
+        else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<true, 4>), grid, dim3(kAttThreads), 0, s, ka);
+        else hipLaunchKernelGGL((attend_kernel<true, kUnitsPerSplitMax>), grid, dim3(kAttThreads), 0, s, ka);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ka.n_split == 1) return e;
     hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(a.n_q * kGroups)), dim3(256), 0,
