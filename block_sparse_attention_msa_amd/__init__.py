@@ -30,6 +30,7 @@ MSA_OP_ATTEND_DECODE = 3
 MSA_OP_ATTEND_PREFILL = 4
 DSA_OP_SELECT = 5
 DSA_OP_ATTEND_DECODE = 6
+MSA_OP_BLOCK_SCORES_PREFILL = 7
 
 EXPORTS = (
     "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
             "msa_block_scores": [D, C, P, P, P, I64, I32, P, I64, P],
             "msa_topk_blocks": [D, P, I64, P, I64, I32, P, P, P],
             "msa_select": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
-            "msa_block_scores_prefill": [D, C, P, I32, I32, I64, P, I64, P],
+            "msa_block_scores_prefill": [D, C, P, I32, I32, I64, P, I64, P, ctypes.c_size_t, P],
             "msa_select_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
             "msa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
             "msa_attend_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
@@ -205,10 +206,12 @@ def msa_select(dims, cache, idx_q, stream, pos, max_pos, sel, n_sel, ws, hip_str
            "msa_select")
 
 
-def msa_block_scores_prefill(dims, cache, idx_q, stream_id, pos0, bs, hip_stream=None):
+def msa_block_scores_prefill(dims, cache, idx_q, stream_id, pos0, bs, ws, hip_stream=None):
+    wp, wn = _ws(ws)
     _check(lib().msa_block_scores_prefill(ctypes.byref(dims), ctypes.byref(cache),
                                           _p(idx_q, torch.float32), stream_id, pos0, idx_q.shape[0],
-                                          _p(bs, torch.float32, "bs"), bs.shape[-1], _stream(hip_stream)),
+                                          _p(bs, torch.float32, "bs"), bs.shape[-1], wp, wn,
+                                          _stream(hip_stream)),
            "msa_block_scores_prefill")
 
 

@@ -126,9 +126,11 @@ hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, co
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
                                       int64_t nblk_stride, hipStream_t s);
 
+// ws: prefill_scores_ws_bytes(pos0 + n_q - 1) bytes (the split keys).
+size_t prefill_scores_ws_bytes(int32_t max_pos);
 hipError_t launch_block_scores_prefill(const CacheView& c, const float* idx_q, int32_t stream,
                                        int32_t pos0, int64_t n_q, int nblk, float* bs,
-                                       int64_t nblk_stride, hipStream_t s);
+                                       int64_t nblk_stride, void* ws, hipStream_t s);
 
 hipError_t launch_topk_blocks(const float* bs, int64_t nblk_stride, const int32_t* pos,
                               int64_t n_q, int nblk, int top_k, int32_t* sel, int32_t* n_sel,

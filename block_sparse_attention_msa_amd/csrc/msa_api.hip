@@ -67,6 +67,11 @@ size_t select_ws(int64_t n_q, int32_t max_pos) {
     return align256(static_cast<size_t>(n_q) * kGroups * nblk_of(max_pos) * sizeof(float));
 }
 
+// msa_select_prefill: block scores, then the split keys of the scorer.
+size_t select_prefill_ws(int64_t n_q, int32_t max_pos) {
+    return select_ws(n_q, max_pos) + align256(msa::prefill_scores_ws_bytes(max_pos));
+}
+
 msa::CacheView view(const msa_cache* c) {
     return msa::CacheView{c->idx_k, c->dsa_k, c->k, c->v, c->cap};
 }
@@ -114,9 +119,13 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
     if (check_dims(dims, dsa ? Mode::Dsa : Mode::Msa) != MSA_OK) return bad;
     switch (op) {
         case MSA_OP_SELECT:
-        case MSA_OP_SELECT_PREFILL:
             if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;
             return select_ws(n_q, max_pos);
+        case MSA_OP_SELECT_PREFILL:
+            if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;
+            return select_prefill_ws(n_q, max_pos);
+        case MSA_OP_BLOCK_SCORES_PREFILL:
+            return align256(msa::prefill_scores_ws_bytes(max_pos));
         case MSA_OP_ATTEND_DECODE:
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
         case MSA_OP_ATTEND_PREFILL:
@@ -195,7 +204,7 @@ msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float*
 
 msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
                                     int32_t stream, int32_t pos0, int64_t n_q, float* d_bs,
-                                    int64_t nblk_stride, void* hip_stream) {
+                                    int64_t nblk_stride, void* d_ws, size_t ws_bytes, void* hip_stream) {
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
@@ -205,8 +214,10 @@ msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache
     MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_bs}));
     const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
     if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < msa::prefill_scores_ws_bytes(max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(msa::launch_block_scores_prefill(view(cache), d_idx_q, stream, pos0, n_q,
-                                                       nblk_of(max_pos), d_bs, nblk_stride,
+                                                       nblk_of(max_pos), d_bs, nblk_stride, d_ws,
                                                        static_cast<hipStream_t>(hip_stream)));
 }
 
@@ -223,14 +234,15 @@ msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cache, cons
     const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({d_ws}));
-    if (ws_bytes < select_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < select_prefill_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     // The top-k kernel reads each query's position from device memory; the
     // prefill positions pos0 + i are materialised after the block scores.
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int nblk = nblk_of(max_pos);
     float* bs = static_cast<float*>(d_ws);
+    void* keys_ws = static_cast<char*>(d_ws) + select_ws(n_q, max_pos);
     MSA_TRY(hip_status(msa::launch_block_scores_prefill(view(cache), d_idx_q, stream, pos0, n_q, nblk,
-                                                        bs, nblk, s)));
+                                                        bs, nblk, keys_ws, s)));
     return hip_status(msa::launch_topk_blocks_range(bs, nblk, pos0, n_q, nblk, dims->top_k, d_sel,
                                                     d_n_sel, s));
 }

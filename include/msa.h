@@ -110,7 +110,8 @@ typedef enum msa_op {
     MSA_OP_ATTEND_DECODE = 3,   /* msa_attend_decode */
     MSA_OP_ATTEND_PREFILL = 4,  /* msa_attend_prefill */
     DSA_OP_SELECT = 5,          /* dsa_select */
-    DSA_OP_ATTEND_DECODE = 6    /* dsa_attend_decode */
+    DSA_OP_ATTEND_DECODE = 6,   /* dsa_attend_decode */
+    MSA_OP_BLOCK_SCORES_PREFILL = 7   /* msa_block_scores_prefill */
 } msa_op;
 
 /* Bytes of workspace `op` needs for n_q queries whose positions are all
@@ -188,11 +189,15 @@ MSA_API msa_status msa_select(const msa_dims* dims, const msa_cache* cache, cons
  * positions pos0 .. pos0 + n_q - 1 of stream `stream` (host values), scored
  * with matrix-core tiles.  Same output layout and values as
  * msa_block_scores (f32 sums, summation order differs).
+ * Workspace: msa_workspace_bytes(dims, MSA_OP_BLOCK_SCORES_PREFILL, n_q,
+ * pos0 + n_q - 1) bytes at d_ws (16-byte aligned;
+ * MSA_ERR_WORKSPACE_TOO_SMALL otherwise): the index keys 0 .. pos0 + n_q - 1
+ * of the stream split into bf16 high and low parts, written by the call.
  */
 MSA_API msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache,
                                     const float* d_idx_q, int32_t stream, int32_t pos0,
                                     int64_t n_q, float* d_bs, int64_t nblk_stride,
-                                    void* hip_stream);
+                                    void* d_ws, size_t ws_bytes, void* hip_stream);
 
 /* msa_block_scores_prefill followed by msa_topk_blocks (workspace:
  * MSA_OP_SELECT_PREFILL with max_pos = pos0 + n_q - 1). */

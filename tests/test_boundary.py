@@ -84,6 +84,7 @@ def test_null_misaligned_and_range(L):
     assert sel(ws=None) == NULL
     need = M.workspace_bytes(d, M.MSA_OP_SELECT, 1, 100)
     assert sel(wsb=need - 1) == WS
+    assert sel(wsb=need) != WS                 # exactly enough (fails later only for want of a GPU)
     assert sel(n_q=0) == OK                    # empty call, nothing launched
     assert sel(n_q=0, ws=None) == OK
 
@@ -99,6 +100,14 @@ def test_prefill_range_checks(L):
     assert f(0, 991, 10) == RANGE              # last position 1000 == cap
     assert f(0, 990, 0) == OK
     assert f(0, 0, -5) == SHAPE
+    need = M.workspace_bytes(d, M.MSA_OP_SELECT_PREFILL, 10, 999)
+    fw = lambda wsb: L.msa_select_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 990, 10, A, A, A, wsb, None)
+    assert fw(need - 1) == WS
+    assert fw(need) != WS
+    need = M.workspace_bytes(d, M.MSA_OP_BLOCK_SCORES_PREFILL, 10, 999)
+    fb = lambda wsb: L.msa_block_scores_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 990, 10, A, 8, A, wsb, None)
+    assert fb(need - 1) == WS
+    assert fb(need) != WS
     g = lambda n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 990, n, A, A, A, 1 << 30,
                                        None)
     assert g(11) == RANGE
@@ -143,7 +152,11 @@ def test_workspace_sizes(L):
     # select: n_q * 4 groups * nblk floats, 256-byte aligned
     assert M.workspace_bytes(d, M.MSA_OP_SELECT, 32, 32767) == 32 * 4 * 256 * 4
     assert M.workspace_bytes(d, M.MSA_OP_SELECT, 1, 0) == 256
-    assert M.workspace_bytes(d, M.MSA_OP_SELECT_PREFILL, 4096, 32767) == 4096 * 4 * 256 * 4
+    # prefill select: the block scores, then the keys split into bf16 high
+    # and low parts (4 groups x 512 B per key)
+    assert M.workspace_bytes(d, M.MSA_OP_SELECT_PREFILL, 4096, 32767) == 4096 * 4 * 256 * 4 + 32768 * 4 * 512
+    assert M.workspace_bytes(d, M.MSA_OP_BLOCK_SCORES_PREFILL, 4096, 32767) == 32768 * 4 * 512
+    assert M.workspace_bytes(d, M.MSA_OP_BLOCK_SCORES_PREFILL, 1, 100) == 101 * 4 * 512
     # attention partials: per (query, group, split) 16 heads x (128 + 2) floats
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0

@@ -150,7 +150,7 @@ def _prefill_parity(wl: W.Workload, sample=None):
     idx_q = dev(gw.qs["idx_q"])
     nblk = wl.max_pos // 128 + 1
     bs = torch.empty((n_q, 4, nblk), dtype=torch.float32, device=DEV)
-    M.msa_block_scores_prefill(dims, gw.cache, idx_q, s0, pos0, bs)
+    M.msa_block_scores_prefill(dims, gw.cache, idx_q, s0, pos0, bs, gw.ws(dims, M.MSA_OP_BLOCK_SCORES_PREFILL))
     sel = torch.empty((n_q, 4, wl.top_k), dtype=torch.int32, device=DEV)
     n_sel = torch.empty((n_q, 4), dtype=torch.int32, device=DEV)
     M.msa_select_prefill(dims, gw.cache, idx_q, s0, pos0, sel, n_sel,
