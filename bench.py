@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="decode step only (for profiling)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for rocprofv3 counter runs: one plain 1 GiB device copy (calibration of the "
-                         "byte counters), then 3 decode steps; prints no result line")
+                         "byte counters), then 3 decode steps and one prefill chunk; prints no result line")
     return ap.parse_args()
 
 
@@ -157,6 +157,9 @@ def main():
         for _ in range(3):
             step()
         torch.cuda.synchronize()
+        del idx_k, k, v, cache
+        torch.cuda.empty_cache()
+        bench_prefill(M, W, torch, dev, bits, tens, wsbuf, profile=True)
         log("[bench] profile pass done")
         return
 
@@ -299,7 +302,7 @@ def measure_copy_bandwidth(torch, dev, n_bytes=1 << 30, iters=10):
     return 2 * n_bytes / t / 1e9
 
 
-def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10):
+def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10, profile=False):
     wl = W.CONFIGS["prefill_4096_at_32k"]
     host = W.caches(wl)
     qs = W.queries(wl)
@@ -332,9 +335,11 @@ def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10):
         M.msa_attend_prefill(dims, cache, q, 0, pos0, sel, out, ws_att)
         if e: e[3].record()
 
-    for _ in range(2):
+    for _ in range(2 if not profile else 1):
         run()
     torch.cuda.synchronize()
+    if profile:
+        return {}
     for i in range(iters):
         run(ev[i])
     torch.cuda.synchronize()
