@@ -28,16 +28,16 @@ namespace {
 // The keys are split once, by a pre-pass, into 512-byte rows [hi | lo] per
 // (group, key) in the workspace; the GEMM kernel then copies them straight
 // into LDS (global_load_lds, no registers, no conversion) through a ring of
-// two 64-key stages while the matrix cores work on the previous stage.
+// two 128-key stages while the matrix cores work on the previous stage.
 // ---------------------------------------------------------------------------
 constexpr int kScWaves = 8;
 constexpr int kScThreads = 64 * kScWaves;
 constexpr int kScSub = 2;                                   // 16-query sub-tiles per wave
 constexpr int kScQueryTile = kScWaves * 16 * kScSub;        // 256 queries per workgroup
 constexpr int kScBlocksPerWg = 16;                          // key range of a workgroup: 2048 keys
-constexpr int kScStageKeys = 64;                            // keys per LDS stage
+constexpr int kScStageKeys = 128;                           // keys per LDS stage
 constexpr int kScRowBytes = 2 * kIdxDim * 2;                // one key's [hi | lo] row: 512 B
-constexpr int kScStageBytes = kScStageKeys * kScRowBytes;   // 32 KiB
+constexpr int kScStageBytes = kScStageKeys * kScRowBytes;   // 64 KiB
 constexpr int kScCopies = kScStageBytes / 16 / kScThreads;  // 16-byte copies per thread and stage
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
@@ -211,26 +211,27 @@ __global__ __launch_bounds__(kScThreads, 1) void block_scores_prefill_kernel(ScA
         for (int kt = 0; kt < kScStageKeys / 16; ++kt) {
             if (kt + 1 < kScStageKeys / 16) load_b(sb, kt + 1, bh[(kt + 1) & 1], bl[(kt + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);     // the next tile's reads stay ahead of these products
-            // two independent accumulation chains per sub-tile (even / odd dim steps)
-            f32x4 acc2[kScSub][2];
+            // one accumulation chain per (sub-tile, product), issued round
+            // robin, so that consecutive products never wait on each other
+            f32x4 acc3[3][kScSub];
 #pragma unroll
-            for (int st = 0; st < kScSub; ++st) acc2[st][0] = acc2[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int pr = 0; pr < 3; ++pr)
+#pragma unroll
+                for (int st = 0; st < kScSub; ++st) acc3[pr][st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 bhi = bh[kt & 1][ks];
                 const bf16x8 blo = bl[kt & 1][ks];
 #pragma unroll
-                for (int st = 0; st < kScSub; ++st) {
-                    f32x4& c = acc2[st][ks & 1];
-                    c = mfma_16x16x32_bf16(qhi[st][ks], bhi, c);
-                    c = mfma_16x16x32_bf16(qhi[st][ks], blo, c);
-                    c = mfma_16x16x32_bf16(qlo[st][ks], bhi, c);
-                }
+                for (int st = 0; st < kScSub; ++st) acc3[0][st] = mfma_16x16x32_bf16(qhi[st][ks], bhi, acc3[0][st]);
+#pragma unroll
+                for (int st = 0; st < kScSub; ++st) acc3[1][st] = mfma_16x16x32_bf16(qhi[st][ks], blo, acc3[1][st]);
+#pragma unroll
+                for (int st = 0; st < kScSub; ++st) acc3[2][st] = mfma_16x16x32_bf16(qlo[st][ks], bhi, acc3[2][st]);
             }
-            __builtin_amdgcn_sched_barrier(0);
             f32x4 acc[kScSub];
 #pragma unroll
-            for (int st = 0; st < kScSub; ++st) acc[st] = acc2[st][0] + acc2[st][1];
+            for (int st = 0; st < kScSub; ++st) acc[st] = acc3[0][st] + (acc3[1][st] + acc3[2][st]);
             const int key = kb + 16 * kt + l16;
             const int tile_last = kb + 16 * kt + 15;
             if (tile_last <= wave_min_pos && tile_last < key_end) {   // wave-uniform: no masking
