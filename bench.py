@@ -14,8 +14,10 @@ Also measured in the same run and reported under "extra": the indexer scan
 and decode attention GB/s, the 4096-query prefill chunk at positions
 28672..32767 (append + MFMA block scores + top-16 + block-sparse attention,
 prefill tok/s; plus the attention alone on a selection shared by every 16
-consecutive queries, the overlap real text shows), and the DSA
-lightning-indexer decode (16 streams x 65536).
+consecutive queries, the overlap real text shows), the DSA
+lightning-indexer decode (16 streams x 65536), and one decode step of the
+long-context 8 x 131072 configuration and of the single-stream 4096-slot
+integer configuration (mean and p10/p90 step time).
 
 `roofline` is the dominant kernel (the decode indexer scan): algorithmic bytes
 per launch / mean launch time from HIP events recorded on the stream the
@@ -256,6 +258,10 @@ def main():
         extra.update(bench_prefill(M, W, torch, dev, bits, tens, wsbuf))
         torch.cuda.empty_cache()
         extra.update(bench_dsa(M, W, torch, dev, bits, tens, wsbuf))
+        torch.cuda.empty_cache()
+        for name in ("decode_8x128k", "decode_1x4k_int"):
+            extra.update(bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name))
+            torch.cuda.empty_cache()
 
     traffic = load_traffic("block_scores_decode_kernel@decode_32x32k", "block_scores.hip")
     line = {
@@ -388,6 +394,68 @@ def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10, profile=False):
         "prefill_attend_frac_bf16_mfma": round(att_flop / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "prefill_attend_shared16_us": round(t_sh * 1e3, 2),
         "prefill_attend_shared16_frac_bf16_mfma": round(att_flop / (t_sh * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+    }
+
+
+def bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name, iters=30):
+    """One decode step (append + msa_select + msa_attend_decode) of another
+    decode configuration: the long-context 8 x 131072 scan and the
+    single-stream 4096-slot latency case."""
+    wl = W.CONFIGS[name]
+    host = W.caches(wl)
+    qs = W.queries(wl)
+    S, cap, p = wl.n_stream, wl.cap, wl.max_pos
+    dims = M.msa_dims(16, W.SCALE)
+    idx_k = tens(host["idx_k"])
+    k = bits(host["k"], torch.bfloat16)
+    v = bits(host["v"], torch.bfloat16)
+    cache = M.make_cache(k=k, v=v, idx_k=idx_k)
+    stream = tens(qs["stream"])
+    pos = tens(qs["pos"])
+    idx_q = tens(qs["idx_q"])
+    q = bits(qs["q"], torch.bfloat16)
+    rows = (qs["stream"], qs["pos"])
+    new_idx = tens(host["idx_k"][rows])
+    new_k = bits(host["k"][rows], torch.bfloat16)
+    new_v = bits(host["v"][rows], torch.bfloat16)
+    sel = torch.empty((S, 4, 16), dtype=torch.int32, device=dev)
+    n_sel = torch.empty((S, 4), dtype=torch.int32, device=dev)
+    out = torch.empty((S, 64, 128), dtype=torch.float32, device=dev)
+    ws_sel = wsbuf(dims, M.MSA_OP_SELECT, S, p)
+    ws_att = wsbuf(dims, M.MSA_OP_ATTEND_DECODE, S, p)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+
+    def run(e=None):
+        if e: e[0].record()
+        M.msa_index_append(dims, cache, stream, pos, p, new_idx, new_k, new_v)
+        if e: e[1].record()
+        M.msa_select(dims, cache, idx_q, stream, pos, p, sel, n_sel, ws_sel)
+        if e: e[2].record()
+        M.msa_attend_decode(dims, cache, q, stream, pos, p, sel, out, ws_att)
+        if e: e[3].record()
+
+    for _ in range(5):
+        run()
+    torch.cuda.synchronize()
+    for i in range(iters):
+        run(ev[i])
+    torch.cuda.synchronize()
+    seg = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(iters)])   # ms
+    step = seg.sum(1)
+    scan_bytes = S * (p + 1) * 4 * 128 * 4
+    t_sel = seg[:, 1].mean()
+    log(f"[bench] {name}: step {step.mean() * 1e3:.1f} us (p10 {np.percentile(step, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(step, 90) * 1e3:.1f}): append {seg[:, 0].mean() * 1e3:.1f} select "
+        f"{t_sel * 1e3:.1f} attend {seg[:, 2].mean() * 1e3:.1f} us; indexer {scan_bytes / (t_sel * 1e-3) / 1e9:.0f} GB/s")
+    key = name.replace("decode_", "")
+    return {
+        f"decode_{key}_queries_s": round(S / (step.mean() * 1e-3), 1),
+        f"decode_{key}_us": {"step": round(step.mean() * 1e3, 2), "step_p10": round(np.percentile(step, 10) * 1e3, 2),
+                             "step_p90": round(np.percentile(step, 90) * 1e3, 2),
+                             "append": round(seg[:, 0].mean() * 1e3, 2), "select": round(t_sel * 1e3, 2),
+                             "attend": round(seg[:, 2].mean() * 1e3, 2)},
+        f"decode_{key}_indexer_GBps": round(scan_bytes / (t_sel * 1e-3) / 1e9, 1),
+        f"decode_{key}_indexer_frac_hbm": round(scan_bytes / (t_sel * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
 
 
