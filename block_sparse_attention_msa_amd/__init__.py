@@ -54,7 +54,8 @@ class Dims(ctypes.Structure):
 
 class Cache(ctypes.Structure):
     _fields_ = [("idx_k", ctypes.c_void_p), ("dsa_k", ctypes.c_void_p), ("k", ctypes.c_void_p),
-                ("v", ctypes.c_void_p), ("cap", ctypes.c_int64), ("n_stream", ctypes.c_int32)]
+                ("v", ctypes.c_void_p), ("cap", ctypes.c_int64), ("n_stream", ctypes.c_int32),
+                ("idx_k_f16", ctypes.c_void_p)]
 
 
 def msa_dims(top_k: int = 16, scale: float = 128 ** -0.5) -> Dims:
@@ -155,12 +156,14 @@ def _check(code: int, where: str):
 
 
 def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor] = None,
-               dsa_k: Optional[torch.Tensor] = None) -> Cache:
+               dsa_k: Optional[torch.Tensor] = None, idx_k_f16: Optional[torch.Tensor] = None) -> Cache:
     """Cache descriptor over caller-owned tensors (keep them alive):
-    k, v [S][cap][4][128] bf16; idx_k [S][cap][4][128] f32; dsa_k [S][cap][128] f16."""
+    k, v [S][cap][4][128] bf16; idx_k [S][cap][4][128] f32, or idx_k_f16 the
+    same in f16; dsa_k [S][cap][128] f16."""
     S, cap = k.shape[0], k.shape[1]
     return Cache(_p(idx_k, torch.float32, "idx_k"), _p(dsa_k, torch.float16, "dsa_k"),
-                 _p(k, torch.bfloat16, "k"), _p(v, torch.bfloat16, "v"), cap, S)
+                 _p(k, torch.bfloat16, "k"), _p(v, torch.bfloat16, "v"), cap, S,
+                 _p(idx_k_f16, torch.float16, "idx_k_f16"))
 
 
 # ---------------------------------------------------------------------------

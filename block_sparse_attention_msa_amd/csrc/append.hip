@@ -2,7 +2,8 @@
 //
 // MSA ("Add MiniMax-M3 (MSA: MiniMax Sparse Attention) support",
 // Implementation): the index keys live in their own per-layer F32 cache next
-// to the bf16 K/V cache; the append is an exact copy of the rows.
+// to the bf16 K/V cache; the append is an exact copy of the rows (or, for an
+// fp16 index cache, one round-to-nearest-even conversion of each key).
 // DSA ("deepseek2 : GLM-DSA sparse attention (lightning indexer)", What this
 // does): indexer keys are Hadamard-rotated before they enter the F16 cache.
 // The rotation here is the Sylvester-ordered fast Walsh-Hadamard transform
@@ -46,7 +47,7 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
 
 // One workgroup of 128 threads per new row.
 __global__ __launch_bounds__(128) void append_kernel(
-    float* __restrict__ idx_k, uint16_t* __restrict__ dsa_k, uint16_t* __restrict__ k,
+    float* __restrict__ idx_k, uint16_t* __restrict__ idx_k16, uint16_t* __restrict__ dsa_k, uint16_t* __restrict__ k,
     uint16_t* __restrict__ v, int64_t cap, const int32_t* __restrict__ stream,
     const int32_t* __restrict__ pos, const float* __restrict__ idx_k_new,
     const uint16_t* __restrict__ dsa_key_new, const uint16_t* __restrict__ k_new,
@@ -57,8 +58,15 @@ __global__ __launch_bounds__(128) void append_kernel(
 
     if (idx_k_new) {   // 4 x 128 f32 = 128 x 16 B
         const u32x4* src = reinterpret_cast<const u32x4*>(idx_k_new + i * kGroups * kIdxDim);
-        u32x4* dst = reinterpret_cast<u32x4*>(idx_k + slot * kGroups * kIdxDim);
-        dst[tid] = src[tid];
+        if (idx_k16) {     // fp16 cache: 4 keys -> 8 B per thread
+            const f32x4 x = __builtin_bit_cast(f32x4, src[tid]);
+            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+            const f16x4 h = __builtin_convertvector(x, f16x4);    // round to nearest even
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            reinterpret_cast<u32x2_t*>(idx_k16 + slot * kGroups * kIdxDim)[tid] = __builtin_bit_cast(u32x2_t, h);
+        } else {
+            reinterpret_cast<u32x4*>(idx_k + slot * kGroups * kIdxDim)[tid] = src[tid];
+        }
     }
     if (tid < 64) {    // 4 x 128 bf16 = 64 x 16 B each
         if (k_new) {
@@ -94,14 +102,14 @@ __global__ __launch_bounds__(128) void append_kernel(
 
 }  // namespace
 
-hipError_t launch_append(float* idx_k, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
+hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
                          const int32_t* stream, const int32_t* pos, int64_t n_new,
                          const float* idx_k_new, const uint16_t* dsa_key_new,
                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
     // The scale is computed on the host, as 1 / sqrt(128) in IEEE double.
     const double inv_sqrt_n = 1.0 / __builtin_sqrt(static_cast<double>(kIdxDim));
     hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(n_new)), dim3(128), 0, s, idx_k,
-                       dsa_k, k, v, cap, stream, pos, idx_k_new, dsa_key_new, k_new, v_new,
+                       idx_k16, dsa_k, k, v, cap, stream, pos, idx_k_new, dsa_key_new, k_new, v_new,
                        inv_sqrt_n);
     return hipGetLastError();
 }

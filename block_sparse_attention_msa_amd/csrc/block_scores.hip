@@ -10,7 +10,10 @@
 // Decode: one workgroup per (query, two key blocks).  The F32 index-key cache is
 // streamed once with 128-bit loads; each 16-lane DPP row of a wavefront owns
 // one group's 512-byte slice of a token row, so a token's four group scores
-// come out of one DPP row reduction each and no scores are materialised.
+// come out of one DPP row reduction each and no scores are materialised.  An
+// fp16 index cache (the review thread's F16 indexer setting) is scanned the
+// same way with half the bytes: a lane's 16-byte load holds 8 keys of its
+// group, widened to f32 for the products.
 
 #include "common.hpp"
 
@@ -100,14 +103,87 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
     }
 }
 
+// The same scan over an fp16 index cache: a token row is 4 x 128 fp16 =
+// 1 KiB, lane c of DPP row g holds dims 8c .. 8c+7 of group g (one 16-byte
+// load per token), 16 tokens in flight per wave (16 KiB, as above).
+constexpr int kScanUnroll16 = 16;
+constexpr int kRowU4h = kGroups * kIdxDim / 8;   // 64 sixteen-byte pieces per fp16 token row
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float dot8h(const f32x4& q0, const f32x4& q1, const u32x4& raw) {
+    const f16x8 h = __builtin_bit_cast(f16x8, raw);
+    float d = q0.x * static_cast<float>(h[0]);
+    d = fmaf(q0.y, static_cast<float>(h[1]), d);
+    d = fmaf(q0.z, static_cast<float>(h[2]), d);
+    d = fmaf(q0.w, static_cast<float>(h[3]), d);
+    d = fmaf(q1.x, static_cast<float>(h[4]), d);
+    d = fmaf(q1.y, static_cast<float>(h[5]), d);
+    d = fmaf(q1.z, static_cast<float>(h[6]), d);
+    d = fmaf(q1.w, static_cast<float>(h[7]), d);
+    return d;
+}
+
+__global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kernel(
+    const uint16_t* __restrict__ idx_k, int64_t cap, const float* __restrict__ idx_q,
+    const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
+    float* __restrict__ bs, int64_t nblk_stride, int nblk) {
+    const int64_t i = blockIdx.x;
+    const int b0 = blockIdx.y * kScanBlocksPerWg;
+    const int p = q_pos[i];
+    const int loc = p / kBlock;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int b = b0 + wave / kScanWavesPerBlock;
+    float m = -INFINITY;
+    if (b < nblk && b <= loc) {
+        const f32x4* qrow = reinterpret_cast<const f32x4*>(idx_q + i * kGroups * kIdxDim);
+        const f32x4 q0 = qrow[g * 32 + 2 * c];          // dims 8c .. 8c+3 of group g
+        const f32x4 q1 = qrow[g * 32 + 2 * c + 1];      // dims 8c+4 .. 8c+7
+        const u32x4* rows = reinterpret_cast<const u32x4*>(
+            idx_k + (static_cast<int64_t>(q_stream[i]) * cap + static_cast<int64_t>(b) * kBlock) *
+                        (kGroups * kIdxDim)) + g * 16 + c;
+        const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
+        const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+        int t = t_begin;
+        for (; t + kScanUnroll16 <= t_end; t += kScanUnroll16) {
+            u32x4 a[kScanUnroll16];
+#pragma unroll
+            for (int u = 0; u < kScanUnroll16; ++u) a[u] = __builtin_nontemporal_load(rows + (t + u) * kRowU4h);
+#pragma unroll
+            for (int u = 0; u < kScanUnroll16; ++u) m = fmaxf(m, row16_sum(dot8h(q0, q1, a[u])));
+        }
+        for (; t < t_end; ++t) m = fmaxf(m, row16_sum(dot8h(q0, q1, rows[t * kRowU4h])));
+    }
+    __shared__ float red[kScanWaves][kGroups];
+    if (c == 0) red[wave][g] = m;
+    __syncthreads();
+    if (threadIdx.x < kGroups * kScanBlocksPerWg) {
+        const int gg = threadIdx.x % kGroups;
+        const int bl = threadIdx.x / kGroups;
+        const int bb2 = b0 + bl;
+        if (bb2 < nblk) {
+            float r = -INFINITY;    // stays -inf for blocks past the query's own block
+#pragma unroll
+            for (int w = 0; w < kScanWavesPerBlock; ++w) r = fmaxf(r, red[bl * kScanWavesPerBlock + w][gg]);
+            bs[(i * kGroups + gg) * nblk_stride + bb2] = r;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
                                       int64_t nblk_stride, hipStream_t s) {
     const unsigned ny = static_cast<unsigned>((nblk + kScanBlocksPerWg - 1) / kScanBlocksPerWg);
-    hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
-                       0, s, c.idx_k, c.cap, idx_q, stream, pos, bs, nblk_stride, nblk);
+    if (c.idx_k16)
+        hipLaunchKernelGGL(block_scores_decode_f16_kernel, dim3(static_cast<unsigned>(n_q), ny),
+                           dim3(64 * kScanWaves), 0, s, c.idx_k16, c.cap, idx_q, stream, pos, bs, nblk_stride, nblk);
+    else
+        hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
+                           0, s, c.idx_k, c.cap, idx_q, stream, pos, bs, nblk_stride, nblk);
     return hipGetLastError();
 }
 

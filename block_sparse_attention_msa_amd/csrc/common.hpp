@@ -110,14 +110,15 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
 namespace msa {
 
 struct CacheView {
-    const float* idx_k;
+    const float* idx_k;        // f32 index keys, or NULL when idx_k16 holds them
     const uint16_t* dsa_k;
     const uint16_t* k;
     const uint16_t* v;
     int64_t cap;
+    const uint16_t* idx_k16;   // fp16 index keys, or NULL
 };
 
-hipError_t launch_append(float* idx_k, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
+hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
                          const int32_t* stream, const int32_t* pos, int64_t n_new,
                          const float* idx_k_new, const uint16_t* dsa_key_new,
                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);

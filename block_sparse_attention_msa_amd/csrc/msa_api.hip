@@ -73,7 +73,13 @@ size_t select_prefill_ws(int64_t n_q, int32_t max_pos) {
 }
 
 msa::CacheView view(const msa_cache* c) {
-    return msa::CacheView{c->idx_k, c->dsa_k, c->k, c->v, c->cap};
+    return msa::CacheView{c->idx_k, c->dsa_k, c->k, c->v, c->cap, c->idx_k_f16};
+}
+
+// The MSA index keys: exactly one of the f32 and fp16 caches.
+msa_status check_index_cache(const msa_cache* c) {
+    if (c->idx_k && c->idx_k_f16) return MSA_ERR_UNSUPPORTED;
+    return check_ptrs({c->idx_k ? static_cast<const void*>(c->idx_k) : static_cast<const void*>(c->idx_k_f16)});
 }
 
 msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
@@ -85,11 +91,14 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
     MSA_TRY(check_count_pos(n_new, max_pos, cache));
     if (n_new == 0) return MSA_OK;
     MSA_TRY(check_ptrs({d_stream, d_pos}));
-    if (d_idx_k_new) MSA_TRY(check_ptrs({d_idx_k_new, cache->idx_k}));
+    if (d_idx_k_new) {
+        MSA_TRY(check_ptrs({d_idx_k_new}));
+        MSA_TRY(check_index_cache(cache));
+    }
     if (d_key_new) MSA_TRY(check_ptrs({d_key_new, cache->dsa_k}));
     if (d_k_new) MSA_TRY(check_ptrs({d_k_new, cache->k}));
     if (d_v_new) MSA_TRY(check_ptrs({d_v_new, cache->v}));
-    return hip_status(msa::launch_append(cache->idx_k, cache->dsa_k, cache->k, cache->v, cache->cap,
+    return hip_status(msa::launch_append(cache->idx_k, cache->idx_k_f16, cache->dsa_k, cache->k, cache->v, cache->cap,
                                          d_stream, d_pos, n_new, d_idx_k_new, d_key_new, d_k_new,
                                          d_v_new, static_cast<hipStream_t>(hip_stream)));
 }
@@ -161,7 +170,8 @@ msa_status msa_block_scores(const msa_dims* dims, const msa_cache* cache, const 
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
-    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_stream, d_pos, d_bs}));
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_idx_q, d_stream, d_pos, d_bs}));
     if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
     return hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q,
                                                       nblk_of(max_pos), d_bs, nblk_stride,
@@ -190,7 +200,8 @@ msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float*
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
-    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({d_ws}));
     if (ws_bytes < select_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
@@ -211,7 +222,8 @@ msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
-    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_bs}));
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_idx_q, d_bs}));
     const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
     if (nblk_stride < nblk_of(max_pos)) return MSA_ERR_BAD_SHAPE;
     MSA_TRY(check_ptrs({d_ws}));
@@ -230,7 +242,8 @@ msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cache, cons
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
-    MSA_TRY(check_ptrs({cache->idx_k, d_idx_q, d_sel, d_n_sel}));
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_idx_q, d_sel, d_n_sel}));
     const int32_t max_pos = static_cast<int32_t>(pos0 + n_q - 1);
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({d_ws}));

@@ -67,20 +67,31 @@ __device__ __forceinline__ void sc_lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Pre-pass: keys 0 .. n_keys-1 of `stream` -> khl[g][key][0..127 hi, 128..255 lo].
-__global__ __launch_bounds__(256) void split_keys_kernel(const float* __restrict__ idx_k, int64_t cap,
+// Pre-pass: keys 0 .. n_keys-1 of `stream` -> khl[g][key][0..127 hi, 128..255 lo],
+// from the f32 index cache or (idx_k16 non-NULL) the fp16 one, whose values
+// widen to f32 exactly.
+__global__ __launch_bounds__(256) void split_keys_kernel(const float* __restrict__ idx_k,
+                                                         const uint16_t* __restrict__ idx_k16, int64_t cap,
                                                          int32_t stream, int64_t n_keys,
                                                          uint16_t* __restrict__ khl) {
-    const int64_t n8 = n_keys * kGroups * (kIdxDim / 8);   // 8-float pieces
-    const float* src = idx_k + static_cast<int64_t>(stream) * cap * kGroups * kIdxDim;
+    const int64_t n8 = n_keys * kGroups * (kIdxDim / 8);   // 8-key pieces
+    const int64_t row0 = static_cast<int64_t>(stream) * cap * kGroups * kIdxDim;
     for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n8;
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int64_t key = e / (kGroups * (kIdxDim / 8));
         const int g = static_cast<int>((e / (kIdxDim / 8)) % kGroups);
         const int d8 = static_cast<int>(e % (kIdxDim / 8));
-        const float* x = src + (key * kGroups + g) * kIdxDim + 8 * d8;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(x);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(x + 4);
+        const int64_t off = row0 + (key * kGroups + g) * kIdxDim + 8 * d8;
+        f32x4 x0, x1;
+        if (idx_k16) {
+            typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+            const f16x8 h = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(idx_k16 + off));
+            x0 = f32x4{static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]), static_cast<float>(h[3])};
+            x1 = f32x4{static_cast<float>(h[4]), static_cast<float>(h[5]), static_cast<float>(h[6]), static_cast<float>(h[7])};
+        } else {
+            x0 = *reinterpret_cast<const f32x4*>(idx_k + off);
+            x1 = *reinterpret_cast<const f32x4*>(idx_k + off + 4);
+        }
         __bf16 h[8], l[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) split_bf16(c < 4 ? x0[c] : x1[c - 4], h[c], l[c]);
@@ -299,7 +310,8 @@ hipError_t launch_block_scores_prefill(const CacheView& c, const float* idx_q, i
     const int64_t n8 = n_keys * kGroups * (kIdxDim / 8);
     const int64_t want = (n8 + 255) / 256;
     const unsigned split_grid = static_cast<unsigned>(want < 8192 ? want : 8192);
-    hipLaunchKernelGGL(split_keys_kernel, dim3(split_grid), dim3(256), 0, s, c.idx_k, c.cap, stream, n_keys, khl);
+    hipLaunchKernelGGL(split_keys_kernel, dim3(split_grid), dim3(256), 0, s, c.idx_k, c.idx_k16, c.cap, stream,
+                       n_keys, khl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     ScArgs a;

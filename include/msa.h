@@ -95,12 +95,20 @@ typedef struct msa_dims {
 
 /* Per-layer caches (device memory owned by the caller). */
 typedef struct msa_cache {
-    float* idx_k;       /* MSA index keys, or NULL when unused */
+    float* idx_k;       /* MSA index keys (f32), or NULL when unused */
     uint16_t* dsa_k;    /* DSA rotated indexer keys (fp16), or NULL */
     uint16_t* k;        /* bf16 keys */
     uint16_t* v;        /* bf16 values (not transposed) */
     int64_t cap;        /* slots per stream */
     int32_t n_stream;   /* independent streams (sequences) */
+    /* MSA index keys stored as fp16 [n_stream][cap][n_group][idx_dim], or
+     * NULL.  [MSA-PR] review thread, indexer precision: the index cache
+     * type is a setting (F32 by default) and F16 indexer tensors were
+     * tested beside F32.  msa_index_append rounds the f32 keys it receives
+     * to fp16 (nearest, ties to even); scores still accumulate in f32.  The
+     * index operations use whichever of idx_k / idx_k_f16 is set; setting
+     * both is MSA_ERR_UNSUPPORTED.  Halves the bytes the decode scan reads. */
+    uint16_t* idx_k_f16;
 } msa_cache;
 
 /* Operations whose workspace size can be queried. */

@@ -139,6 +139,24 @@ def test_append_validation(L):
     assert L.dsa_index_append(ctypes.byref(dd), ctypes.byref(cd), A, A, 1, 5, A, None, None, None) == NULL
 
 
+def test_fp16_index_cache_validation(L):
+    d = M.msa_dims()
+    both = M.Cache(A, A, A, A, 4096, 2, B)           # f32 and fp16 index caches at once
+    f16 = M.Cache(None, A, A, A, 4096, 2, B)         # fp16 only
+    f16_mis = M.Cache(None, A, A, A, 4096, 2, MIS)
+    sel = lambda c: L.msa_select(ctypes.byref(d), ctypes.byref(c), A, A, A, 1, 100, A, A, A, 1 << 30, None)
+    assert sel(both) == UNSUP
+    assert sel(f16) != UNSUP and sel(f16) not in (NULL, ALIGN)   # accepted (fails later only for want of a GPU)
+    assert sel(f16_mis) == ALIGN
+    assert L.msa_block_scores(ctypes.byref(d), ctypes.byref(both), A, A, A, 1, 100, A, 1, None) == UNSUP
+    assert L.msa_select_prefill(ctypes.byref(d), ctypes.byref(both), A, 0, 0, 10, A, A, A, 1 << 30, None) == UNSUP
+    assert L.msa_block_scores_prefill(ctypes.byref(d), ctypes.byref(both), A, 0, 0, 10, A, 1, A, 1 << 30,
+                                      None) == UNSUP
+    app = lambda c: L.msa_index_append(ctypes.byref(d), ctypes.byref(c), A, A, 1, 5, A, None, None, None)
+    assert app(both) == UNSUP
+    assert app(f16_mis) == ALIGN
+
+
 def test_topk_block_limit(L):
     d = M.msa_dims()
     # 4096 blocks of 128 is the most a top-k wave ranks
