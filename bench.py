@@ -207,35 +207,50 @@ def main():
     log(f"[bench] decode step {ms_per_step * 1e3:.1f} us: append {t_append * 1e3:.1f} scan {t_scan * 1e3:.1f} "
         f"topk {t_topk * 1e3:.1f} attend {t_att * 1e3:.1f} us; scan {scan_gbps:.0f} GB/s, attend {att_gbps:.0f} GB/s")
 
+    def step_segments(c):
+        """Mean per-kernel times (ms) of the decode step on cache c."""
+        evc = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
+
+        def run(e=None):
+            if e: e[0].record()
+            M.msa_index_append(dims, c, stream, pos, p, new_idx, new_k, new_v)
+            if e: e[1].record()
+            M.msa_block_scores(dims, c, idx_q, stream, pos, p, bs)
+            if e: e[2].record()
+            M.msa_topk_blocks(dims, bs, pos, p, sel, n_sel)
+            if e: e[3].record()
+            M.msa_attend_decode(dims, c, q, stream, pos, p, sel, out, ws_att)
+            if e: e[4].record()
+
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        for i in range(n_ev):
+            run(evc[i])
+        torch.cuda.synchronize()
+        return np.array([[evc[i][j].elapsed_time(evc[i][j + 1]) for j in range(4)] for i in range(n_ev)]).mean(0)
+
     # The same step on an fp16 index cache (the keys rounded to fp16 on the
     # device): the scan reads half the bytes.
     idx_k16 = idx_k.to(torch.float16)
-    cache16 = M.make_cache(k=k, v=v, idx_k_f16=idx_k16)
-    ev16 = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
-
-    def step16(e=None):
-        if e: e[0].record()
-        M.msa_index_append(dims, cache16, stream, pos, p, new_idx, new_k, new_v)
-        if e: e[1].record()
-        M.msa_block_scores(dims, cache16, idx_q, stream, pos, p, bs)
-        if e: e[2].record()
-        M.msa_topk_blocks(dims, bs, pos, p, sel, n_sel)
-        if e: e[3].record()
-        M.msa_attend_decode(dims, cache16, q, stream, pos, p, sel, out, ws_att)
-        if e: e[4].record()
-
-    for _ in range(args.warmup):
-        step16()
-    torch.cuda.synchronize()
-    for i in range(n_ev):
-        step16(ev16[i])
-    torch.cuda.synchronize()
-    seg16 = np.array([[ev16[i][j].elapsed_time(ev16[i][j + 1]) for j in range(4)] for i in range(n_ev)]).mean(0)
+    seg16 = step_segments(M.make_cache(k=k, v=v, idx_k_f16=idx_k16))
     step16_ms = seg16.sum()
     scan16_bytes = S * (p + 1) * 4 * 128 * 2 + S * 4 * 128 * 4 + S * 4 * nblk * 4
     log(f"[bench] fp16 index cache: decode step {step16_ms * 1e3:.1f} us ({S / (step16_ms * 1e-3):.0f} queries/s), "
         f"scan {seg16[1] * 1e3:.1f} us = {scan16_bytes / (seg16[1] * 1e-3) / 1e9:.0f} GB/s")
-    del idx_k16, cache16
+    del idx_k16
+
+    # The same step on a paged cache: the same buffers seen as a pool of
+    # S * cap / 128 pages of 128 tokens, each stream's blocks scattered over
+    # the pool by a seeded permutation.
+    n_pages = S * cap // 128
+    table = tens(np.random.default_rng(0).permutation(n_pages).astype(np.int32).reshape(S, cap // 128))
+    pool = lambda t: t.view((n_pages * 128,) + tuple(t.shape[2:]))
+    seg_pg = step_segments(M.make_cache(k=pool(k), v=pool(v), idx_k=pool(idx_k), block_table=table, cap=cap))
+    steppg_ms = seg_pg.sum()
+    log(f"[bench] paged cache: decode step {steppg_ms * 1e3:.1f} us ({S / (steppg_ms * 1e-3):.0f} queries/s), "
+        f"scan {seg_pg[1] * 1e3:.1f} us = {scan_bytes / (seg_pg[1] * 1e-3) / 1e9:.0f} GB/s, "
+        f"attend {seg_pg[3] * 1e3:.1f} us")
 
     copy_gbps = measure_copy_bandwidth(torch, dev)
     log(f"[bench] device copy {copy_gbps:.0f} GB/s (read + write)")
@@ -255,6 +270,9 @@ def main():
                               "scan_us": round(seg16[1] * 1e3, 2),
                               "scan_GBps": round(scan16_bytes / (seg16[1] * 1e-3) / 1e9, 1),
                               "scan_frac_hbm": round(scan16_bytes / (seg16[1] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "decode_paged": {"queries_s": round(S / (steppg_ms * 1e-3), 1), "step_us": round(steppg_ms * 1e3, 2),
+                         "scan_us": round(seg_pg[1] * 1e3, 2), "attend_us": round(seg_pg[3] * 1e3, 2),
+                         "scan_GBps": round(scan_bytes / (seg_pg[1] * 1e-3) / 1e9, 1)},
     }
 
     # ------------------------------------------------------------------

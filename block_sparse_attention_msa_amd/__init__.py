@@ -55,7 +55,8 @@ class Dims(ctypes.Structure):
 class Cache(ctypes.Structure):
     _fields_ = [("idx_k", ctypes.c_void_p), ("dsa_k", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("cap", ctypes.c_int64), ("n_stream", ctypes.c_int32),
-                ("idx_k_f16", ctypes.c_void_p)]
+                ("idx_k_f16", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("table_stride", ctypes.c_int32)]
 
 
 def msa_dims(top_k: int = 16, scale: float = 128 ** -0.5) -> Dims:
@@ -156,14 +157,29 @@ def _check(code: int, where: str):
 
 
 def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor] = None,
-               dsa_k: Optional[torch.Tensor] = None, idx_k_f16: Optional[torch.Tensor] = None) -> Cache:
-    """Cache descriptor over caller-owned tensors (keep them alive):
-    k, v [S][cap][4][128] bf16; idx_k [S][cap][4][128] f32, or idx_k_f16 the
-    same in f16; dsa_k [S][cap][128] f16."""
-    S, cap = k.shape[0], k.shape[1]
-    return Cache(_p(idx_k, torch.float32, "idx_k"), _p(dsa_k, torch.float16, "dsa_k"),
-                 _p(k, torch.bfloat16, "k"), _p(v, torch.bfloat16, "v"), cap, S,
-                 _p(idx_k_f16, torch.float16, "idx_k_f16"))
+               dsa_k: Optional[torch.Tensor] = None, idx_k_f16: Optional[torch.Tensor] = None,
+               block_table: Optional[torch.Tensor] = None, cap: Optional[int] = None) -> Cache:
+    """Cache descriptor over caller-owned tensors: k, v [S][cap][4][128] bf16;
+    idx_k [S][cap][4][128] f32, or idx_k_f16 the same in f16; dsa_k
+    [S][cap][128] f16.
+    Paged: block_table [S][stride] int32 (page of each logical 128-token
+    block), the caches pools [n_pages * 128][4][128] (dsa_k [n_pages * 128][128]),
+    and cap the logical capacity per stream (<= stride * 128).
+    The descriptor holds references to the tensors, so their memory stays
+    allocated while it lives."""
+    if block_table is None:
+        S, cap_ = k.shape[0], k.shape[1]
+        table, stride = None, 0
+    else:
+        if cap is None:
+            raise ValueError("a paged cache needs cap (positions per stream)")
+        S, stride = block_table.shape
+        cap_, table = cap, _p(block_table, torch.int32, "block_table")
+    c = Cache(_p(idx_k, torch.float32, "idx_k"), _p(dsa_k, torch.float16, "dsa_k"),
+              _p(k, torch.bfloat16, "k"), _p(v, torch.bfloat16, "v"), cap_, S,
+              _p(idx_k_f16, torch.float16, "idx_k_f16"), table, stride)
+    c.tensors = (k, v, idx_k, dsa_k, idx_k_f16, block_table)
+    return c
 
 
 # ---------------------------------------------------------------------------

@@ -48,13 +48,13 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
 // One workgroup of 128 threads per new row.
 __global__ __launch_bounds__(128) void append_kernel(
     float* __restrict__ idx_k, uint16_t* __restrict__ idx_k16, uint16_t* __restrict__ dsa_k, uint16_t* __restrict__ k,
-    uint16_t* __restrict__ v, int64_t cap, const int32_t* __restrict__ stream,
+    uint16_t* __restrict__ v, Pager pg, const int32_t* __restrict__ stream,
     const int32_t* __restrict__ pos, const float* __restrict__ idx_k_new,
     const uint16_t* __restrict__ dsa_key_new, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, double inv_sqrt_n) {
     const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
-    const int64_t slot = static_cast<int64_t>(stream[i]) * cap + pos[i];
+    const int64_t slot = pg.row(stream[i], pos[i]);
 
     if (idx_k_new) {   // 4 x 128 f32 = 128 x 16 B
         const u32x4* src = reinterpret_cast<const u32x4*>(idx_k_new + i * kGroups * kIdxDim);
@@ -102,14 +102,14 @@ __global__ __launch_bounds__(128) void append_kernel(
 
 }  // namespace
 
-hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
+hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, const Pager& pg,
                          const int32_t* stream, const int32_t* pos, int64_t n_new,
                          const float* idx_k_new, const uint16_t* dsa_key_new,
                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
     // The scale is computed on the host, as 1 / sqrt(128) in IEEE double.
     const double inv_sqrt_n = 1.0 / __builtin_sqrt(static_cast<double>(kIdxDim));
     hipLaunchKernelGGL(append_kernel, dim3(static_cast<unsigned>(n_new)), dim3(128), 0, s, idx_k,
-                       idx_k16, dsa_k, k, v, cap, stream, pos, idx_k_new, dsa_key_new, k_new, v_new,
+                       idx_k16, dsa_k, k, v, pg, stream, pos, idx_k_new, dsa_key_new, k_new, v_new,
                        inv_sqrt_n);
     return hipGetLastError();
 }

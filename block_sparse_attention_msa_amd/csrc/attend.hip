@@ -36,8 +36,9 @@ constexpr int kUnitBytes = kUnit * kRowBytes;     // 32 KiB of K (and of V) per 
 constexpr int kCopiesPerUnit = kUnitBytes / 16 / kAttThreads;   // 16-byte copies per thread, K or V
 constexpr int kPartFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;   // acc + (m, l)
 constexpr float kLog2e = 1.4426950408889634f;
-// Largest id list one split stages: 4096 DSA tokens (or 64 MSA blocks).
-constexpr int kMaxSplitEntries = 4096;
+// Largest id list one split stages: a split streams at most 8 units (see
+// attend_num_splits), i.e. 1024 DSA tokens or 8 MSA blocks.
+constexpr int kMaxSplitEntries = 8 * kUnit;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     __shared__ __attribute__((aligned(16))) char vbuf0[kUnitBytes];
     __shared__ __attribute__((aligned(16))) char vbuf1[kUnitBytes];
     __shared__ int32_t sel_s[kMaxSplitEntries];    // this split's ids
+    __shared__ int32_t row_s[kMaxSplitEntries + 1];   // their cache rows (MSA: a block's first row), then the query's own
     __shared__ float mrg_m[kAttWaves][kHeadsPerGroup];
     __shared__ float mrg_l[kAttWaves][kHeadsPerGroup];
     __shared__ int n_valid_s;
@@ -108,8 +110,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     const int p = a.pos[i];
     const int32_t* sel = a.sel + i * static_cast<int64_t>(a.sel_len) * (kTokenIds ? 1 : kGroups) +
                          g * a.sel_g_stride;
-    const uint16_t* kg = a.k + (s * a.cap * kGroups + g) * kHeadDim;   // row t at + t*kGroups*kHeadDim
-    const uint16_t* vg = a.v + (s * a.cap * kGroups + g) * kHeadDim;
+    const uint16_t* kg = a.k + g * kHeadDim;   // cache row r at + r*kGroups*kHeadDim
+    const uint16_t* vg = a.v + g * kHeadDim;
+    const Pager pg = a.pg;
+    const int own_row = static_cast<int>(pg.row(s, p));   // cache rows fit int32 (< 2 TiB of K)
     constexpr int kRow = kGroups * kHeadDim;
 
     // this split's units and their ids (ascending, -1 padding at the end)
@@ -125,13 +129,18 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks + 8 * l4);
     }
-    if (threadIdx.x == 0) n_valid_s = 0;
+    if (threadIdx.x == 0) {
+        n_valid_s = 0;
+        row_s[kMaxSplitEntries] = own_row;
+    }
     __syncthreads();
     for (int e = e_begin + static_cast<int>(threadIdx.x); e < e_begin + (u_end - u_begin) * (kTokenIds ? kUnit : 1);
          e += kAttThreads) {
         int id = e < e_end ? sel[e] : -1;
         if (kTokenIds ? (id > p) : (id > p / kBlock)) id = -1;
         sel_s[e - e_begin] = id;
+        row_s[e - e_begin] = id < 0 ? own_row
+                                    : static_cast<int>(kTokenIds ? pg.row(s, id) : pg.block_row(s, id));
         // units are valid up to the first unit whose first id is padding
         if (id >= 0 && (kTokenIds ? ((e - e_begin) % kUnit == 0) : true))
             atomicMax(&n_valid_s, (e - e_begin) / (kTokenIds ? kUnit : 1) + 1);
@@ -144,16 +153,22 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     // Copies of unit u into (kd, vd): slot c = 256*j + thread holds segment
     // (c % 16) ^ f(row) of row c / 16; rows whose key is padding or past the
     // query read the query's own row (finite, masked below).
-    auto stage = [&](int u, char* kd, char* vd) {
+    auto stage = [&](int u, char* kd, char* vd) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kCopiesPerUnit; ++j) {
             const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
             const int row = c >> 4;
             const int seg = (c & 15) ^ rowperm(row);
-            int tok = p;
-            if (u < n_units) tok = kTokenIds ? sel_s[u * kUnit + row] : sel_s[u] * kBlock + row;
-            if (tok < 0 || tok > p) tok = p;
-            const int64_t off = static_cast<int64_t>(tok) * kRow + 8 * seg;
+            // every read is an unconditional LDS read (in bounds for every
+            // u < kMaxUnits; the query's own row sits past the entries), so
+            // that no select between LDS and other memory becomes a flat load
+            const int e = kTokenIds ? u * kUnit + row : u;
+            const int tok = kTokenIds ? sel_s[e] : sel_s[e] * kBlock + row;
+            const int r_e = row_s[e];
+            const int r_own = row_s[kMaxSplitEntries];
+            const bool bad = u >= n_units || tok < 0 || tok > p;
+            const int crow = bad ? r_own : r_e + (kTokenIds ? 0 : row);
+            const int64_t off = static_cast<int64_t>(crow) * kRow + 8 * seg;
             __builtin_amdgcn_global_load_lds(kg + off, LDS_PTR(void, kd + (kAttThreads * j + 64 * wave) * 16), 16, 0, 0);
             __builtin_amdgcn_global_load_lds(vg + off, LDS_PTR(void, vd + (kAttThreads * j + 64 * wave) * 16), 16, 0, 0);
         }
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     // Online-softmax update with keys 32w .. 32w+31 of unit u.  The unit's
     // K and V operands are read first; `release` runs once they are in
     // registers (the ring buffer may then be refilled) and before the math.
-    auto compute = [&](int u, const char* kb, const char* vb, auto&& release) {
+    auto compute = [&](int u, const char* kb, const char* vb, auto&& release) __attribute__((always_inline)) {
         // validity of this lane's keys 32w + 16t + 4*l4 + r
         uint32_t valid = 0;
         if (u < n_units)
@@ -256,11 +271,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     static_assert(kMaxUnits % 2 == 0, "units alternate between the two ring buffers");
     stage(0, kbuf0, vbuf0);
     stage(1, kbuf1, vbuf1);
-    auto step = [&](int u, const char* kb, const char* vb, char* kn, char* vn) {
+    auto step = [&](int u, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
         if (u + 1 < kMaxUnits) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerUnit));   // compile-time
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();                             // unit u is in LDS
-        compute(u, kb, vb, [&]() {
+        compute(u, kb, vb, [&]() __attribute__((always_inline)) {
             lds_barrier();                         // every wave has its operands: refill the buffers
             if (u + 2 < kMaxUnits) stage(u + 2, kn, vn);
         });
@@ -348,6 +363,7 @@ int num_units(int sel_len, int unit) {
 }
 
 constexpr int kUnitsPerSplitMax = 8;
+static_assert(kMaxSplitEntries == kUnitsPerSplitMax * kUnit, "ids one split stages");
 
 }  // namespace
 

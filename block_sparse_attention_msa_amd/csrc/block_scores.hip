@@ -48,7 +48,7 @@ __device__ __forceinline__ float dot8(const f32x4& q0, const f32x4& q1, const f3
 // tokens each.  Index keys are read once with non-temporal 128-bit loads
 // (they are streamed, never re-read), 16 KiB per wave in flight.
 __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
-    const float* __restrict__ idx_k, int64_t cap, const float* __restrict__ idx_q,
+    const float* __restrict__ idx_k, Pager pg, const float* __restrict__ idx_q,
     const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
     float* __restrict__ bs, int64_t nblk_stride, int nblk) {
     const int64_t i = blockIdx.x;
@@ -66,8 +66,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
         const f32x4 q0 = qrow[g * 32 + c];
         const f32x4 q1 = qrow[g * 32 + 16 + c];
         const f32x4* rows = reinterpret_cast<const f32x4*>(
-            idx_k + (static_cast<int64_t>(q_stream[i]) * cap + static_cast<int64_t>(b) * kBlock) *
-                        (kGroups * kIdxDim)) + g * 32 + c;
+            idx_k + pg.block_row_uniform(q_stream[i], b) * (kGroups * kIdxDim)) + g * 32 + c;
         const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
         const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
         int t = t_begin;
@@ -124,7 +123,7 @@ __device__ __forceinline__ float dot8h(const f32x4& q0, const f32x4& q1, const u
 }
 
 __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kernel(
-    const uint16_t* __restrict__ idx_k, int64_t cap, const float* __restrict__ idx_q,
+    const uint16_t* __restrict__ idx_k, Pager pg, const float* __restrict__ idx_q,
     const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
     float* __restrict__ bs, int64_t nblk_stride, int nblk) {
     const int64_t i = blockIdx.x;
@@ -142,8 +141,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kerne
         const f32x4 q0 = qrow[g * 32 + 2 * c];          // dims 8c .. 8c+3 of group g
         const f32x4 q1 = qrow[g * 32 + 2 * c + 1];      // dims 8c+4 .. 8c+7
         const u32x4* rows = reinterpret_cast<const u32x4*>(
-            idx_k + (static_cast<int64_t>(q_stream[i]) * cap + static_cast<int64_t>(b) * kBlock) *
-                        (kGroups * kIdxDim)) + g * 16 + c;
+            idx_k + pg.block_row_uniform(q_stream[i], b) * (kGroups * kIdxDim)) + g * 16 + c;
         const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
         const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
         int t = t_begin;
@@ -180,10 +178,10 @@ hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, co
     const unsigned ny = static_cast<unsigned>((nblk + kScanBlocksPerWg - 1) / kScanBlocksPerWg);
     if (c.idx_k16)
         hipLaunchKernelGGL(block_scores_decode_f16_kernel, dim3(static_cast<unsigned>(n_q), ny),
-                           dim3(64 * kScanWaves), 0, s, c.idx_k16, c.cap, idx_q, stream, pos, bs, nblk_stride, nblk);
+                           dim3(64 * kScanWaves), 0, s, c.idx_k16, c.pg, idx_q, stream, pos, bs, nblk_stride, nblk);
     else
         hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
-                           0, s, c.idx_k, c.cap, idx_q, stream, pos, bs, nblk_stride, nblk);
+                           0, s, c.idx_k, c.pg, idx_q, stream, pos, bs, nblk_stride, nblk);
     return hipGetLastError();
 }
 

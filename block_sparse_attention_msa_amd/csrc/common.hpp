@@ -109,6 +109,34 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
 // ---------------------------------------------------------------------------
 namespace msa {
 
+// Token rows of the caches.  Without a block table, stream s owns rows
+// s * cap .. s * cap + cap - 1 (slot == position).  With one, the caches are
+// pools of 128-row pages: logical block b of stream s lives in page
+// table[s * stride + b], and its 128 tokens are consecutive rows there.
+struct Pager {
+    const int32_t* table;      // [n_stream][stride] page of each logical block, or NULL
+    int32_t stride;
+    int64_t cap;
+    __device__ __forceinline__ int64_t row(int64_t s, int tok) const {
+        return table ? static_cast<int64_t>(table[s * stride + (tok >> 7)]) * kBlock + (tok & (kBlock - 1))
+                     : s * cap + tok;
+    }
+    // first row of logical block b (its 128 rows follow)
+    __device__ __forceinline__ int64_t block_row(int64_t s, int b) const {
+        return table ? static_cast<int64_t>(table[s * stride + b]) * kBlock : s * cap + static_cast<int64_t>(b) * kBlock;
+    }
+    // the same for a (s, b) every lane of the wave shares: the table entry is
+    // read through the scalar cache (no vector-memory load, which would be
+    // counted with the copies into LDS in flight)
+    __device__ __forceinline__ int64_t block_row_uniform(int64_t s, int b) const {
+        if (!table) return s * cap + static_cast<int64_t>(b) * kBlock;
+        const __attribute__((address_space(4))) int32_t* t =
+            (const __attribute__((address_space(4))) int32_t*)(reinterpret_cast<uintptr_t>(table));
+        return static_cast<int64_t>(t[s * stride + b]) * kBlock;
+    }
+};
+static_assert(kBlock == 128, "pages are MSA blocks of 128 tokens");
+
 struct CacheView {
     const float* idx_k;        // f32 index keys, or NULL when idx_k16 holds them
     const uint16_t* dsa_k;
@@ -116,9 +144,10 @@ struct CacheView {
     const uint16_t* v;
     int64_t cap;
     const uint16_t* idx_k16;   // fp16 index keys, or NULL
+    Pager pg;
 };
 
-hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, int64_t cap,
+hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, const Pager& pg,
                          const int32_t* stream, const int32_t* pos, int64_t n_new,
                          const float* idx_k_new, const uint16_t* dsa_key_new,
                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
@@ -146,7 +175,7 @@ hipError_t launch_topk_blocks_range(const float* bs, int64_t nblk_stride, int32_
 struct AttendArgs {
     const uint16_t* k;
     const uint16_t* v;
-    int64_t cap;
+    Pager pg;
     const uint16_t* q;
     const int32_t* stream;   // per query
     const int32_t* pos;      // per query
@@ -165,12 +194,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 // Prefill attention for the consecutive positions pos0 .. pos0 + n_q - 1 of
 // one stream (MSA blocks); ws holds the per-tile step lists.
 size_t prefill_attend_ws_bytes(int64_t n_q, int top_k);
-hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
+hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pager& pg, const uint16_t* q,
                                  int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
                                  float scale, float* out, void* ws, hipStream_t s);
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
-hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,
+hipError_t launch_dsa_select(const uint16_t* dsa_k, const Pager& pg, const uint16_t* q_idx,
                              const int32_t* stream, const int32_t* pos, int64_t n_q,
                              int32_t max_pos, int top_k, int32_t* sel, int32_t* n_sel,
                              void* ws, hipStream_t s);

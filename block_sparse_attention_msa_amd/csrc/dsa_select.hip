@@ -35,7 +35,7 @@ __device__ __forceinline__ float dot8_f16(const u32x4& q, const u32x4& k) {
     return d;
 }
 
-__global__ __launch_bounds__(256) void dsa_score_kernel(const uint16_t* __restrict__ dsa_k, int64_t cap,
+__global__ __launch_bounds__(256) void dsa_score_kernel(const uint16_t* __restrict__ dsa_k, Pager pg,
                                                         const uint16_t* __restrict__ q_idx,
                                                         const int32_t* __restrict__ q_stream,
                                                         const int32_t* __restrict__ q_pos,
@@ -49,17 +49,22 @@ __global__ __launch_bounds__(256) void dsa_score_kernel(const uint16_t* __restri
     const int r = lane >> 4;     // key row within a group of four
     const int c = lane & 15;     // 16-byte column (8 fp16 dims)
     const u32x4 q = *reinterpret_cast<const u32x4*>(q_idx + i * kIdxDim + 8 * c);
-    const uint16_t* base = dsa_k + static_cast<int64_t>(q_stream[i]) * cap * kIdxDim;
+    const int64_t s = q_stream[i];
     float* out = scores + i * stride;
     const int j_begin = j_wg + wave * (kScoreKeysPerWg / 4);
     const int j_end = min(j_begin + kScoreKeysPerWg / 4, p + 1);
+    static_assert(kBlock % (4 * kScoreUnroll) == 0, "an iteration's keys lie in one 128-key block");
     for (int j0 = j_begin; j0 < j_end; j0 += 4 * kScoreUnroll) {
+        // keys j0 .. j0 + 31 (and p >= j0) share one block: one row lookup
+        const int64_t rb = pg.block_row_uniform(s, j0 / kBlock);
+        const int jb = j0 & ~(kBlock - 1);
         u32x4 kr[kScoreUnroll];
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
             int j = j0 + 4 * u + r;
             j = min(j, p);                                   // rows past p are never written
-            kr[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(j) * kIdxDim + 8 * c));
+            kr[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(dsa_k + (rb + (j - jb)) * kIdxDim + 8 * c));
         }
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
@@ -327,7 +332,7 @@ size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos) {
     return static_cast<size_t>(n_q) * score_stride(max_pos) * sizeof(float);
 }
 
-hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t* q_idx,
+hipError_t launch_dsa_select(const uint16_t* dsa_k, const Pager& pg, const uint16_t* q_idx,
                              const int32_t* stream, const int32_t* pos, int64_t n_q,
                              int32_t max_pos, int top_k, int32_t* sel, int32_t* n_sel, void* ws,
                              hipStream_t s) {
@@ -335,7 +340,7 @@ hipError_t launch_dsa_select(const uint16_t* dsa_k, int64_t cap, const uint16_t*
     const int64_t stride = score_stride(max_pos);
     const unsigned nx = static_cast<unsigned>((max_pos + kScoreKeysPerWg) / kScoreKeysPerWg);
     hipLaunchKernelGGL(dsa_score_kernel, dim3(nx, static_cast<unsigned>(n_q)), dim3(256), 0, s, dsa_k,
-                       cap, q_idx, stream, pos, scores, stride);
+                       pg, q_idx, stream, pos, scores, stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(dsa_topk_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kSelThreads), 0, s, scores,

@@ -32,6 +32,10 @@ msa_status check_cache(const msa_cache* c) {
     if (!c) return MSA_ERR_NULL_ARG;
     if (c->cap < 1 || c->n_stream < 1) return MSA_ERR_BAD_SHAPE;
     if (c->cap > (int64_t(1) << 31) - 1) return MSA_ERR_UNSUPPORTED;   // positions are int32
+    if (c->d_block_table) {
+        if (reinterpret_cast<uintptr_t>(c->d_block_table) % 4) return MSA_ERR_MISALIGNED;
+        if (c->table_stride < 1 || int64_t(c->table_stride) * kBlock < c->cap) return MSA_ERR_BAD_SHAPE;
+    }
     return MSA_OK;
 }
 
@@ -73,7 +77,8 @@ size_t select_prefill_ws(int64_t n_q, int32_t max_pos) {
 }
 
 msa::CacheView view(const msa_cache* c) {
-    return msa::CacheView{c->idx_k, c->dsa_k, c->k, c->v, c->cap, c->idx_k_f16};
+    return msa::CacheView{c->idx_k, c->dsa_k, c->k, c->v, c->cap, c->idx_k_f16,
+                          msa::Pager{c->d_block_table, c->table_stride, c->cap}};
 }
 
 // The MSA index keys: exactly one of the f32 and fp16 caches.
@@ -98,7 +103,7 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
     if (d_key_new) MSA_TRY(check_ptrs({d_key_new, cache->dsa_k}));
     if (d_k_new) MSA_TRY(check_ptrs({d_k_new, cache->k}));
     if (d_v_new) MSA_TRY(check_ptrs({d_v_new, cache->v}));
-    return hip_status(msa::launch_append(cache->idx_k, cache->idx_k_f16, cache->dsa_k, cache->k, cache->v, cache->cap,
+    return hip_status(msa::launch_append(cache->idx_k, cache->idx_k_f16, cache->dsa_k, cache->k, cache->v, view(cache).pg,
                                          d_stream, d_pos, n_new, d_idx_k_new, d_key_new, d_k_new,
                                          d_v_new, static_cast<hipStream_t>(hip_stream)));
 }
@@ -274,7 +279,7 @@ msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
         MSA_TRY(check_ptrs({d_ws}));
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
     }
-    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, n_q, d_sel,
+    msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q, d_stream, d_pos, n_q, d_sel,
                       dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
@@ -291,7 +296,7 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
     if (nblk_of(static_cast<int32_t>(pos0 + n_q - 1)) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out, d_ws}));
     if (ws_bytes < msa::prefill_attend_ws_bytes(n_q, dims->top_k)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(msa::launch_prefill_attend(cache->k, cache->v, cache->cap, d_q, stream, pos0, n_q, d_sel,
+    return hip_status(msa::launch_prefill_attend(cache->k, cache->v, view(cache).pg, d_q, stream, pos0, n_q, d_sel,
                                                  dims->top_k, dims->scale, d_out, d_ws,
                                                  static_cast<hipStream_t>(hip_stream)));
 }
@@ -308,7 +313,7 @@ msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16
     if (n_q > 65535) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({d_ws}));
     if (ws_bytes < msa::dsa_select_ws_bytes(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(msa::launch_dsa_select(cache->dsa_k, cache->cap, d_q_idx, d_stream, d_pos, n_q,
+    return hip_status(msa::launch_dsa_select(cache->dsa_k, view(cache).pg, d_q_idx, d_stream, d_pos, n_q,
                                              max_pos, dims->top_k, d_sel, d_n_sel, d_ws,
                                              static_cast<hipStream_t>(hip_stream)));
 }
@@ -327,7 +332,7 @@ msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
         MSA_TRY(check_ptrs({d_ws}));
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
     }
-    msa::AttendArgs a{cache->k, cache->v, cache->cap, d_q, d_stream, d_pos, n_q, d_sel,
+    msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q, d_stream, d_pos, n_q, d_sel,
                       dims->top_k, 0, 1, dims->scale, d_out, d_ws};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
 }

@@ -75,8 +75,10 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Step lists.  Workgroup (tile, g): entry = {block id, mask of tile queries},
-// ascending block order, at most kPb mask bits per entry.
+// Step lists.  Workgroup (tile, g): entry = {block id, mask of tile queries,
+// first cache row of the block (low, high word)}, ascending block order, at
+// most kPb mask bits per entry.  The row is resolved here, through the block
+// table of a paged cache, so that the sweep does no table lookups.
 // ---------------------------------------------------------------------------
 struct StepArgs {
     const int32_t* sel;
@@ -85,8 +87,10 @@ struct StepArgs {
     int64_t n_q;
     int nblk;
     int max_steps;
+    Pager pg;
+    int32_t stream;
     int32_t* counts;
-    u32x2* steps;
+    u32x4* steps;
 };
 
 __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a) {
@@ -124,9 +128,10 @@ __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a
     int before = 0;
     for (int w = 0; w < wave; ++w) before += wave_sums[w];
     int pos = before + incl - cnt;
-    u32x2* out = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
+    u32x4* out = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
     for (int b = b0; b < b1; ++b) {
         uint32_t m = qmask[b];
+        const uint64_t row = m != 0u ? static_cast<uint64_t>(a.pg.block_row(a.stream, b)) : 0u;
         while (m != 0u) {
             uint32_t sub = 0u;
             for (int i = 0; i < kPb && m != 0u; ++i) {
@@ -134,7 +139,8 @@ __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a
                 sub |= low;
                 m ^= low;
             }
-            out[pos++] = u32x2{static_cast<uint32_t>(b), sub};
+            out[pos++] = u32x4{static_cast<uint32_t>(b), sub, static_cast<uint32_t>(row),
+                               static_cast<uint32_t>(row >> 32)};
         }
     }
     if (threadIdx.x == kStepsThreads - 1) a.counts[blockIdx.x] = before + incl;
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a
 struct PaArgs {
     const uint16_t* k;
     const uint16_t* v;
-    int64_t cap;
+    Pager pg;
     const uint16_t* q;
     int32_t stream;
     int32_t pos0;
@@ -154,7 +160,7 @@ struct PaArgs {
     int64_t last_row;
     int max_steps;
     const int32_t* counts;
-    const u32x2* steps;
+    const u32x4* steps;
     float scale;
     float* out;
 };
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     const int l16 = lane & 15;
     const int l4 = lane >> 4;
     const int n_steps = a.counts[blockIdx.x];
-    const u32x2* steps = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
+    const u32x4* steps = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
 
     // Separate objects, so that reads of one are not made to wait for copies
     // in flight into another.
@@ -185,7 +191,6 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     __shared__ int redo_flag;
 
     const float qk_scale = a.scale * kLog2eP;
-    const int64_t s_base = static_cast<int64_t>(a.stream) * a.cap * kGroups;
     const int64_t q_base = (q_first * kGroups + g) * kHeadsPerGroup * kHeadDim;   // query q_first's 16 heads
     constexpr int64_t kQStride = int64_t(kGroups) * kHeadsPerGroup * kHeadDim;     // next query
 
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         float r = 0.f;
         if (t < n_tq) {
             const uint16_t* qr = a.q + q_base + t * kQStride + h * kHeadDim;
-            const uint16_t* kr = a.k + (s_base + static_cast<int64_t>(a.pos0 + q_first + t) * kGroups + g) * kHeadDim;
+            const uint16_t* kr = a.k + (a.pg.row(a.stream, a.pos0 + static_cast<int>(q_first) + t) * kGroups + g) * kHeadDim;
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll 4
             for (int d = 0; d < kHeadDim; d += 8) {
@@ -255,9 +260,11 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         const int row = slot >> 4;
         soff[j] = static_cast<uint32_t>(row * kGroups * kHeadDim + 8 * ((slot & 15) ^ rowperm(row)));
     }
-    auto stage_row_j = [&](const uint16_t* cache, int b, char* dst, int j) {
-        const int row0 = b * kBlock;
-        const uint16_t* src = cache + (s_base + static_cast<int64_t>(row0) * kGroups + g) * kHeadDim;
+    // e: the block's step entry (block id, mask, first cache row)
+    auto stage_row_j = [&](const uint16_t* cache, const u32x4& e, char* dst, int j) {
+        const int row0 = static_cast<int>(e[0]) * kBlock;
+        const int64_t rb = static_cast<int64_t>((static_cast<uint64_t>(e[3]) << 32) | e[2]);
+        const uint16_t* src = cache + (rb * kGroups + g) * kHeadDim;
         uint32_t o = soff[j];
         if (row0 + kBlock - 1 > last_row) {                   // wave-uniform: the chunk's last block
             // rows past the chunk's last key are read from that key's row:
@@ -322,13 +329,12 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     // One step: block b, tile queries `mask` (at most kPb), V in vcur; the
     // next step's V goes to vnext.
     auto step = [&](int i, const char* vcur, char* vnext) {
-        const u32x2 e = steps[i];
+        const u32x4 e = steps[i];
         const int b = static_cast<int>(e[0]);
         const uint32_t mask = e[1];
         const int np = __builtin_popcount(mask);
         const bool more = i + 1 < n_steps;
-        const u32x2 en = steps[more ? i + 1 : i];
-        const int bn = static_cast<int>(en[0]);
+        const u32x4 en = steps[more ? i + 1 : i];
         const int qpos0 = a.pos0 + static_cast<int>(q_first);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                        // B0: this step's K, Q, V are in LDS
@@ -339,8 +345,8 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
 #pragma unroll
         for (int ks4 = 0; ks4 < 4; ++ks4) kop[ks4] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks4]);
         if (more) {
-            stage_row_j(a.v, bn, vnext, 0);
-            stage_row_j(a.v, bn, vnext, 1);
+            stage_row_j(a.v, en, vnext, 0);
+            stage_row_j(a.v, en, vnext, 1);
         }
         float xmax = -INFINITY;
         {
@@ -367,8 +373,8 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
             }
         }
         if (more) {
-            stage_row_j(a.v, bn, vnext, 2);
-            stage_row_j(a.v, bn, vnext, 3);
+            stage_row_j(a.v, en, vnext, 2);
+            stage_row_j(a.v, en, vnext, 3);
         }
         if (__builtin_amdgcn_ballot_w64(xmax > kOverflow) != 0 && lane == 0) redo_flag = 1;
         lds_barrier();                                          // B1: P is in LDS; K, Q free
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         }
         if (more) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) stage_row_j(a.k, bn, kbuf, j);
+            for (int j = 0; j < 4; ++j) stage_row_j(a.k, en, kbuf, j);
             uint32_t mn = en[1];
             for (int p = 0; mn != 0u; ++p) {
                 stage_q(p, __builtin_ctz(mn));
@@ -473,12 +479,11 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     };
 
     if (n_steps > 0) {
-        const u32x2 e0 = steps[0];
-        const int b0 = static_cast<int>(e0[0]);
+        const u32x4 e0 = steps[0];
         uint32_t m = e0[1];
         for (int j = 0; j < 4; ++j) {
-            stage_row_j(a.k, b0, kbuf, j);
-            stage_row_j(a.v, b0, vbuf0, j);
+            stage_row_j(a.k, e0, kbuf, j);
+            stage_row_j(a.v, e0, vbuf0, j);
         }
         for (int p = 0; m != 0u; ++p) {
             stage_q(p, __builtin_ctz(m));
@@ -514,16 +519,16 @@ int64_t n_tiles_of(int64_t n_q) { return (n_q + kTq - 1) / kTq; }
 size_t prefill_attend_ws_bytes(int64_t n_q, int top_k) {
     const int64_t n_wg = n_tiles_of(n_q) * kGroups;
     const size_t counts = (static_cast<size_t>(n_wg) * sizeof(int32_t) + 255) & ~size_t(255);
-    return counts + static_cast<size_t>(n_wg) * kTq * top_k * sizeof(u32x2);
+    return counts + static_cast<size_t>(n_wg) * kTq * top_k * sizeof(u32x4);
 }
 
-hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t cap, const uint16_t* q,
+hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pager& pg, const uint16_t* q,
                                  int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
                                  float scale, float* out, void* ws, hipStream_t s) {
     const int64_t n_wg = n_tiles_of(n_q) * kGroups;
     const size_t counts_bytes = (static_cast<size_t>(n_wg) * sizeof(int32_t) + 255) & ~size_t(255);
     int32_t* counts = static_cast<int32_t*>(ws);
-    u32x2* steps = reinterpret_cast<u32x2*>(static_cast<char*>(ws) + counts_bytes);
+    u32x4* steps = reinterpret_cast<u32x4*>(static_cast<char*>(ws) + counts_bytes);
     const int nblk = (pos0 + static_cast<int>(n_q) - 1) / kBlock + 1;
 
     StepArgs sa;
@@ -533,6 +538,8 @@ hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t c
     sa.n_q = n_q;
     sa.nblk = nblk;
     sa.max_steps = kTq * top_k;
+    sa.pg = pg;
+    sa.stream = stream;
     sa.counts = counts;
     sa.steps = steps;
     hipLaunchKernelGGL(prefill_steps_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(kStepsThreads),
@@ -543,7 +550,7 @@ hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, int64_t c
     PaArgs a;
     a.k = k;
     a.v = v;
-    a.cap = cap;
+    a.pg = pg;
     a.q = q;
     a.stream = stream;
     a.pos0 = pos0;

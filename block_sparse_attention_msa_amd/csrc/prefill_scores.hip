@@ -71,17 +71,16 @@ __device__ __forceinline__ void sc_lds_barrier() {
 // from the f32 index cache or (idx_k16 non-NULL) the fp16 one, whose values
 // widen to f32 exactly.
 __global__ __launch_bounds__(256) void split_keys_kernel(const float* __restrict__ idx_k,
-                                                         const uint16_t* __restrict__ idx_k16, int64_t cap,
+                                                         const uint16_t* __restrict__ idx_k16, Pager pg,
                                                          int32_t stream, int64_t n_keys,
                                                          uint16_t* __restrict__ khl) {
     const int64_t n8 = n_keys * kGroups * (kIdxDim / 8);   // 8-key pieces
-    const int64_t row0 = static_cast<int64_t>(stream) * cap * kGroups * kIdxDim;
     for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < n8;
          e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
         const int64_t key = e / (kGroups * (kIdxDim / 8));
         const int g = static_cast<int>((e / (kIdxDim / 8)) % kGroups);
         const int d8 = static_cast<int>(e % (kIdxDim / 8));
-        const int64_t off = row0 + (key * kGroups + g) * kIdxDim + 8 * d8;
+        const int64_t off = (pg.row(stream, static_cast<int>(key)) * kGroups + g) * kIdxDim + 8 * d8;
         f32x4 x0, x1;
         if (idx_k16) {
             typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -310,7 +309,7 @@ hipError_t launch_block_scores_prefill(const CacheView& c, const float* idx_q, i
     const int64_t n8 = n_keys * kGroups * (kIdxDim / 8);
     const int64_t want = (n8 + 255) / 256;
     const unsigned split_grid = static_cast<unsigned>(want < 8192 ? want : 8192);
-    hipLaunchKernelGGL(split_keys_kernel, dim3(split_grid), dim3(256), 0, s, c.idx_k, c.idx_k16, c.cap, stream,
+    hipLaunchKernelGGL(split_keys_kernel, dim3(split_grid), dim3(256), 0, s, c.idx_k, c.idx_k16, c.pg, stream,
                        n_keys, khl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

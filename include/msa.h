@@ -109,6 +109,21 @@ typedef struct msa_cache {
      * index operations use whichever of idx_k / idx_k_f16 is set; setting
      * both is MSA_ERR_UNSUPPORTED.  Halves the bytes the decode scan reads. */
     uint16_t* idx_k_f16;
+    /* Paged caches ([MSA-PR] review thread on per-stream caches: slot-anchored
+     * per-stream caches versus a unified cache addressed through a block
+     * index).  NULL: stream s owns rows s*cap .. s*cap+cap-1 of every cache
+     * (slot == position).  Otherwise a DEVICE array [n_stream][table_stride]
+     * of int32: logical block b (positions 128b .. 128b+127) of stream s lives
+     * in page d_block_table[s*table_stride + b], i.e. cache rows
+     * page*128 .. page*128+127 of idx_k / idx_k_f16 / dsa_k / k / v, which are
+     * then pools of pages.  cap stays the logical capacity per stream and
+     * needs table_stride*128 >= cap (MSA_ERR_BAD_SHAPE otherwise, and for
+     * table_stride < 1); the table must be 4-byte aligned (MSA_ERR_MISALIGNED).
+     * Device precondition (not checked): every
+     * entry a call reaches (blocks 0 .. max_pos/128 of the streams it touches)
+     * is a page inside all the pools the call reads or writes. */
+    const int32_t* d_block_table;
+    int32_t table_stride;
 } msa_cache;
 
 /* Operations whose workspace size can be queried. */

@@ -157,6 +157,27 @@ def test_fp16_index_cache_validation(L):
     assert app(f16_mis) == ALIGN
 
 
+def test_block_table_validation(L):
+    d = M.msa_dims()
+    ok = M.Cache(A, None, A, A, 4096, 2, None, B, 32)        # 32 pages of 128 cover cap 4096
+    odd = ctypes.c_void_p(0x20002)                           # table entries are int32: 4-byte alignment
+    mis = M.Cache(A, None, A, A, 4096, 2, None, odd, 32)
+    short = M.Cache(A, None, A, A, 4097, 2, None, B, 32)     # cap beyond stride * 128
+    zero = M.Cache(A, None, A, A, 4096, 2, None, B, 0)
+    sel = lambda c: L.msa_select(ctypes.byref(d), ctypes.byref(c), A, A, A, 1, 100, A, A, A, 1 << 30, None)
+    assert sel(ok) not in (NULL, ALIGN, SHAPE, UNSUP)       # accepted (fails later only for want of a GPU)
+    assert sel(mis) == ALIGN
+    assert sel(short) == SHAPE
+    assert sel(zero) == SHAPE
+    app = lambda c: L.msa_index_append(ctypes.byref(d), ctypes.byref(c), A, A, 1, 5, A, None, None, None)
+    assert app(mis) == ALIGN and app(short) == SHAPE
+    att = lambda c: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 0, 10, A, A, A, 1 << 30, None)
+    assert att(mis) == ALIGN and att(zero) == SHAPE
+    dd = M.dsa_dims()
+    dsa_mis = M.Cache(None, A, A, A, 4096, 2, None, odd, 32)
+    assert L.dsa_select(ctypes.byref(dd), ctypes.byref(dsa_mis), A, A, A, 1, 100, A, A, A, 1 << 30, None) == ALIGN
+
+
 def test_topk_block_limit(L):
     d = M.msa_dims()
     # 4096 blocks of 128 is the most a top-k wave ranks
@@ -179,10 +200,10 @@ def test_workspace_sizes(L):
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
     # prefill attention: per (32-query tile, group) a step count (256-byte
-    # aligned array) and up to 32 * top_k 8-byte step entries
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 2048 + 512 * 32 * 16 * 8
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 1, 100) == 256 + 4 * 32 * 16 * 8
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 33, 100) == 256 + 8 * 32 * 16 * 8
+    # aligned array) and up to 32 * top_k 16-byte step entries
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 2048 + 512 * 32 * 16 * 16
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 1, 100) == 256 + 4 * 32 * 16 * 16
+    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 33, 100) == 256 + 8 * 32 * 16 * 16
     dd = M.dsa_dims()
     assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
     with pytest.raises(M.MsaError):
