@@ -75,6 +75,8 @@ def _declare(L):
     L.oracle_dsa_rotate.restype = _I
     L.oracle_dsa_select.argtypes = [_I, _I, _I64, _P, _I64, _P, _P, _P, _P, _P, _P]
     L.oracle_dsa_select.restype = _I
+    L.oracle_dsa_select_heads.argtypes = [_I, _I, _I, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P]
+    L.oracle_dsa_select_heads.restype = _I
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -213,4 +215,31 @@ def dsa_select(k_rot, stream, pos, q_idx, *, top_k=2048, want_scores=False):
                                  _ptr(n_sel))
     if rc != 0:
         raise ValueError(f"oracle_dsa_select failed: {rc}")
+    return sel, n_sel, scores
+
+
+def dsa_select_heads(k_rot, stream, pos, q_idx_h, head_w, *, top_k=2048, want_scores=False):
+    """Multi-head lightning indexer: score(i, j) = sum_h w[i][h] *
+    max(0, q[i][h] . k[j]) (the reduction is a reading: the DSA pull request's
+    review thread gives per-head scores, an element-wise product and a head
+    reduction, not the formula), then the same top-k as dsa_select.
+
+    k_rot: [S][cap][Di] fp16 bits; q_idx_h: [n_q][H][Di] fp16 bits;
+    head_w: [n_q][H] f32.  Returns (sel, n_sel, scores or None)."""
+    k_rot = _c(k_rot, np.uint16)
+    q_idx_h = _c(q_idx_h, np.uint16)
+    head_w = _c(head_w, np.float32)
+    stream = _idx(stream)
+    pos = _idx(pos)
+    _, cap, Di = k_rot.shape
+    n_q, H = head_w.shape
+    if q_idx_h.shape != (n_q, H, Di):
+        raise ValueError("q_idx_h must be [n_q][H][Di]")
+    scores = np.empty((n_q, cap), np.float64) if want_scores else None
+    sel = np.empty((n_q, top_k), np.int32)
+    n_sel = np.empty(n_q, np.int32)
+    rc = lib().oracle_dsa_select_heads(Di, H, top_k, cap, _ptr(k_rot), n_q, _ptr(stream), _ptr(pos),
+                                       _ptr(q_idx_h), _ptr(head_w), _ptr(scores), _ptr(sel), _ptr(n_sel))
+    if rc != 0:
+        raise ValueError(f"oracle_dsa_select_heads failed: {rc}")
     return sel, n_sel, scores

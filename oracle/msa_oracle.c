@@ -388,3 +388,50 @@ ORACLE_API int oracle_dsa_select(int idx_dim, int top_k, int64_t cap,
     }
     return 0;
 }
+
+/*
+ * DSA token selection with a multi-head indexer ([DSA-PR] review thread: the
+ * indexer forms one K*Q score per indexer head, n_ihead = 32 for GLM, takes
+ * an element-wise product with a second matrix and reduces over the heads
+ * to one score per (query, key) before the top-k).  The pages do not print
+ * the reduction; it is read as the published lightning-indexer form the
+ * pull request is named after:
+ *     score(i, j) = sum_h w[i][h] * max(0, q[i][h] . k[j])
+ * with per-query head weights w (any scale folded in by the caller).
+ *   k_rot  : [n_stream][cap][idx_dim] fp16 rotated indexer keys
+ *   q_idx  : [n_q][n_head][idx_dim] fp16 (not rotated)
+ *   head_w : [n_q][n_head] f32
+ *   score_out, sel, n_sel : as oracle_dsa_select
+ */
+ORACLE_API int oracle_dsa_select_heads(int idx_dim, int n_head, int top_k, int64_t cap,
+                                       const uint16_t* k_rot, int64_t n_q,
+                                       const int32_t* stream, const int32_t* pos,
+                                       const uint16_t* q_idx, const float* head_w,
+                                       double* score_out, int32_t* sel, int32_t* n_sel) {
+    if (n_head < 1) return -1;
+    for (int64_t i = 0; i < n_q; ++i)
+        if (pos[i] < 0 || pos[i] >= cap) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n_q; ++i) {
+        int64_t p = pos[i];
+        const uint16_t* ks = k_rot + (int64_t)stream[i] * cap * idx_dim;
+        double* t = (double*)malloc((size_t)(p + 1) * sizeof *t);
+        for (int64_t j = 0; j <= p; ++j) {
+            double total = 0.0;
+            for (int h = 0; h < n_head; ++h) {
+                const uint16_t* qv = q_idx + (i * n_head + h) * idx_dim;
+                double s = 0.0;
+                for (int d = 0; d < idx_dim; ++d)
+                    s += oracle_f16_to_f64(qv[d]) * oracle_f16_to_f64(ks[j * idx_dim + d]);
+                double relu = s > 0.0 ? s : 0.0;
+                total += (double)head_w[i * n_head + h] * relu;
+            }
+            t[j] = total;
+        }
+        if (score_out)
+            for (int64_t j = 0; j < cap; ++j) score_out[i * cap + j] = j <= p ? t[j] : -INFINITY;
+        n_sel[i] = select_ranked(t, p + 1, -1, top_k, sel + i * (int64_t)top_k);
+        free(t);
+    }
+    return 0;
+}

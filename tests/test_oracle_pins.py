@@ -391,6 +391,98 @@ def test_dsa_short_context_is_dense_attention():
     np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-12)
 
 
+def _f16(a):
+    return np.asarray(a, np.float16).view(np.uint16)
+
+
+def test_dsa_heads_hand_worked_example():
+    """Two heads, 2-dim keys, worked by hand:
+    q0 = (2, 1), q1 = (-1, 3), w = (1, 0.5);
+    k0 = (1, 0): max(0, 2) + 0.5 max(0, -1) = 2
+    k1 = (0, 1): 1 + 0.5 * 3 = 2.5
+    k2 = (1, 1): 3 + 0.5 * 2 = 4
+    k3 = (-1, 2): max(0, -1) + 0.5 * 7 = 3.5"""
+    k = _f16([[[1, 0], [0, 1], [1, 1], [-1, 2]]])
+    q = _f16([[[2, 1], [-1, 3]]])
+    w = np.array([[1.0, 0.5]], np.float32)
+    sel, n_sel, sc = oracle.dsa_select_heads(k, [0], [3], q, w, top_k=2, want_scores=True)
+    assert np.array_equal(sc[0], [2.0, 2.5, 4.0, 3.5])
+    assert n_sel[0] == 2 and np.array_equal(sel[0], [2, 3])
+    sel, n_sel, _ = oracle.dsa_select_heads(k, [0], [1], q, w, top_k=2)   # causal: keys 0, 1 only
+    assert n_sel[0] == 2 and np.array_equal(sel[0], [0, 1])
+
+
+def test_dsa_heads_brute_force_exact():
+    """Small integers and dyadic weights: every sum is exact, so the oracle
+    must equal a rational-arithmetic evaluation of the formula."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    H, D, cap, n_q = 3, 8, 12, 4
+    k = rng.integers(-3, 4, size=(2, cap, D))
+    q = rng.integers(-3, 4, size=(n_q, H, D))
+    w = rng.integers(-4, 5, size=(n_q, H)) / 4.0
+    stream = np.array([0, 1, 1, 0], np.int32)
+    pos = np.array([11, 5, 0, 7], np.int32)
+    sel, n_sel, sc = oracle.dsa_select_heads(_f16(k), stream, pos, _f16(q), w.astype(np.float32), top_k=5,
+                                             want_scores=True)
+    for i in range(n_q):
+        want = []
+        for j in range(pos[i] + 1):
+            tot = Fraction(0)
+            for h in range(H):
+                dot = sum(int(q[i, h, d]) * int(k[stream[i], j, d]) for d in range(D))
+                tot += Fraction(w[i, h]) * max(0, dot)
+            want.append(tot)
+        assert [Fraction(x) for x in sc[i, :pos[i] + 1]] == want
+        assert np.all(np.isneginf(sc[i, pos[i] + 1:]))
+        order = sorted(range(pos[i] + 1), key=lambda j: (-want[j], j))
+        kk = min(5, pos[i] + 1)
+        assert n_sel[i] == kk and list(sel[i, :kk]) == sorted(order[:kk])
+        assert np.all(sel[i, kk:] == -1)
+
+
+def test_dsa_heads_single_positive_head_is_single_head_select():
+    """One head of weight 1 whose dot products are all positive is the
+    single-head indexer."""
+    rng = np.random.default_rng(12)
+    k = _f16(rng.uniform(0.1, 1.0, size=(2, 400, 128)))
+    q = _f16(rng.uniform(0.1, 1.0, size=(3, 128)))
+    stream, pos = np.array([0, 1, 1], np.int32), np.array([399, 200, 37], np.int32)
+    s1, n1, sc1 = oracle.dsa_select(k, stream, pos, q, top_k=64, want_scores=True)
+    s2, n2, sc2 = oracle.dsa_select_heads(k, stream, pos, q[:, None, :], np.ones((3, 1), np.float32),
+                                          top_k=64, want_scores=True)
+    assert np.array_equal(sc1, sc2) and np.array_equal(s1, s2) and np.array_equal(n1, n2)
+
+
+def test_dsa_heads_relu_sign_and_linearity():
+    rng = np.random.default_rng(13)
+    H, D, cap = 4, 16, 64
+    k = rng.integers(-2, 3, size=(1, cap, D))
+    q = rng.integers(-2, 3, size=(2, H, D))
+    w = (rng.integers(-4, 5, size=(2, H)) / 8.0).astype(np.float32)
+    pos = np.array([63, 40], np.int32)
+    st = np.zeros(2, np.int32)
+    score = lambda qq, ww: oracle.dsa_select_heads(_f16(k), st, pos, _f16(qq), ww, top_k=8, want_scores=True)[2]
+    base = score(q, w)
+    # a head with no positive dot product adds nothing, whatever its weight
+    kpos = np.abs(k)
+    kpos[..., 0] += 1                                   # every key has a positive first entry
+    qneg = np.concatenate([q, -np.ones((2, 1, D), np.int64)], axis=1)
+    for wx in (-3.0, 0.0, 5.0):
+        w5 = np.concatenate([w, np.full((2, 1), wx, np.float32)], axis=1)
+        a = oracle.dsa_select_heads(_f16(kpos), st, pos, _f16(qneg), w5, top_k=8, want_scores=True)[2]
+        b = oracle.dsa_select_heads(_f16(kpos), st, pos, _f16(q), w, top_k=8, want_scores=True)[2]
+        assert np.array_equal(a, b)
+    # the ReLU acts per head before the weights: negating a query head is not
+    # negating its contribution
+    fin = np.isfinite(base)
+    assert not np.array_equal(score(-q, w)[fin], -base[fin])
+    # linear in the weights, and odd in them
+    w2 = (rng.integers(-4, 5, size=(2, H)) / 8.0).astype(np.float32)
+    assert np.array_equal(score(q, w + w2)[fin], base[fin] + score(q, w2)[fin])
+    assert np.array_equal(score(q, -w)[fin], -base[fin])
+
+
 def _read_golden_1x4k():
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "decode_1x4k_int.txt")

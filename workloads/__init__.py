@@ -23,6 +23,10 @@ Recipe (stated once, used everywhere):
     store them as f32 (all partial sums are exact in f32).
   * The prefill workload multiplies the f32 indexer vectors by
     float32(1/sqrt(128)) after drawing.
+  * Multi-head DSA indexer (n_ihead = 32 heads, the GLM geometry the DSA pull
+    request reports): per query, n_ihead fp16 query rows drawn as above and
+    n_ihead f32 head weights drawn as float32 N(0, 1) times
+    float32(1/sqrt(n_ihead)) (both signs occur).
 There is no dataset: the pages measure on wikitext-2 with real weights, which
 these synthetic tensors of the real geometry stand in for.
 """
@@ -46,6 +50,8 @@ SCALE = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))   # the f32 value both side
 
 # tensor-kind tags of the seed sequence
 _T_IDX_K, _T_K, _T_V, _T_IDX_Q, _T_Q, _T_DSA_K, _T_DSA_Q = 1, 2, 3, 4, 5, 6, 7
+_T_DSA_QH, _T_DSA_W = 8, 9
+DSA_N_IHEAD = 32
 
 
 @dataclasses.dataclass(frozen=True)
@@ -159,6 +165,27 @@ def query_q(wl: Workload, i: int) -> np.ndarray:
 def query_dsa(wl: Workload, i: int) -> np.ndarray:
     """[IDX_DIM] fp16 bits of the DSA indexer query of query i."""
     return to_f16_bits(_normal_f32(_rng(wl.seed, _T_DSA_Q, i), (IDX_DIM,)))
+
+
+def query_dsa_heads(wl: Workload, i: int, n_head: int = DSA_N_IHEAD) -> np.ndarray:
+    """[n_head][IDX_DIM] fp16 bits of the multi-head DSA indexer query of query i."""
+    return to_f16_bits(_normal_f32(_rng(wl.seed, _T_DSA_QH, i), (n_head, IDX_DIM)))
+
+
+def head_weights(wl: Workload, i: int, n_head: int = DSA_N_IHEAD) -> np.ndarray:
+    """[n_head] f32 indexer head weights of query i."""
+    return _normal_f32(_rng(wl.seed, _T_DSA_W, i), (n_head,)) * np.float32(1.0 / math.sqrt(n_head))
+
+
+def queries_dsa_heads(wl: Workload, n_head: int = DSA_N_IHEAD,
+                      idx: Optional[List[int]] = None) -> Dict[str, np.ndarray]:
+    """Stacked multi-head indexer queries: q_idx_h [n_q][n_head][IDX_DIM] fp16
+    bits and head_w [n_q][n_head] f32."""
+    idx = list(range(wl.n_q)) if idx is None else list(idx)
+    if not idx:
+        return {"q_idx_h": np.zeros((0, n_head, IDX_DIM), np.uint16), "head_w": np.zeros((0, n_head), np.float32)}
+    return {"q_idx_h": np.stack([query_dsa_heads(wl, i, n_head) for i in idx]),
+            "head_w": np.stack([head_weights(wl, i, n_head) for i in idx]).astype(np.float32)}
 
 
 def queries(wl: Workload, idx: Optional[List[int]] = None) -> Dict[str, np.ndarray]:
