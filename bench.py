@@ -560,12 +560,50 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20):
     att_bytes = S * 4 * 2048 * 128 * 2 * 2 + S * 2048 * 4
     total = seg.sum()
     log(f"[bench] dsa: append {seg[0] * 1e3:.1f} select {seg[1] * 1e3:.1f} attend {seg[2] * 1e3:.1f} us")
+
+    # The multi-head indexer (32 heads, weights per query): a "full" layer
+    # selects with it; an IndexShare "shared" layer reuses the last full
+    # layer's selection and only appends and attends.
+    n_head = W.DSA_N_IHEAD
+    qh = W.queries_dsa_heads(wl, n_head)
+    q_h = bits(qh["q_idx_h"], torch.float16)
+    w_h = tens(qh["head_w"])
+    ev_h = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+
+    def run_heads(e=None, select=True):
+        if e: e[0].record()
+        M.dsa_index_append(dims, cache, stream, pos, p, new_key, new_k, new_v)
+        if e: e[1].record()
+        if select:
+            M.dsa_select_heads(dims, cache, q_h, w_h, stream, pos, p, sel, n_sel, ws_sel)
+        if e: e[2].record()
+        M.dsa_attend_decode(dims, cache, q, stream, pos, p, sel, out, ws_att)
+        if e: e[3].record()
+
+    for _ in range(3):
+        run_heads()
+    torch.cuda.synchronize()
+    for i in range(iters):
+        run_heads(ev_h[i])
+    torch.cuda.synchronize()
+    seg_h = np.array([[ev_h[i][j].elapsed_time(ev_h[i][j + 1]) for j in range(3)] for i in range(iters)]).mean(0)
+    for i in range(iters):
+        run_heads(ev_h[i], select=False)
+    torch.cuda.synchronize()
+    shared_ms = float(np.mean([ev_h[i][0].elapsed_time(ev_h[i][3]) for i in range(iters)]))
+    full_ms = seg_h.sum()
+    log(f"[bench] dsa {n_head}-head indexer: append {seg_h[0] * 1e3:.1f} select {seg_h[1] * 1e3:.1f} "
+        f"attend {seg_h[2] * 1e3:.1f} us; shared layer (no select) {shared_ms * 1e3:.1f} us")
     return {
         "dsa_queries_s": round(S / (total * 1e-3), 1),
         "dsa_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
                    "attend": round(seg[2] * 1e3, 2)},
         "dsa_select_GBps": round(scan_bytes / (seg[1] * 1e-3) / 1e9, 1),
         "dsa_path_GBps": round((scan_bytes + att_bytes) / (total * 1e-3) / 1e9, 1),
+        "dsa_heads": {"n_head": n_head, "full_layer_queries_s": round(S / (full_ms * 1e-3), 1),
+                      "full_layer_us": round(full_ms * 1e3, 2), "select_us": round(seg_h[1] * 1e3, 2),
+                      "select_GBps": round(scan_bytes / (seg_h[1] * 1e-3) / 1e9, 1),
+                      "shared_layer_us": round(shared_ms * 1e3, 2)},
     }
 
 

@@ -36,7 +36,7 @@ EXPORTS = (
     "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",
     "msa_topk_blocks", "msa_select", "msa_block_scores_prefill", "msa_select_prefill",
     "msa_attend_decode", "msa_attend_prefill", "dsa_index_append", "dsa_select",
-    "dsa_attend_decode",
+    "dsa_select_heads", "dsa_attend_decode",
 )
 
 
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "msa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
             "msa_attend_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
             "dsa_select": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "dsa_select_heads": [D, C, P, P, I32, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
             "dsa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
         }
         for name, args in sig.items():
@@ -264,6 +265,18 @@ def dsa_select(dims, cache, q_idx, stream, pos, max_pos, sel, n_sel, ws, hip_str
                             _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
                             _p(sel, torch.int32), _p(n_sel, torch.int32), wp, wn, _stream(hip_stream)),
            "dsa_select")
+
+
+def dsa_select_heads(dims, cache, q_idx_h, head_w, stream, pos, max_pos, sel, n_sel, ws, hip_stream=None):
+    """q_idx_h [n_q][n_head][128] fp16, head_w [n_q][n_head] f32."""
+    if q_idx_h.dim() != 3 or head_w.shape != q_idx_h.shape[:2]:
+        raise ValueError("q_idx_h must be [n_q][n_head][128] and head_w [n_q][n_head]")
+    wp, wn = _ws(ws)
+    _check(lib().dsa_select_heads(ctypes.byref(dims), ctypes.byref(cache), _p(q_idx_h, torch.float16, "q_idx_h"),
+                                  _p(head_w, torch.float32, "head_w"), q_idx_h.shape[1],
+                                  _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                                  _p(sel, torch.int32), _p(n_sel, torch.int32), wp, wn, _stream(hip_stream)),
+           "dsa_select_heads")
 
 
 def dsa_attend_decode(dims, cache, q, stream, pos, max_pos, sel, out, ws=None, hip_stream=None):

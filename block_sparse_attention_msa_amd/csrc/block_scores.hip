@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
     const int p = q_pos[i];
     const int loc = p / kBlock;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar table reads
     const int g = lane >> 4;     // the DPP row of this lane = its group
     const int c = lane & 15;     // lane's 16-byte column within the group's first/second half
     const int b = b0 + wave / kScanWavesPerBlock;   // this wave's key block
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kerne
     const int p = q_pos[i];
     const int loc = p / kBlock;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar table reads
     const int g = lane >> 4;
     const int c = lane & 15;
     const int b = b0 + wave / kScanWavesPerBlock;

@@ -203,5 +203,11 @@ hipError_t launch_dsa_select(const uint16_t* dsa_k, const Pager& pg, const uint1
                              const int32_t* stream, const int32_t* pos, int64_t n_q,
                              int32_t max_pos, int top_k, int32_t* sel, int32_t* n_sel,
                              void* ws, hipStream_t s);
+// Multi-head indexer form: n_head in {16, 32, 48, 64}, q_idx_h [n_q][n_head][128]
+// fp16, head_w [n_q][n_head] f32; same workspace as launch_dsa_select.
+hipError_t launch_dsa_select_heads(const uint16_t* dsa_k, const Pager& pg, const uint16_t* q_idx_h,
+                                   const float* head_w, int n_head, const int32_t* stream,
+                                   const int32_t* pos, int64_t n_q, int32_t max_pos, int top_k,
+                                   int32_t* sel, int32_t* n_sel, void* ws, hipStream_t s);
 
 }  // namespace msa

@@ -318,6 +318,24 @@ msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16
                                              static_cast<hipStream_t>(hip_stream)));
 }
 
+msa_status dsa_select_heads(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q_idx_h,
+                            const float* d_head_w, int32_t n_head, const int32_t* d_stream,
+                            const int32_t* d_pos, int64_t n_q, int32_t max_pos, int32_t* d_sel,
+                            int32_t* d_n_sel, void* d_ws, size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Dsa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_head < 16 || n_head > 64 || n_head % 16) return MSA_ERR_UNSUPPORTED;
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
+    MSA_TRY(check_ptrs({cache->dsa_k, d_q_idx_h, d_head_w, d_stream, d_pos, d_sel, d_n_sel}));
+    if (n_q > 65535) return MSA_ERR_UNSUPPORTED;
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < msa::dsa_select_ws_bytes(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(msa::launch_dsa_select_heads(cache->dsa_k, view(cache).pg, d_q_idx_h, d_head_w, n_head,
+                                                   d_stream, d_pos, n_q, max_pos, dims->top_k, d_sel, d_n_sel,
+                                                   d_ws, static_cast<hipStream_t>(hip_stream)));
+}
+
 msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
                              const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
                              int32_t max_pos, const int32_t* d_sel, float* d_out, void* d_ws,

@@ -294,6 +294,26 @@ MSA_API msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, cons
                       void* d_ws, size_t ws_bytes, void* hip_stream);
 
 /*
+ * [DSA-PR] review thread (the indexer memory discussion): the GLM indexer has
+ * n_ihead = 32 heads; each forms its own K*Q score, the scores take an
+ * element-wise product with a second matrix and are reduced over the heads
+ * to one score per (query, key) before the top-k.  The pages do not print the
+ * reduction; it is read as the lightning indexer's
+ *     t[j] = sum_h head_w[i][h] * max(0, sum_d q_idx_h[i][h][d] * dsa_k[stream][j][d])
+ * (fp16 products, f32 sums) for j <= pos; the top-k is dsa_select's.
+ *   d_q_idx_h [n_q][n_head][idx_dim] fp16, d_head_w [n_q][n_head] f32 (any
+ *   scale folded in), n_head in {16, 32, 48, 64} (MSA_ERR_UNSUPPORTED
+ *   otherwise).  Workspace: DSA_OP_SELECT.  A layer that shares another
+ *   layer's indexer (IndexShare) passes that layer's d_sel to
+ *   dsa_attend_decode instead of selecting again.
+ */
+MSA_API msa_status dsa_select_heads(const msa_dims* dims, const msa_cache* cache,
+                            const uint16_t* d_q_idx_h, const float* d_head_w, int32_t n_head,
+                            const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                            int32_t max_pos, int32_t* d_sel, int32_t* d_n_sel,
+                            void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
  * [DSA-PR] "What this does": attention over the kept keys only.  As
  * msa_attend_decode, but d_sel [n_q][top_k] holds token ids shared by all
  * groups (dims->block must be 1).  Workspace: DSA_OP_ATTEND_DECODE.

@@ -153,3 +153,23 @@ def check_attention(got: np.ndarray, ref: np.ndarray, mask_qg=None, heads_per_gr
         assert ma <= ATOL_MAX, f"query {i}: max-abs {ma}"
         assert rel <= RTOL_L2, f"query {i}: rel-L2 {rel}"
     return worst_abs, worst_rel
+
+
+def check_token_selection(g_sel, g_nsel, o_sel, o_nsel, scores, pos, top_k):
+    equal = np.zeros(len(pos), bool)
+    for i in range(len(pos)):
+        k = min(top_k, pos[i] + 1)
+        assert g_nsel[i] == o_nsel[i] == k
+        ids = g_sel[i, :k]
+        assert np.all(np.diff(ids) > 0) and ids.min() >= 0 and ids.max() <= pos[i]
+        assert np.all(g_sel[i, k:] == -1)
+        a, b = set(ids.tolist()), set(o_sel[i, :k].tolist())
+        if a == b:
+            equal[i] = True
+            continue
+        t = scores[i, :pos[i] + 1]
+        thr = GAP_REL * np.abs(t).max()
+        boundary = t[o_sel[i, :k]].min()
+        for x in a ^ b:
+            assert abs(t[x] - boundary) < thr, f"query {i}: token {x} outside the near-tie band"
+    return equal

@@ -178,6 +178,21 @@ def test_block_table_validation(L):
     assert L.dsa_select(ctypes.byref(dd), ctypes.byref(dsa_mis), A, A, A, 1, 100, A, A, A, 1 << 30, None) == ALIGN
 
 
+def test_dsa_select_heads_validation(L):
+    dd = M.dsa_dims()
+    c = M.Cache(None, A, A, A, 4096, 2, None, None, 0)
+    call = lambda nh, w=A, q=A: L.dsa_select_heads(ctypes.byref(dd), ctypes.byref(c), q, w, nh, A, A, 1, 100,
+                                                   A, A, A, 1 << 30, None)
+    for nh in (0, 8, 20, 80, -16):
+        assert call(nh) == UNSUP
+    assert call(32, w=None) == NULL
+    assert call(32, w=MIS) == ALIGN
+    assert call(32) not in (NULL, ALIGN, SHAPE, UNSUP)     # accepted (fails later only for want of a GPU)
+    md = M.msa_dims()
+    assert L.dsa_select_heads(ctypes.byref(md), ctypes.byref(c), A, A, 32, A, A, 1, 100, A, A, A, 1 << 30,
+                              None) == UNSUP                # MSA geometry
+
+
 def test_topk_block_limit(L):
     d = M.msa_dims()
     # 4096 blocks of 128 is the most a top-k wave ranks

@@ -9,29 +9,9 @@ import torch
 import block_sparse_attention_msa_amd as M
 import oracle
 import workloads as W
-from _gpu_common import DEV, GAP_REL, GpuWorkload, check_attention, dev, dev_bits, host_bits, log
+from _gpu_common import DEV, GpuWorkload, check_attention, check_token_selection, dev, dev_bits, host_bits, log
 
 pytestmark = pytest.mark.gpu
-
-
-def _check_token_selection(g_sel, g_nsel, o_sel, o_nsel, scores, pos, top_k):
-    equal = np.zeros(len(pos), bool)
-    for i in range(len(pos)):
-        k = min(top_k, pos[i] + 1)
-        assert g_nsel[i] == o_nsel[i] == k
-        ids = g_sel[i, :k]
-        assert np.all(np.diff(ids) > 0) and ids.min() >= 0 and ids.max() <= pos[i]
-        assert np.all(g_sel[i, k:] == -1)
-        a, b = set(ids.tolist()), set(o_sel[i, :k].tolist())
-        if a == b:
-            equal[i] = True
-            continue
-        t = scores[i, :pos[i] + 1]
-        thr = GAP_REL * np.abs(t).max()
-        boundary = t[o_sel[i, :k]].min()
-        for x in a ^ b:
-            assert abs(t[x] - boundary) < thr, f"query {i}: token {x} outside the near-tie band"
-    return equal
 
 
 def _dsa_parity(wl: W.Workload, host=None):
@@ -53,7 +33,7 @@ def _dsa_parity(wl: W.Workload, host=None):
     torch.cuda.synchronize()
     o_sel, o_nsel, scores = oracle.dsa_select(o_rot, gw.qs["stream"], gw.qs["pos"], gw.qs["q_idx"],
                                               top_k=wl.top_k, want_scores=True)
-    equal = _check_token_selection(sel.cpu().numpy(), n_sel.cpu().numpy(), o_sel, o_nsel, scores,
+    equal = check_token_selection(sel.cpu().numpy(), n_sel.cpu().numpy(), o_sel, o_nsel, scores,
                                    gw.qs["pos"], wl.top_k)
     log(f"  selection: {equal.sum()} of {len(equal)} queries identical")
     o_out = oracle.sparse_attend(gw.host["k"], gw.host["v"], gw.qs["stream"], gw.qs["pos"], gw.qs["q"],

@@ -168,6 +168,8 @@ def test_paged_dsa():
     n_q = wl.n_q
     q_idx, stream, pos = dev_bits(qs["q_idx"], torch.float16), dev(qs["stream"]), dev(qs["pos"])
     q = dev_bits(qs["q"], torch.bfloat16)
+    qh = W.queries_dsa_heads(wl, 32)
+    q_h, w_h = dev_bits(qh["q_idx_h"], torch.float16), dev(qh["head_w"])
     res = []
     for c in (c_flat, c_paged):
         sel = torch.empty((n_q, wl.top_k), dtype=torch.int32, device=DEV)
@@ -176,7 +178,11 @@ def test_paged_dsa():
         M.dsa_select(dims, c, q_idx, stream, pos, wl.max_pos, sel, n_sel, _ws(dims, M.DSA_OP_SELECT, n_q, wl.max_pos))
         M.dsa_attend_decode(dims, c, q, stream, pos, wl.max_pos, sel, out,
                             _ws(dims, M.DSA_OP_ATTEND_DECODE, n_q, wl.max_pos))
-        res.append((sel, n_sel, out))
+        sel_h = torch.empty((n_q, wl.top_k), dtype=torch.int32, device=DEV)
+        n_sel_h = torch.empty(n_q, dtype=torch.int32, device=DEV)
+        M.dsa_select_heads(dims, c, q_h, w_h, stream, pos, wl.max_pos, sel_h, n_sel_h,
+                           _ws(dims, M.DSA_OP_SELECT, n_q, wl.max_pos))
+        res.append((sel, n_sel, out, sel_h, n_sel_h))
     torch.cuda.synchronize()
     for a, b in zip(*res):
         assert torch.equal(a, b), "paged DSA differs from per-stream"
