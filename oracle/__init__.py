@@ -77,6 +77,8 @@ def _declare(L):
     L.oracle_dsa_select.restype = _I
     L.oracle_dsa_select_heads.argtypes = [_I, _I, _I, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P]
     L.oracle_dsa_select_heads.restype = _I
+    L.oracle_index_project.argtypes = [_I64, _I, _I, _I, _P, _P, _P, _P, _P, _D, _D, _I, _P, _P, _P]
+    L.oracle_index_project.restype = _I
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -243,3 +245,30 @@ def dsa_select_heads(k_rot, stream, pos, q_idx_h, head_w, *, top_k=2048, want_sc
     if rc != 0:
         raise ValueError(f"oracle_dsa_select_heads failed: {rc}")
     return sel, n_sel, scores
+
+
+def index_project(x, w_q, w_k, g_q, g_k, pos, *, eps, theta, rot_dim, n_group=4, want_q=True, want_k=True):
+    """Indexer projection: per token and group, y = W x, gemma-style RMS norm
+    (times 1 + gamma), RoPE on the first rot_dim dims with pairs (i, i +
+    rot_dim / 2).  The step order and rotation convention are readings (the
+    MSA pull request names the F32 projections, a gemma-style norm and 0.5
+    partial rotary only).
+
+    x [n_tok][d] f32; w_q, w_k [n_group * hd][d] f32; g_q, g_k [n_group][hd] f32.
+    Returns (q [n_tok][n_group][hd], k [...]) in fp64 (None where not wanted)."""
+    x = _c(x, np.float32)
+    w_q, w_k = _c(w_q, np.float32), _c(w_k, np.float32)
+    g_q, g_k = _c(g_q, np.float32), _c(g_k, np.float32)
+    pos = _idx(pos)
+    n_tok, d = x.shape
+    hd = w_q.shape[0] // n_group
+    if w_q.shape != (n_group * hd, d) or w_k.shape != w_q.shape or g_q.shape != (n_group, hd) or \
+            g_k.shape != g_q.shape or pos.shape != (n_tok,):
+        raise ValueError("index_project: inconsistent shapes")
+    q = np.empty((n_tok, n_group, hd), np.float64) if want_q else None
+    k = np.empty((n_tok, n_group, hd), np.float64) if want_k else None
+    rc = lib().oracle_index_project(n_tok, d, n_group, hd, _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(g_q), _ptr(g_k),
+                                    eps, theta, rot_dim, _ptr(pos), _ptr(q), _ptr(k))
+    if rc != 0:
+        raise ValueError("index_project: rot_dim must be even and at most the head dim")
+    return q, k

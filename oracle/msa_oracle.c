@@ -435,3 +435,61 @@ ORACLE_API int oracle_dsa_select_heads(int idx_dim, int n_head, int top_k, int64
     }
     return 0;
 }
+
+/*
+ * Indexer projection of n_tok tokens ([MSA-PR] Overview and Quantization:
+ * per-group index query and key projections of the hidden state, kept in
+ * F32; review thread, RADV validation comment: the layer uses a gemma-style
+ * norm and RoPE on half of each head, "0.5 partial rotary").  The order of
+ * the steps and the rotation convention are not printed; they are read as
+ *   y  = W[g] x                          (head_dim rows of W per group)
+ *   z  = y / sqrt(mean(y^2) + eps) * (1 + gamma[g])   (gemma-style RMS norm)
+ *   RoPE on dims 0 .. rot_dim - 1, pairs (i, i + rot_dim / 2), angle
+ *   pos * theta^(-2 i / rot_dim); dims >= rot_dim pass through.
+ *   x   : [n_tok][d_model] f32        w_q, w_k : [n_group * head_dim][d_model] f32
+ *   g_q, g_k : [n_group][head_dim] f32  pos : [n_tok]
+ *   q_out, k_out : [n_tok][n_group][head_dim] fp64 (either may be NULL)
+ */
+static void project_head(const float* x, const float* w, const float* gamma, int d_model, int head_dim,
+                         double eps, double theta, int rot_dim, int32_t pos, double* out) {
+    double* y = (double*)malloc((size_t)head_dim * sizeof *y);
+    double ss = 0.0;
+    for (int i = 0; i < head_dim; ++i) {
+        double s = 0.0;
+        for (int d = 0; d < d_model; ++d) s += (double)w[(int64_t)i * d_model + d] * (double)x[d];
+        y[i] = s;
+        ss += s * s;
+    }
+    double inv_rms = 1.0 / sqrt(ss / head_dim + eps);
+    for (int i = 0; i < head_dim; ++i) out[i] = y[i] * inv_rms * (1.0 + (double)gamma[i]);
+    int half = rot_dim / 2;
+    for (int i = 0; i < half; ++i) {
+        double ang = (double)pos * pow(theta, -2.0 * i / rot_dim);
+        double c = cos(ang), s = sin(ang);
+        double a = out[i], b = out[i + half];
+        out[i] = a * c - b * s;
+        out[i + half] = a * s + b * c;
+    }
+    free(y);
+}
+
+ORACLE_API int oracle_index_project(int64_t n_tok, int d_model, int n_group, int head_dim,
+                                    const float* x, const float* w_q, const float* w_k,
+                                    const float* g_q, const float* g_k, double eps, double theta,
+                                    int rot_dim, const int32_t* pos, double* q_out, double* k_out) {
+    if (rot_dim < 0 || rot_dim > head_dim || rot_dim % 2) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n_tok; ++t) {
+        for (int g = 0; g < n_group; ++g) {
+            const int64_t o = (t * n_group + g) * head_dim;
+            const int64_t wo = (int64_t)g * head_dim * d_model;
+            if (q_out)
+                project_head(x + t * d_model, w_q + wo, g_q + g * head_dim, d_model, head_dim, eps, theta,
+                             rot_dim, pos[t], q_out + o);
+            if (k_out)
+                project_head(x + t * d_model, w_k + wo, g_k + g * head_dim, d_model, head_dim, eps, theta,
+                             rot_dim, pos[t], k_out + o);
+        }
+    }
+    return 0;
+}

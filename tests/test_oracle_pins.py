@@ -483,6 +483,83 @@ def test_dsa_heads_relu_sign_and_linearity():
     assert np.array_equal(score(q, -w)[fin], -base[fin])
 
 
+def test_index_project_hand_worked():
+    """x = (1, 2), W = [[1, 1], [1, -1]]: y = (3, -1), rms = sqrt(5).
+    pos 0: z = (3, -1) / sqrt(5) * (1 + gamma) with gamma = (0, 0.5);
+    pos 1 (rot_dim 2, one pair, frequency theta^0 = 1): rotate by 1 rad."""
+    x = np.array([[1.0, 2.0], [1.0, 2.0]], np.float32)
+    w = np.array([[1, 1], [1, -1]], np.float32)
+    g = np.array([[0.0, 0.5]], np.float32)
+    q, _ = oracle.index_project(x, w, w, g, g, [0, 1], eps=0.0, theta=10000.0, rot_dim=2, n_group=1,
+                                want_k=False)
+    a, b = 3 / math.sqrt(5), -1.5 / math.sqrt(5)
+    np.testing.assert_allclose(q[0, 0], [a, b], rtol=1e-15)
+    np.testing.assert_allclose(q[1, 0], [a * math.cos(1) - b * math.sin(1), a * math.sin(1) + b * math.cos(1)],
+                               rtol=1e-14)
+
+
+def _proj_inputs(seed, n_tok=5, d=96, hd=128, n_group=4):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_tok, d)).astype(np.float32)
+    w = (rng.standard_normal((n_group * hd, d)) / math.sqrt(d)).astype(np.float32)
+    g = (0.1 * rng.standard_normal((n_group, hd))).astype(np.float32)
+    return x, w, g
+
+
+def test_index_project_rope_angles():
+    """y = c * e_i for one i at a time: the rotated pair (i, i + 32) must make
+    the angle pos * theta^(-2 i / 64) with the first axis."""
+    hd, rot, theta = 128, 64, 10000.0
+    for i in (0, 1, 7, 31):
+        w = np.zeros((hd, 1), np.float32)
+        w[i, 0] = 1.0
+        for p in (1, 5, 1000, 32767):
+            q, _ = oracle.index_project(np.ones((1, 1), np.float32), w, w, np.zeros((1, hd), np.float32),
+                                        np.zeros((1, hd), np.float32), [p], eps=0.0, theta=theta, rot_dim=rot,
+                                        n_group=1, want_k=False)
+            ang = p * theta ** (-2.0 * i / rot)
+            z = math.sqrt(hd)                                  # e_i normalised to rms 1
+            np.testing.assert_allclose([q[0, 0, i], q[0, 0, i + rot // 2]], [z * math.cos(ang), z * math.sin(ang)],
+                                       rtol=1e-12, atol=1e-12)
+            others = np.delete(q[0, 0], [i, i + rot // 2])
+            assert np.all(others == 0.0)
+
+
+def test_index_project_relative_position():
+    """RoPE: q at a and k at b score the same as q at a + c and k at b + c."""
+    x, w, g = _proj_inputs(21, n_tok=1)
+    xs = np.repeat(x, 4, axis=0)
+    q, k = oracle.index_project(xs, w, w[::-1].copy(), g, g[::-1].copy(), [100, 37, 30100, 30037],
+                                eps=1e-6, theta=10000.0, rot_dim=64)
+    for gg in range(4):
+        assert abs(q[0, gg] @ k[1, gg] - q[2, gg] @ k[3, gg]) < 1e-9 * np.abs(q[0, gg]).sum() * np.abs(k[1, gg]).max()
+    assert abs(q[0, 0] @ k[1, 0] - q[0, 0] @ k[3, 0]) > 1e-6      # not position-independent
+
+
+def test_index_project_norm_and_library_reduction():
+    x, w, g = _proj_inputs(22)
+    z = np.zeros_like(g)
+    pos = np.array([0, 3, 100, 4095, 32767], np.int32)
+    q0, _ = oracle.index_project(x, w, w, z, z, np.zeros(5, np.int32), eps=0.0, theta=10000.0, rot_dim=64,
+                                 want_k=False)
+    y = (x.astype(np.float64) @ w.astype(np.float64).T).reshape(5, 4, 128)
+    ref = y / np.sqrt((y ** 2).mean(-1, keepdims=True))
+    np.testing.assert_allclose(q0, ref, rtol=1e-12, atol=1e-12)
+    # eps: the mean square is mean(y^2) / (mean(y^2) + eps)
+    eps = 0.25
+    qe, _ = oracle.index_project(x, w, w, z, z, np.zeros(5, np.int32), eps=eps, theta=10000.0, rot_dim=64,
+                                 want_k=False)
+    ms = (y ** 2).mean(-1)
+    np.testing.assert_allclose((qe ** 2).mean(-1), ms / (ms + eps), rtol=1e-12)
+    # RoPE keeps each head's norm and leaves dims >= 64 unchanged
+    qp, _ = oracle.index_project(x, w, w, g, g, pos, eps=1e-6, theta=10000.0, rot_dim=64, want_k=False)
+    qg, _ = oracle.index_project(x, w, w, g, g, np.zeros(5, np.int32), eps=1e-6, theta=10000.0, rot_dim=64,
+                                 want_k=False)
+    np.testing.assert_allclose(np.linalg.norm(qp, axis=-1), np.linalg.norm(qg, axis=-1), rtol=1e-12)
+    assert np.array_equal(qp[..., 64:], qg[..., 64:])
+    assert not np.allclose(qp[1:, :, :64], qg[1:, :, :64])
+
+
 def _read_golden_1x4k():
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "decode_1x4k_int.txt")

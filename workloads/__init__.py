@@ -23,6 +23,12 @@ Recipe (stated once, used everywhere):
     store them as f32 (all partial sums are exact in f32).
   * The prefill workload multiplies the f32 indexer vectors by
     float32(1/sqrt(128)) after drawing.
+  * Indexer projection: hidden states float32 N(0, 1) [n_tok][d_model];
+    F32 projection weights N(0, 1) * float32(1/sqrt(d_model)), [512][d_model]
+    each for queries and keys (4 groups x 128); norm gains float32
+    0.1 * N(0, 1) [4][128] each; eps 1e-6, RoPE base 10000 on 64 of 128 dims.
+    d_model defaults to 3072 (the pages give no hidden size for the full
+    model; the pull request's random-weight test model uses 768).
   * Multi-head DSA indexer (n_ihead = 32 heads, the GLM geometry the DSA pull
     request reports): per query, n_ihead fp16 query rows drawn as above and
     n_ihead f32 head weights drawn as float32 N(0, 1) times
@@ -51,6 +57,11 @@ SCALE = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))   # the f32 value both side
 # tensor-kind tags of the seed sequence
 _T_IDX_K, _T_K, _T_V, _T_IDX_Q, _T_Q, _T_DSA_K, _T_DSA_Q = 1, 2, 3, 4, 5, 6, 7
 _T_DSA_QH, _T_DSA_W = 8, 9
+_T_X, _T_WQ, _T_WK, _T_GQ, _T_GK = 10, 11, 12, 13, 14
+PROJ_D_MODEL = 3072
+PROJ_EPS = 1e-6
+PROJ_THETA = 10000.0
+PROJ_ROT_DIM = 64
 DSA_N_IHEAD = 32
 
 
@@ -227,3 +238,20 @@ def caches(wl: Workload, streams: Optional[List[int]] = None) -> Dict[str, np.nd
             out["idx_k"][j] = stream_idx_k(wl, s)
         out["k"][j], out["v"][j] = stream_kv(wl, s)
     return out
+
+
+def hidden_states(n_tok: int, d_model: int = PROJ_D_MODEL, seed: int = 0) -> np.ndarray:
+    """[n_tok][d_model] f32 hidden states entering the indexer projection."""
+    return _normal_f32(_rng(seed, _T_X, 0), (n_tok, d_model))
+
+
+def projection_weights(d_model: int = PROJ_D_MODEL, seed: int = 0) -> Dict[str, np.ndarray]:
+    """F32 indexer projection weights w_q, w_k [512][d_model] and norm gains
+    g_q, g_k [4][128]."""
+    scale = np.float32(1.0 / math.sqrt(d_model))
+    return {
+        "w_q": _normal_f32(_rng(seed, _T_WQ, 0), (N_GROUP * IDX_DIM, d_model)) * scale,
+        "w_k": _normal_f32(_rng(seed, _T_WK, 0), (N_GROUP * IDX_DIM, d_model)) * scale,
+        "g_q": _normal_f32(_rng(seed, _T_GQ, 0), (N_GROUP, IDX_DIM)) * np.float32(0.1),
+        "g_k": _normal_f32(_rng(seed, _T_GK, 0), (N_GROUP, IDX_DIM)) * np.float32(0.1),
+    }
