@@ -314,6 +314,8 @@ def main():
         for name in ("decode_8x128k", "decode_1x4k_int"):
             extra.update(bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name))
             torch.cuda.empty_cache()
+        extra.update(bench_project(M, W, torch, dev, tens))
+        torch.cuda.empty_cache()
 
     traffic = load_traffic("block_scores_decode_kernel@decode_32x32k", "block_scores.hip")
     line = {
@@ -605,6 +607,52 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20):
                       "select_GBps": round(scan_bytes / (seg_h[1] * 1e-3) / 1e9, 1),
                       "shared_layer_us": round(shared_ms * 1e3, 2)},
     }
+
+
+def bench_project(M, W, torch, dev, tens, iters=20):
+    """Indexer projection (hidden states -> idx_q, idx_k appended) at d_model
+    3072: the 32 decode tokens of the 32 x 32K step and the 4096-token
+    prefill chunk.  F32 products: priced against the 157.3 TFLOP/s f32
+    matrix peak."""
+    d = W.PROJ_D_MODEL
+    w = {k: tens(v) for k, v in W.projection_weights(d).items()}
+    pr = M.make_proj(w_q=w["w_q"], w_k=w["w_k"], g_q=w["g_q"], g_k=w["g_k"], eps=W.PROJ_EPS,
+                     rope_theta=W.PROJ_THETA, rot_dim=W.PROJ_ROT_DIM)
+    dims = M.msa_dims(16, W.SCALE)
+    res = {}
+    for name, S, n_tok, cap in (("decode_32", 32, 32, 32768), ("prefill_4096", 1, 4096, 32768)):
+        idx = torch.empty((S, cap, 4, 128), dtype=torch.float32, device=dev)
+        kv = torch.empty((S, cap, 4, 128), dtype=torch.bfloat16, device=dev)
+        cache = M.make_cache(k=kv, v=kv, idx_k=idx)
+        if n_tok == S:
+            st = torch.arange(S, dtype=torch.int32, device=dev)
+            ps = torch.full((S,), cap - 1, dtype=torch.int32, device=dev)
+        else:
+            st = torch.zeros(n_tok, dtype=torch.int32, device=dev)
+            ps = torch.arange(cap - n_tok, cap, dtype=torch.int32, device=dev)
+        x = tens(W.hidden_states(n_tok, d))
+        q = torch.empty((n_tok, 4, 128), dtype=torch.float32, device=dev)
+        ws = torch.empty(M.workspace_bytes(dims, M.MSA_OP_INDEX_PROJECT, n_tok, 0), dtype=torch.uint8, device=dev)
+        run = lambda: M.msa_index_project(dims, cache, pr, x, st, ps, cap - 1, q, ws)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        flop = 2.0 * n_tok * d * 1024
+        wbytes = 2 * 512 * d * 4
+        log(f"[bench] index projection {name}: {us:.1f} us, {flop / us / 1e6:.1f} TFLOP/s, "
+            f"weights {wbytes / us / 1e3:.0f} GB/s")
+        res[name] = {"us": round(us, 2), "TFLOPs": round(flop / us / 1e6, 2),
+                     "frac_fp32_mfma": round(flop / us / 1e6 / 157.3, 4),
+                     "weight_GBps": round(wbytes / us / 1e3, 1)}
+        del idx, kv, cache
+    return {"index_project_d3072": res}
 
 
 if __name__ == "__main__":

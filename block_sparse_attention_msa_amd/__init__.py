@@ -31,12 +31,13 @@ MSA_OP_ATTEND_PREFILL = 4
 DSA_OP_SELECT = 5
 DSA_OP_ATTEND_DECODE = 6
 MSA_OP_BLOCK_SCORES_PREFILL = 7
+MSA_OP_INDEX_PROJECT = 8
 
 EXPORTS = (
     "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",
     "msa_topk_blocks", "msa_select", "msa_block_scores_prefill", "msa_select_prefill",
     "msa_attend_decode", "msa_attend_prefill", "dsa_index_append", "dsa_select",
-    "dsa_select_heads", "dsa_attend_decode",
+    "dsa_select_heads", "dsa_attend_decode", "msa_index_project",
 )
 
 
@@ -57,6 +58,12 @@ class Cache(ctypes.Structure):
                 ("v", ctypes.c_void_p), ("cap", ctypes.c_int64), ("n_stream", ctypes.c_int32),
                 ("idx_k_f16", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("table_stride", ctypes.c_int32)]
+
+
+class Proj(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p),
+                ("g_q", ctypes.c_void_p), ("g_k", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("rot_dim", ctypes.c_int32)]
 
 
 def msa_dims(top_k: int = 16, scale: float = 128 ** -0.5) -> Dims:
@@ -100,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "msa_attend_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
             "dsa_select": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
             "dsa_select_heads": [D, C, P, P, I32, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "msa_index_project": [D, C, ctypes.POINTER(Proj), P, P, P, I64, I32, P, P, ctypes.c_size_t, P],
             "dsa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
         }
         for name, args in sig.items():
@@ -183,9 +191,31 @@ def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor
     return c
 
 
+def make_proj(*, w_q: torch.Tensor, w_k: torch.Tensor, g_q: torch.Tensor, g_k: torch.Tensor,
+              eps: float, rope_theta: float, rot_dim: int) -> Proj:
+    """Indexer projection parameters over caller-owned f32 tensors: w_q, w_k
+    [512][d_model], g_q, g_k [4][128]; held by reference while the
+    descriptor lives."""
+    if w_q.dim() != 2 or w_k.shape != w_q.shape:
+        raise ValueError("w_q and w_k must be [512][d_model]")
+    pr = Proj(w_q.shape[1], _p(w_q, torch.float32, "w_q"), _p(w_k, torch.float32, "w_k"),
+              _p(g_q, torch.float32, "g_q"), _p(g_k, torch.float32, "g_k"), eps, rope_theta, rot_dim)
+    pr.tensors = (w_q, w_k, g_q, g_k)
+    return pr
+
+
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
+def msa_index_project(dims, cache, proj, x, stream, pos, max_pos, idx_q, ws, hip_stream=None):
+    """x [n_tok][d_model] f32 -> idx_q [n_tok][4][128] f32; keys appended to the index cache."""
+    wp, wn = _ws(ws)
+    _check(lib().msa_index_project(ctypes.byref(dims), ctypes.byref(cache), ctypes.byref(proj),
+                                   _p(x, torch.float32, "x"), _p(stream, torch.int32), _p(pos, torch.int32),
+                                   pos.numel(), max_pos, _p(idx_q, torch.float32, "idx_q"), wp, wn,
+                                   _stream(hip_stream)), "msa_index_project")
+
+
 def msa_index_append(dims, cache, stream, pos, max_pos, idx_k_new=None, k_new=None, v_new=None,
                      hip_stream=None):
     _check(lib().msa_index_append(ctypes.byref(dims), ctypes.byref(cache), _p(stream, torch.int32),

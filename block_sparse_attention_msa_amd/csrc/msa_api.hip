@@ -148,8 +148,32 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
             return align256(msa::dsa_select_ws_bytes(n_q, max_pos));
         case DSA_OP_ATTEND_DECODE:
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, 1));
+        case MSA_OP_INDEX_PROJECT:
+            return align256(msa::project_ws_bytes(n_q));
     }
     return bad;
+}
+
+msa_status msa_index_project(const msa_dims* dims, const msa_cache* cache, const msa_proj* proj,
+                             const float* d_x, const int32_t* d_stream, const int32_t* d_pos, int64_t n_tok,
+                             int32_t max_pos, float* d_idx_q, void* d_ws, size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    if (!proj) return MSA_ERR_NULL_ARG;
+    if (proj->d_model < 32 || proj->d_model % 32 || proj->rot_dim < 0 || proj->rot_dim > 64 ||
+        proj->rot_dim % 2 || !(proj->eps >= 0.f) || !(proj->rope_theta > 0.f))
+        return MSA_ERR_UNSUPPORTED;
+    MSA_TRY(check_count_pos(n_tok, max_pos, cache));
+    if (n_tok == 0) return MSA_OK;   // empty call: nothing to read or launch
+    if (n_tok > (int64_t(1) << 24)) return MSA_ERR_UNSUPPORTED;
+    MSA_TRY(check_ptrs({proj->d_w_q, proj->d_w_k, proj->d_g_q, proj->d_g_k, d_x, d_stream, d_pos, d_idx_q}));
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < msa::project_ws_bytes(n_tok)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(msa::launch_index_project(d_x, proj->d_model, proj->d_w_q, proj->d_w_k, proj->d_g_q,
+                                                proj->d_g_k, proj->eps, proj->rope_theta, proj->rot_dim, d_stream,
+                                                d_pos, n_tok, d_idx_q, cache->idx_k, cache->idx_k_f16, view(cache).pg,
+                                                d_ws, static_cast<hipStream_t>(hip_stream)));
 }
 
 msa_status msa_index_append(const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,

@@ -134,7 +134,8 @@ typedef enum msa_op {
     MSA_OP_ATTEND_PREFILL = 4,  /* msa_attend_prefill */
     DSA_OP_SELECT = 5,          /* dsa_select */
     DSA_OP_ATTEND_DECODE = 6,   /* dsa_attend_decode */
-    MSA_OP_BLOCK_SCORES_PREFILL = 7   /* msa_block_scores_prefill */
+    MSA_OP_BLOCK_SCORES_PREFILL = 7,  /* msa_block_scores_prefill */
+    MSA_OP_INDEX_PROJECT = 8          /* msa_index_project (n_q = tokens) */
 } msa_op;
 
 /* Bytes of workspace `op` needs for n_q queries whose positions are all
@@ -163,6 +164,42 @@ MSA_API msa_status msa_index_append(const msa_dims* dims, const msa_cache* cache
                             int32_t max_pos, const float* d_idx_k_new,
                             const uint16_t* d_k_new, const uint16_t* d_v_new,
                             void* hip_stream);
+
+/* Indexer projection parameters (msa_index_project).  DEVICE pointers,
+ * caller-owned, 16-byte aligned. */
+typedef struct msa_proj {
+    int32_t d_model;        /* hidden size, a positive multiple of 32 */
+    const float* d_w_q;     /* [n_group * idx_dim][d_model] f32, row-major (out x in) */
+    const float* d_w_k;     /* [n_group * idx_dim][d_model] f32 */
+    const float* d_g_q;     /* [n_group][idx_dim] f32 norm gains (scale 1 + g) */
+    const float* d_g_k;     /* [n_group][idx_dim] f32 */
+    float eps;              /* RMS norm epsilon, >= 0 */
+    float rope_theta;       /* RoPE base, > 0 */
+    int32_t rot_dim;        /* rotated dims per head: even, 0 .. 64 */
+} msa_proj;
+
+/*
+ * [MSA-PR] Overview and Quantization (per-group index query and key
+ * projections of the hidden state, kept in F32); review thread, RADV
+ * validation comment (gemma-style norm, RoPE over half of each head).  The
+ * step order and the rotation pairs are a reading: per token t and group g
+ *   y = w[g] x[t];  z = y / sqrt(mean(y^2) + eps) * (1 + gain[g]);
+ *   RoPE on dims 0 .. rot_dim - 1, pairs (i, i + rot_dim / 2), angle
+ *   d_pos[t] * rope_theta^(-2 i / rot_dim) (evaluated in f64).
+ * Writes the queries to d_idx_q [n_tok][n_group][idx_dim] f32 and appends
+ * the keys to the index cache at (d_stream[t], d_pos[t]) (f32, or fp16
+ * rounded to nearest even, paged or not), i.e. it replaces the idx_k part of
+ * msa_index_append.  d_x [n_tok][d_model] f32.  Products and sums in f32
+ * (matrix cores), d_model split into at most 128 slices summed in a fixed
+ * order.  Workspace: MSA_OP_INDEX_PROJECT with n_q = n_tok.
+ * Errors: d_model not a positive multiple of 32, rot_dim odd or > 64, eps < 0
+ * or rope_theta <= 0 -> MSA_ERR_UNSUPPORTED.  Device preconditions as
+ * msa_index_append.
+ */
+MSA_API msa_status msa_index_project(const msa_dims* dims, const msa_cache* cache, const msa_proj* proj,
+                             const float* d_x, const int32_t* d_stream, const int32_t* d_pos,
+                             int64_t n_tok, int32_t max_pos, float* d_idx_q, void* d_ws,
+                             size_t ws_bytes, void* hip_stream);
 
 /*
  * [MSA-PR] Implementation: bs = maxpool_128(idx_q . idx_k^T + causal mask),

@@ -193,6 +193,28 @@ def test_dsa_select_heads_validation(L):
                               None) == UNSUP                # MSA geometry
 
 
+def test_index_project_validation(L):
+    d = M.msa_dims()
+    c = M.Cache(A, None, A, A, 4096, 2, None, None, 0)
+    call = lambda pr, n=4, ws=1 << 30: L.msa_index_project(ctypes.byref(d), ctypes.byref(c), ctypes.byref(pr), A, A,
+                                                             A, n, 100, A, A, ws, None)
+    ok = M.Proj(768, A, A, A, A, 1e-6, 10000.0, 64)
+    assert call(ok) not in (NULL, ALIGN, SHAPE, UNSUP, WS)        # accepted (fails later only for want of a GPU)
+    for bad in (M.Proj(100, A, A, A, A, 1e-6, 1e4, 64), M.Proj(0, A, A, A, A, 1e-6, 1e4, 64),
+                M.Proj(768, A, A, A, A, 1e-6, 1e4, 63), M.Proj(768, A, A, A, A, 1e-6, 1e4, 66),
+                M.Proj(768, A, A, A, A, -1.0, 1e4, 64), M.Proj(768, A, A, A, A, 1e-6, 0.0, 64)):
+        assert call(bad) == UNSUP
+    assert call(M.Proj(768, None, A, A, A, 1e-6, 1e4, 64)) == NULL
+    assert call(M.Proj(768, A, A, MIS, A, 1e-6, 1e4, 64)) == ALIGN
+    assert call(ok, ws=16) == WS
+    assert call(ok, n=0) == OK
+    assert L.msa_index_project(ctypes.byref(d), ctypes.byref(c), None, A, A, A, 4, 100, A, A, 1 << 30, None) == NULL
+    # workspace: splits of the hidden size x tokens x 1024 f32
+    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 32, 0) == 128 * 32 * 1024 * 4
+    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 4096, 0) == 1 * 4096 * 1024 * 4
+    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 1000, 0) == 8 * 1000 * 1024 * 4
+
+
 def test_topk_block_limit(L):
     d = M.msa_dims()
     # 4096 blocks of 128 is the most a top-k wave ranks
