@@ -79,6 +79,12 @@ def _declare(L):
     L.oracle_dsa_select_heads.restype = _I
     L.oracle_index_project.argtypes = [_I64, _I, _I, _I, _P, _P, _P, _P, _P, _D, _D, _I, _P, _P, _P]
     L.oracle_index_project.restype = _I
+    L.oracle_kv_quantize.argtypes = [_I64, _I, _I, _P, _P, _P]
+    L.oracle_kv_quantize.restype = _I
+    L.oracle_kv_dequantize.argtypes = [_I64, _I, _I, _P, _P, _P]
+    L.oracle_kv_dequantize.restype = _I
+    L.oracle_sparse_attend_f64.argtypes = [_I, _I, _I, _D, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I, _I, _P]
+    L.oracle_sparse_attend_f64.restype = _I
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:
@@ -272,3 +278,56 @@ def index_project(x, w_q, w_k, g_q, g_k, pos, *, eps, theta, rot_dim, n_group=4,
     if rc != 0:
         raise ValueError("index_project: rot_dim must be even and at most the head dim")
     return q, k
+
+
+KV_INT8, KV_Q4_0 = 1, 2
+
+
+def kv_quantize(x_bits, fmt):
+    """Quantize bf16 rows [..., L] (L a multiple of 32) per 32 values:
+    symmetric absmax, int8 (fmt 1) or 4-bit (fmt 2, nibble-packed), one f32
+    scale per 32 values (the quantizer rule is a reading; the pages give the
+    format only).  Returns (codes uint8 [..., L] or [..., L / 2], scales f32
+    [..., L / 32])."""
+    x_bits = _c(x_bits, np.uint16)
+    L = x_bits.shape[-1]
+    n = x_bits.size // L
+    codes = np.empty(x_bits.shape[:-1] + ((L if fmt == KV_INT8 else L // 2),), np.uint8)
+    scales = np.empty(x_bits.shape[:-1] + (L // 32,), np.float32)
+    if lib().oracle_kv_quantize(n, L, fmt, _ptr(x_bits), _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("kv_quantize: row length must be a multiple of 32, fmt 1 or 2")
+    return codes, scales
+
+
+def kv_dequantize(codes, scales, fmt):
+    """codes * scale per element, fp64 [..., L]."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.float32)
+    L = scales.shape[-1] * 32
+    n = scales.size // (L // 32)
+    out = np.empty(scales.shape[:-1] + (L,), np.float64)
+    if lib().oracle_kv_dequantize(n, L, fmt, _ptr(codes), _ptr(scales), _ptr(out)) != 0:
+        raise ValueError("kv_dequantize: bad format")
+    return out
+
+
+def sparse_attend_f64(k_cache, v_cache, stream, pos, q, sel, *, unit, scale, heads_per_group=16,
+                      shared_across_groups=False):
+    """sparse_attend over fp64 K/V caches [S][cap][G][D] (dequantized caches)."""
+    k_cache = _c(k_cache, np.float64)
+    v_cache = _c(v_cache, np.float64)
+    q = _c(q, np.uint16)
+    sel = _idx(sel)
+    stream = _idx(stream)
+    pos = _idx(pos)
+    _, cap, G, D = k_cache.shape
+    n_q = pos.size
+    L = sel.shape[-1]
+    q_stride, g_stride = (L, 0) if shared_across_groups else (G * L, L)
+    out = np.empty((n_q, G * heads_per_group, D), np.float64)
+    rc = lib().oracle_sparse_attend_f64(G, heads_per_group, D, float(scale), cap, _ptr(k_cache), _ptr(v_cache),
+                                        n_q, _ptr(stream), _ptr(pos), _ptr(q), _ptr(sel), q_stride, g_stride,
+                                        L, unit, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_sparse_attend_f64 failed: {rc}")
+    return out

@@ -493,3 +493,136 @@ ORACLE_API int oracle_index_project(int64_t n_tok, int d_model, int n_group, int
     }
     return 0;
 }
+
+/*
+ * Quantized K/V caches ([QSA] Strata compare page, qsa_prompt_attn.hpp header
+ * comment: int8 KV, and Q4_0 KV whose codes enter exactly as int8 with one
+ * FP32 scale per 32 values, as int8 KV's do).  The quantizer is not printed;
+ * it is read as symmetric absmax per 32 consecutive values of a row:
+ *   fmt 1 (int8): s = max|x| / 127, c = rint(x / s) in -127 .. 127
+ *   fmt 2 (q4_0): s = max|x| / 7,   c = rint(x / s) in -7 .. 7 (-8 unused),
+ *                 stored as c + 8 in a nibble; byte j of a 32-value block
+ *                 holds values j (low nibble) and j + 16 (high nibble)
+ * (s = 0 gives c = 0); value = c * s.  These steps decide integers, so they
+ * are taken in IEEE single precision (f32 division and rint, ties to even),
+ * as the kernel takes them.
+ *   x : [n_rows][row_len] bf16, row_len a multiple of 32
+ *   codes : [n_rows][row_len] int8 (fmt 1) or [n_rows][row_len / 2] (fmt 2)
+ *   scales : [n_rows][row_len / 32] f32
+ */
+ORACLE_API int oracle_kv_quantize(int64_t n_rows, int row_len, int fmt, const uint16_t* x,
+                                  uint8_t* codes, float* scales) {
+    if (row_len % 32 || (fmt != 1 && fmt != 2)) return -1;
+    const int nb = row_len / 32;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            float v[32];
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) {
+                v[j] = (float)oracle_bf16_to_f64(x[r * row_len + 32 * b + j]);   /* exact */
+                float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            volatile float s = amax / (fmt == 1 ? 127.0f : 7.0f);
+            scales[r * nb + b] = s;
+            int c[32];
+            for (int j = 0; j < 32; ++j) {
+                volatile float t = s > 0.0f ? v[j] / s : 0.0f;
+                c[j] = (int)rintf(t);
+            }
+            if (fmt == 1) {
+                for (int j = 0; j < 32; ++j) codes[r * row_len + 32 * b + j] = (uint8_t)(int8_t)c[j];
+            } else {
+                uint8_t* q = codes + r * (row_len / 2) + 16 * b;
+                for (int j = 0; j < 16; ++j)
+                    q[j] = (uint8_t)((c[j] + 8) | ((c[j + 16] + 8) << 4));
+            }
+        }
+    }
+    return 0;
+}
+
+ORACLE_API int oracle_kv_dequantize(int64_t n_rows, int row_len, int fmt, const uint8_t* codes,
+                                    const float* scales, double* out) {
+    if (row_len % 32 || (fmt != 1 && fmt != 2)) return -1;
+    const int nb = row_len / 32;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int b = 0; b < nb; ++b)
+            for (int j = 0; j < 32; ++j) {
+                int c;
+                if (fmt == 1) {
+                    c = (int8_t)codes[r * row_len + 32 * b + j];
+                } else {
+                    uint8_t byte = codes[r * (row_len / 2) + 16 * b + (j & 15)];
+                    c = (j < 16 ? (byte & 15) : (byte >> 4)) - 8;
+                }
+                out[r * row_len + 32 * b + j] = (double)c * (double)scales[r * nb + b];
+            }
+    return 0;
+}
+
+/* attend_head over fp64 K/V rows (dequantized caches). */
+static void attend_head_f64(const uint16_t* q, const double* k_base, const double* v_base,
+                            int64_t row_stride, const int64_t* tok, int64_t n_tok, int head_dim,
+                            double scale, double* z, double* out) {
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const double* krow = k_base + tok[i] * row_stride;
+        double s = 0.0;
+        for (int d = 0; d < head_dim; ++d) s += oracle_bf16_to_f64(q[d]) * krow[d];
+        z[i] = scale * s;
+        if (z[i] > m) m = z[i];
+    }
+    double l = 0.0;
+    for (int d = 0; d < head_dim; ++d) out[d] = 0.0;
+    for (int64_t i = 0; i < n_tok; ++i) {
+        double w = exp(z[i] - m);
+        l += w;
+        const double* vrow = v_base + tok[i] * row_stride;
+        for (int d = 0; d < head_dim; ++d) out[d] += w * vrow[d];
+    }
+    for (int d = 0; d < head_dim; ++d) out[d] /= l;
+}
+
+/* oracle_sparse_attend with fp64 K/V caches [n_stream][cap][n_group][head_dim]. */
+ORACLE_API int oracle_sparse_attend_f64(int n_group, int heads_per_group, int head_dim, double scale,
+                                        int64_t cap, const double* k_cache, const double* v_cache,
+                                        int64_t n_q, const int32_t* stream, const int32_t* pos,
+                                        const uint16_t* q, const int32_t* sel, int64_t sel_q_stride,
+                                        int64_t sel_g_stride, int sel_len, int unit, double* out) {
+    for (int64_t i = 0; i < n_q; ++i)
+        if (pos[i] < 0 || pos[i] >= cap) return -1;
+    int err = 0;
+    int n_head = n_group * heads_per_group;
+    int64_t row_stride = (int64_t)n_group * head_dim;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t w = 0; w < n_q * n_group; ++w) {
+        int64_t i = w / n_group;
+        int g = (int)(w % n_group);
+        int64_t p = pos[i];
+        const int32_t* ids = sel + i * sel_q_stride + g * sel_g_stride;
+        int64_t* tok = (int64_t*)malloc((size_t)sel_len * unit * sizeof *tok);
+        double* z = (double*)malloc((size_t)sel_len * unit * sizeof *z);
+        int64_t n_tok = 0;
+        for (int t = 0; t < sel_len; ++t) {
+            if (ids[t] < 0) continue;
+            for (int64_t j = (int64_t)ids[t] * unit; j < ((int64_t)ids[t] + 1) * unit; ++j)
+                if (j <= p) tok[n_tok++] = j;
+        }
+        int64_t base = ((int64_t)stream[i] * cap * n_group + g) * head_dim;
+        if (n_tok == 0) {
+#pragma omp atomic write
+            err = -3;
+        } else {
+            for (int hh = 0; hh < heads_per_group; ++hh) {
+                int h = g * heads_per_group + hh;
+                attend_head_f64(q + (i * n_head + h) * (int64_t)head_dim, k_cache + base, v_cache + base,
+                                row_stride, tok, n_tok, head_dim, scale, z,
+                                out + (i * n_head + h) * (int64_t)head_dim);
+            }
+        }
+        free(tok);
+        free(z);
+    }
+    return err;
+}

@@ -560,6 +560,63 @@ def test_index_project_norm_and_library_reduction():
     assert not np.allclose(qp[1:, :, :64], qg[1:, :, :64])
 
 
+def _bf16_bits(x):
+    return W.to_bf16_bits(np.asarray(x, np.float32))
+
+
+@pytest.mark.parametrize("fmt,qmax", [(1, 127), (2, 7)])
+def test_kv_quantize_round_trip_and_exact_grid(fmt, qmax):
+    rng = np.random.default_rng(31)
+    x = _bf16_bits(rng.standard_normal((50, 128)))
+    codes, sc = oracle.kv_quantize(x, fmt)
+    xf = x.astype(np.uint32) << 16
+    xv = xf.view(np.float32).astype(np.float64)
+    deq = oracle.kv_dequantize(codes, sc, fmt)
+    # within half a step of the original, step = amax / qmax per 32 values; the f32
+    # quotient x / s carries up to 2^-24 * qmax of error, so a value next to a
+    # half step may round to the farther code (relative excess <= 2 * 2^-24 * qmax)
+    step = np.repeat(sc.astype(np.float64), 32, axis=-1)
+    assert np.all(np.abs(deq - xv) <= 0.5 * step * (1 + 2e-5))
+    np.testing.assert_array_equal(sc, (np.abs(xv).reshape(50, 4, 32).max(-1) / qmax).astype(np.float32))
+    # values on the exact grid c * 2^-3 with amax = qmax * 2^-3: codes exact, round trip exact
+    c = rng.integers(-qmax, qmax + 1, size=(3, 128))
+    c[:, ::32] = qmax
+    grid = c * 0.125
+    codes, sc = oracle.kv_quantize(_bf16_bits(grid), fmt)
+    assert np.all(sc == 0.125)
+    np.testing.assert_array_equal(oracle.kv_dequantize(codes, sc, fmt), grid)
+    # an all-zero block gives scale 0 and zero codes
+    z = np.zeros((1, 128), np.uint16)
+    codes, sc = oracle.kv_quantize(z, fmt)
+    assert np.all(sc == 0) and np.all(oracle.kv_dequantize(codes, sc, fmt) == 0)
+
+
+def test_kv_q4_nibble_layout():
+    """One 32-value block on the integer grid, codes c_j = (j % 15) - 7 (amax 7,
+    so the scale is 1): byte j holds c_j + 8 (low nibble) and c_{j+16} + 8 (high)."""
+    c = np.array([(j % 15) - 7 for j in range(32)], np.int64)
+    c[1] = 7
+    codes, sc = oracle.kv_quantize(_bf16_bits(c[None, :].astype(np.float32)), 2)
+    assert sc[0, 0] == 1.0
+    for j in range(16):
+        assert codes[0, j] == (c[j] + 8) | ((c[j + 16] + 8) << 4)
+
+
+def test_attend_f64_equals_bf16_attention_on_bf16_values():
+    wl = W.Workload("t", "msa_decode", 2, 600, (0, 1, 1), (599, 300, 5))
+    ck = W.caches(wl)
+    qs = W.queries(wl)
+    sel = np.full((3, 4, 16), -1, np.int32)
+    for i, p in enumerate(qs["pos"]):
+        nb = p // 128 + 1
+        sel[i, :, :nb] = np.arange(nb)
+    a = oracle.sparse_attend(ck["k"], ck["v"], qs["stream"], qs["pos"], qs["q"], sel, unit=128, scale=W.SCALE)
+    to64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    b = oracle.sparse_attend_f64(to64(ck["k"]), to64(ck["v"]), qs["stream"], qs["pos"], qs["q"], sel, unit=128,
+                                 scale=W.SCALE)
+    assert np.array_equal(a, b)
+
+
 def _read_golden_1x4k():
     import os
     path = os.path.join(os.path.dirname(__file__), "golden", "decode_1x4k_int.txt")
