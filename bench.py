@@ -252,6 +252,28 @@ def main():
         f"scan {seg_pg[1] * 1e3:.1f} us = {scan_bytes / (seg_pg[1] * 1e-3) / 1e9:.0f} GB/s, "
         f"attend {seg_pg[3] * 1e3:.1f} us")
 
+    # The same step on quantized K/V caches (int8, 4-bit; one f32 scale per 32
+    # values), filled by quantizing the bf16 caches through the append.
+    st_all = torch.arange(S, dtype=torch.int32, device=dev).repeat_interleave(cap)
+    ps_all = torch.arange(cap, dtype=torch.int32, device=dev).repeat(S)
+    kv_quant = {}
+    for fmt, name, width in ((M.KV_INT8, "int8", 128), (M.KV_Q4, "q4", 64)):
+        kq = torch.empty((S, cap, 4, width), dtype=torch.uint8, device=dev)
+        vq = torch.empty_like(kq)
+        ksq = torch.empty((S, cap, 4, 4), dtype=torch.float32, device=dev)
+        vsq = torch.empty_like(ksq)
+        cq = M.make_cache(k=kq, v=vq, idx_k=idx_k, kv_format=fmt, k_scale=ksq, v_scale=vsq)
+        M.msa_index_append(dims, cq, st_all, ps_all, cap - 1, None, k.view(S * cap, 4, 128), v.view(S * cap, 4, 128))
+        seg_q = step_segments(cq)
+        kv_bytes = S * 4 * 16 * 128 * 2 * (width + 16)        # codes + scales of the selected K and V rows
+        log(f"[bench] {name} K/V cache: decode step {seg_q.sum() * 1e3:.1f} us ({S / (seg_q.sum() * 1e-3):.0f} queries/s), "
+            f"attend {seg_q[3] * 1e3:.1f} us ({kv_bytes / (seg_q[3] * 1e-3) / 1e9:.0f} GB/s of K/V)")
+        kv_quant[name] = {"queries_s": round(S / (seg_q.sum() * 1e-3), 1), "step_us": round(seg_q.sum() * 1e3, 2),
+                          "attend_us": round(seg_q[3] * 1e3, 2),
+                          "attend_kv_GBps": round(kv_bytes / (seg_q[3] * 1e-3) / 1e9, 1)}
+        del kq, vq, ksq, vsq, cq
+    del st_all, ps_all
+
     copy_gbps = measure_copy_bandwidth(torch, dev)
     log(f"[bench] device copy {copy_gbps:.0f} GB/s (read + write)")
     extra = {
@@ -270,6 +292,7 @@ def main():
                               "scan_us": round(seg16[1] * 1e3, 2),
                               "scan_GBps": round(scan16_bytes / (seg16[1] * 1e-3) / 1e9, 1),
                               "scan_frac_hbm": round(scan16_bytes / (seg16[1] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "decode_kv_quant": kv_quant,
         "decode_paged": {"queries_s": round(S / (steppg_ms * 1e-3), 1), "step_us": round(steppg_ms * 1e3, 2),
                          "scan_us": round(seg_pg[1] * 1e3, 2), "attend_us": round(seg_pg[3] * 1e3, 2),
                          "scan_GBps": round(scan_bytes / (seg_pg[1] * 1e-3) / 1e9, 1)},

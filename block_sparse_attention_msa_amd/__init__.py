@@ -57,7 +57,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("idx_k", ctypes.c_void_p), ("dsa_k", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("cap", ctypes.c_int64), ("n_stream", ctypes.c_int32),
                 ("idx_k_f16", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
-                ("table_stride", ctypes.c_int32)]
+                ("table_stride", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+KV_BF16, KV_INT8, KV_Q4 = 0, 1, 2
 
 
 class Proj(ctypes.Structure):
@@ -167,15 +171,21 @@ def _check(code: int, where: str):
 
 def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor] = None,
                dsa_k: Optional[torch.Tensor] = None, idx_k_f16: Optional[torch.Tensor] = None,
-               block_table: Optional[torch.Tensor] = None, cap: Optional[int] = None) -> Cache:
+               block_table: Optional[torch.Tensor] = None, cap: Optional[int] = None,
+               kv_format: int = KV_BF16, k_scale: Optional[torch.Tensor] = None,
+               v_scale: Optional[torch.Tensor] = None) -> Cache:
     """Cache descriptor over caller-owned tensors: k, v [S][cap][4][128] bf16;
     idx_k [S][cap][4][128] f32, or idx_k_f16 the same in f16; dsa_k
     [S][cap][128] f16.
     Paged: block_table [S][stride] int32 (page of each logical 128-token
     block), the caches pools [n_pages * 128][4][128] (dsa_k [n_pages * 128][128]),
     and cap the logical capacity per stream (<= stride * 128).
+    Quantized K/V (kv_format KV_INT8 / KV_Q4): k, v uint8 codes [S][cap][4][128]
+    (int8) or [S][cap][4][64] (two 4-bit codes per byte), k_scale, v_scale f32
+    [S][cap][4][4] (one scale per 32 values); pools likewise when paged.
     The descriptor holds references to the tensors, so their memory stays
     allocated while it lives."""
+    kv_dtype = torch.bfloat16 if kv_format == KV_BF16 else torch.uint8
     if block_table is None:
         S, cap_ = k.shape[0], k.shape[1]
         table, stride = None, 0
@@ -185,9 +195,10 @@ def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor
         S, stride = block_table.shape
         cap_, table = cap, _p(block_table, torch.int32, "block_table")
     c = Cache(_p(idx_k, torch.float32, "idx_k"), _p(dsa_k, torch.float16, "dsa_k"),
-              _p(k, torch.bfloat16, "k"), _p(v, torch.bfloat16, "v"), cap_, S,
-              _p(idx_k_f16, torch.float16, "idx_k_f16"), table, stride)
-    c.tensors = (k, v, idx_k, dsa_k, idx_k_f16, block_table)
+              _p(k, kv_dtype, "k"), _p(v, kv_dtype, "v"), cap_, S,
+              _p(idx_k_f16, torch.float16, "idx_k_f16"), table, stride, kv_format,
+              _p(k_scale, torch.float32, "k_scale"), _p(v_scale, torch.float32, "v_scale"))
+    c.tensors = (k, v, idx_k, dsa_k, idx_k_f16, block_table, k_scale, v_scale)
     return c
 
 

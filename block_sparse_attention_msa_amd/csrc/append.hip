@@ -100,7 +100,89 @@ __global__ __launch_bounds__(128) void append_kernel(
     }
 }
 
+// Quantized K/V append: one wave per (new row, K or V).  Lane l holds dims
+// 8 * (l % 16) .. + 7 of group l / 16; the four lanes of a quad share one
+// 32-value block.  Reading of the quantizer (Strata compare page: int8 and
+// Q4_0 KV codes with one FP32 scale per 32 values; the rule is not printed):
+// s = max|x| / 127 (int8) or / 7 (4-bit), c = rint(x / s), s = 0 -> c = 0,
+// all in f32 (correctly rounded division, ties to even).  4-bit codes are
+// stored as c + 8; byte j of a block holds values j (low nibble) and j + 16.
+template <int kQ>
+__global__ __launch_bounds__(128) void append_kv_quant_kernel(uint8_t* __restrict__ k, uint8_t* __restrict__ v,
+                                                              float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                                              Pager pg, const int32_t* __restrict__ stream,
+                                                              const int32_t* __restrict__ pos,
+                                                              const uint16_t* __restrict__ k_new,
+                                                              const uint16_t* __restrict__ v_new) {
+    const int64_t i = blockIdx.x;
+    const bool is_v = threadIdx.x >= 64;
+    const uint16_t* src = is_v ? v_new : k_new;
+    if (!src) return;                                            // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int c16 = lane & 15;                                   // 8-value piece of the group row
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + (i * kGroups + g) * kHeadDim + 8 * c16);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t word = w[e >> 1];
+        x[e] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor1>(amax));
+    amax = fmaxf(amax, dpp_f32<kDppQuadXor2>(amax));
+    const float sc = amax / (kQ == 1 ? 127.f : 7.f);
+    int code[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e] = sc > 0.f ? static_cast<int>(__builtin_rintf(x[e] / sc)) : 0;
+    const int64_t rq = pg.row(stream[i], pos[i]) * kGroups + g;
+    uint8_t* dst = is_v ? v : k;
+    float* sdst = is_v ? v_scale : k_scale;
+    if ((lane & 3) == 0) sdst[rq * (kHeadDim / 32) + (c16 >> 2)] = sc;
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    if constexpr (kQ == 1) {
+        u32x2_t o = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e >> 2] |= static_cast<uint32_t>(code[e] & 0xff) << (8 * (e & 3));
+        *reinterpret_cast<u32x2_t*>(dst + rq * kHeadDim + 8 * c16) = o;
+    } else {
+        // quad lanes 0, 1 hold values 0 .. 15 of the block, lanes 2, 3 values 16 .. 31
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t n = static_cast<uint32_t>(code[e] + 8) & 15u;
+            if (e < 4) lo |= n << (4 * e); else hi |= n << (4 * (e - 4));
+        }
+        const uint32_t plo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(lo), kDppQuadXor2, 0xf, 0xf, false));
+        const uint32_t phi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(hi), kDppQuadXor2, 0xf, 0xf, false));
+        if ((lane & 3) < 2) {
+            u32x2_t o = {0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t mine = ((e < 4 ? lo : hi) >> (4 * (e & 3))) & 15u;
+                const uint32_t part = ((e < 4 ? plo : phi) >> (4 * (e & 3))) & 15u;
+                o[e >> 2] |= (mine | (part << 4)) << (8 * (e & 3));
+            }
+            *reinterpret_cast<u32x2_t*>(dst + rq * (kHeadDim / 2) + 16 * (c16 >> 2) + 8 * (lane & 1)) = o;
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_append_kv_quant(int kv_format, uint8_t* k, uint8_t* v, float* k_scale, float* v_scale,
+                                  const Pager& pg, const int32_t* stream, const int32_t* pos, int64_t n_new,
+                                  const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
+    if (kv_format == 1)
+        hipLaunchKernelGGL(append_kv_quant_kernel<1>, dim3(static_cast<unsigned>(n_new)), dim3(128), 0, s, k, v,
+                           k_scale, v_scale, pg, stream, pos, k_new, v_new);
+    else
+        hipLaunchKernelGGL(append_kv_quant_kernel<2>, dim3(static_cast<unsigned>(n_new)), dim3(128), 0, s, k, v,
+                           k_scale, v_scale, pg, stream, pos, k_new, v_new);
+    return hipGetLastError();
+}
 
 hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint16_t* k, uint16_t* v, const Pager& pg,
                          const int32_t* stream, const int32_t* pos, int64_t n_new,

@@ -23,6 +23,14 @@
 //    the log2 domain per wave; the four waves merge in LDS; splits write
 //    (m, l, acc) partials that a second kernel combines in a fixed order, so
 //    results are deterministic.
+//  * Quantized caches (int8 or 4-bit codes, one f32 scale per 32 values; the
+//    Strata compare page's int8 / Q4_0 KV): a unit's codes and scales are
+//    loaded into registers while the previous unit is computed, then written
+//    to the ring buffer in the same permuted layout: K as its codes (exact in
+//    bf16) with the scales beside them, applied to each 32-dim slice of
+//    S^T = K Q^T after its matrix-core product (one slice is one scale
+//    block), and V as code * scale rounded to bf16 (it enters the output
+//    linearly, as the bf16 probabilities do).
 #include "common.hpp"
 
 namespace msa {
@@ -82,7 +90,7 @@ struct KernelArgs {
 // ones are copied from a valid row and fully masked), so the compiler can
 // tell which ring buffer every copy in flight targets and reads of the other
 // buffer never wait for it.
-template <bool kTokenIds, int kMaxUnits>
+template <bool kTokenIds, int kMaxUnits, int kQ = 0>
 __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     const AttendArgs& a = ka.a;
     const int64_t wg = blockIdx.x;                 // ((query * kGroups) + group) * n_split + split
@@ -105,6 +113,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     __shared__ float mrg_m[kAttWaves][kHeadsPerGroup];
     __shared__ float mrg_l[kAttWaves][kHeadsPerGroup];
     __shared__ int n_valid_s;
+    // quantized K: scales of the ring's two units, [slice][key] (4 keys of a lane contiguous)
+    __shared__ __attribute__((aligned(16))) float kscl_s[2][kQ ? 4 * kUnit : 4];
 
     const int64_t s = a.stream[i];
     const int p = a.pos[i];
@@ -174,6 +184,64 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         }
     };
 
+    // Quantized caches: slot j of this thread (as in stage) holds dims
+    // 8 * seg .. + 7 of row `row`: 8 codes (int8: 8 bytes; 4-bit: the low or
+    // high nibbles of 8 bytes of the 32-value block) and that block's scale.
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    constexpr int kQSlots = kQ ? kCopiesPerUnit : 1;
+    u32x2_t kc[kQSlots], vc[kQSlots];
+    float kscl[kQSlots], vscl[kQSlots];
+    auto qload = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kQSlots; ++j) {
+            const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
+            const int row = c >> 4;
+            const int seg = (c & 15) ^ rowperm(row);
+            const int e = kTokenIds ? u * kUnit + row : u;
+            const int tok = kTokenIds ? sel_s[e] : sel_s[e] * kBlock + row;
+            const int r_e = row_s[e];
+            const int r_own = row_s[kMaxSplitEntries];
+            const bool bad = u >= n_units || tok < 0 || tok > p;
+            const int64_t rq = static_cast<int64_t>(bad ? r_own : r_e + (kTokenIds ? 0 : row)) * kGroups + g;
+            const int64_t boff = kQ == 1 ? rq * kHeadDim + 8 * seg
+                                         : rq * (kHeadDim / 2) + 16 * (seg >> 2) + 8 * ((seg & 3) & 1);
+            kc[j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.k) + boff);
+            vc[j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.v) + boff);
+            kscl[j] = a.k_scale[rq * (kHeadDim / 32) + (seg >> 2)];
+            vscl[j] = a.v_scale[rq * (kHeadDim / 32) + (seg >> 2)];
+        }
+    };
+    auto dequant8 = [&](u32x2_t w, float sc, bool high) __attribute__((always_inline)) {
+        float f[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint32_t word = w[b >> 2];
+            const int byte = static_cast<int>((word >> (8 * (b & 3))) & 0xffu);
+            const int code = kQ == 1 ? static_cast<int>(static_cast<int8_t>(byte))
+                                     : (high ? (byte >> 4) : (byte & 15)) - 8;
+            f[b] = static_cast<float>(code) * sc;
+        }
+        u32x4 o;
+        o[0] = pack_bf16x2(f[0], f[1]);
+        o[1] = pack_bf16x2(f[2], f[3]);
+        o[2] = pack_bf16x2(f[4], f[5]);
+        o[3] = pack_bf16x2(f[6], f[7]);
+        return o;
+    };
+    auto qcommit = [&](char* kd, char* vd, float* ksd) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kQSlots; ++j) {
+            const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
+            const int row = c >> 4;
+            const int seg = (c & 15) ^ rowperm(row);
+            const bool high = (seg & 3) >= 2;          // 4-bit: values 16 .. 31 of the block
+            *reinterpret_cast<u32x4*>(kd + 16 * c) = dequant8(kc[j], 1.f, high);   // codes, exact
+            *reinterpret_cast<u32x4*>(vd + 16 * c) = dequant8(vc[j], vscl[j], high);
+            if ((seg & 3) == 0) ksd[(seg >> 2) * kUnit + row] = kscl[j];
+        }
+    };
+    const float* ks_cur = kscl_s[0];           // scales of the unit being computed (quantized K)
+
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[8];
 #pragma unroll
@@ -219,15 +287,34 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
                                                  0, 1, 2, 3, 4, 5, 6, 7);
             }
         }
-        release();
-        if (!any) return;                          // nothing of this wave's keys is visible
         // S^T = K Q^T; lane gets keys 32w + 16t + 4*l4 + r of head l16
         f32x4 st[2];
+        if constexpr (kQ != 0) {
+            // quantized K: slice ks is scale block ks of every key row, so each
+            // slice's product is scaled per key; done before the release,
+            // since the scales live in the ring unit's LDS
+            if (any) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < 2; ++t) {
+                    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) st[t] = mfma_16x16x32_bf16(kA[t][ks], qb[ks], st[t]);
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const f32x4 part = mfma_16x16x32_bf16(kA[t][ks], qb[ks], f32x4{0.f, 0.f, 0.f, 0.f});
+                        const f32x4 sc = *reinterpret_cast<const f32x4*>(ks_cur + ks * kUnit + 32 * wave + 16 * t + 4 * l4);
+                        st[t] += sc * part;
+                    }
+                }
+            }
+        }
+        release();
+        if (!any) return;                          // nothing of this wave's keys is visible
+        if constexpr (kQ == 0) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) st[t] = mfma_16x16x32_bf16(kA[t][ks], qb[ks], st[t]);
+            }
         }
         float x[8];
 #pragma unroll
@@ -269,21 +356,44 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     // most that many are outstanding means unit u has landed.  Only copies
     // into LDS are in flight in the loop.
     static_assert(kMaxUnits % 2 == 0, "units alternate between the two ring buffers");
-    stage(0, kbuf0, vbuf0);
-    stage(1, kbuf1, vbuf1);
-    auto step = [&](int u, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
-        if (u + 1 < kMaxUnits) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerUnit));   // compile-time
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        lds_barrier();                             // unit u is in LDS
-        compute(u, kb, vb, [&]() __attribute__((always_inline)) {
-            lds_barrier();                         // every wave has its operands: refill the buffers
-            if (u + 2 < kMaxUnits) stage(u + 2, kn, vn);
-        });
-    };
+    if constexpr (kQ == 0) {
+        stage(0, kbuf0, vbuf0);
+        stage(1, kbuf1, vbuf1);
+        auto step = [&](int u, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
+            if (u + 1 < kMaxUnits) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerUnit));   // compile-time
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            lds_barrier();                         // unit u is in LDS
+            compute(u, kb, vb, [&]() __attribute__((always_inline)) {
+                lds_barrier();                     // every wave has its operands: refill the buffers
+                if (u + 2 < kMaxUnits) stage(u + 2, kn, vn);
+            });
+        };
 #pragma unroll
-    for (int u = 0; u < kMaxUnits; u += 2) {
-        step(u, kbuf0, vbuf0, kbuf0, vbuf0);
-        step(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
+        for (int u = 0; u < kMaxUnits; u += 2) {
+            step(u, kbuf0, vbuf0, kbuf0, vbuf0);
+            step(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
+        }
+    } else {
+        // quantized: unit u + 2 loads into registers once every wave holds
+        // unit u's operands and is written to u's buffer after u's math
+        qload(0);
+        qcommit(kbuf0, vbuf0, kscl_s[0]);
+        qload(1);
+        qcommit(kbuf1, vbuf1, kscl_s[1]);
+        auto qstep = [&](int u, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
+            ks_cur = kscl_s[u & 1];
+            lds_barrier();                         // unit u is in LDS (written by every wave)
+            compute(u, kb, vb, [&]() __attribute__((always_inline)) {
+                lds_barrier();                     // every wave has its operands and scales
+                if (u + 2 < kMaxUnits) qload(u + 2);
+            });
+            if (u + 2 < kMaxUnits) qcommit(kn, vn, kscl_s[u & 1]);
+        };
+#pragma unroll
+        for (int u = 0; u < kMaxUnits; u += 2) {
+            qstep(u, kbuf0, vbuf0, kbuf0, vbuf0);
+            qstep(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
+        }
     }
 
     // ---- merge the four waves (lane holds O^T[dim 16*dt + 4*l4 + r][head l16])
@@ -365,6 +475,20 @@ int num_units(int sel_len, int unit) {
 constexpr int kUnitsPerSplitMax = 8;
 static_assert(kMaxSplitEntries == kUnitsPerSplitMax * kUnit, "ids one split stages");
 
+// instantiations for splits of up to 2, 4 and 8 units
+template <int kQ>
+void launch_units(const KernelArgs& ka, bool blocks, int nu, dim3 grid, hipStream_t s) {
+    if (blocks) {
+        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<false, 2, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+        else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<false, 4, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+        else hipLaunchKernelGGL((attend_kernel<false, kUnitsPerSplitMax, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+    } else {
+        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<true, 2, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+        else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<true, 4, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+        else hipLaunchKernelGGL((attend_kernel<true, kUnitsPerSplitMax, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+    }
+}
+
 }  // namespace
 
 int attend_num_splits(int64_t n_q, int sel_len, int unit) {
@@ -393,16 +517,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     ka.n_units = num_units(a.sel_len, a.unit);
     ka.units_per_split = (ka.n_units + ka.n_split - 1) / ka.n_split;
     const dim3 grid(static_cast<unsigned>(a.n_q * kGroups * ka.n_split));
-    // instantiations for splits of up to 2, 4 and 8 units
     const int nu = ka.units_per_split;
-    if (a.unit == kBlock) {
-        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<false, 2>), grid, dim3(kAttThreads), 0, s, ka);
-        else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<false, 4>), grid, dim3(kAttThreads), 0, s, ka);
-        else hipLaunchKernelGGL((attend_kernel<false, kUnitsPerSplitMax>), grid, dim3(kAttThreads), 0, s, ka);
-    } else {
-        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<true, 2>), grid, dim3(kAttThreads), 0, s, ka);
-        else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<true, 4>), grid, dim3(kAttThreads), 0, s, ka);
-        else hipLaunchKernelGGL((attend_kernel<true, kUnitsPerSplitMax>), grid, dim3(kAttThreads), 0, s, ka);
+    switch (a.kv_format) {
+        case 0: launch_units<0>(ka, a.unit == kBlock, nu, grid, s); break;
+        case 1: launch_units<1>(ka, a.unit == kBlock, nu, grid, s); break;
+        case 2: launch_units<2>(ka, a.unit == kBlock, nu, grid, s); break;
+        default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ka.n_split == 1) return e;

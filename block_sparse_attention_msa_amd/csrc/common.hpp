@@ -151,6 +151,11 @@ hipError_t launch_append(float* idx_k, uint16_t* idx_k16, uint16_t* dsa_k, uint1
                          const int32_t* stream, const int32_t* pos, int64_t n_new,
                          const float* idx_k_new, const uint16_t* dsa_key_new,
                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
+// Quantized K/V append (kv_format 1: int8, 2: 4-bit codes; one f32 scale per
+// 32 values): rows d_k_new / d_v_new (bf16) are quantized into the caches.
+hipError_t launch_append_kv_quant(int kv_format, uint8_t* k, uint8_t* v, float* k_scale, float* v_scale,
+                                  const Pager& pg, const int32_t* stream, const int32_t* pos, int64_t n_new,
+                                  const uint16_t* k_new, const uint16_t* v_new, hipStream_t s);
 
 hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
@@ -187,6 +192,9 @@ struct AttendArgs {
     float scale;
     float* out;
     void* ws;
+    int kv_format;           // 0 bf16; 1 int8, 2 4-bit codes with f32 scales per 32 values
+    const float* k_scale;    // [rows][kGroups][kHeadDim / 32] (quantized caches)
+    const float* v_scale;
 };
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);

@@ -36,6 +36,11 @@ msa_status check_cache(const msa_cache* c) {
         if (reinterpret_cast<uintptr_t>(c->d_block_table) % 4) return MSA_ERR_MISALIGNED;
         if (c->table_stride < 1 || int64_t(c->table_stride) * kBlock < c->cap) return MSA_ERR_BAD_SHAPE;
     }
+    if (c->kv_format < 0 || c->kv_format > 2) return MSA_ERR_UNSUPPORTED;
+    if (c->kv_format && (c->k || c->v)) {
+        if (!c->k_scale || !c->v_scale) return MSA_ERR_NULL_ARG;
+        if (!aligned16(c->k_scale) || !aligned16(c->v_scale)) return MSA_ERR_MISALIGNED;
+    }
     return MSA_OK;
 }
 
@@ -103,9 +108,17 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
     if (d_key_new) MSA_TRY(check_ptrs({d_key_new, cache->dsa_k}));
     if (d_k_new) MSA_TRY(check_ptrs({d_k_new, cache->k}));
     if (d_v_new) MSA_TRY(check_ptrs({d_v_new, cache->v}));
+    const bool quant = cache->kv_format != 0 && (d_k_new || d_v_new);
+    const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (quant) {
+        MSA_TRY(hip_status(msa::launch_append_kv_quant(
+            cache->kv_format, reinterpret_cast<uint8_t*>(cache->k), reinterpret_cast<uint8_t*>(cache->v),
+            cache->k_scale, cache->v_scale, view(cache).pg, d_stream, d_pos, n_new, d_k_new, d_v_new, st)));
+        if (!d_idx_k_new && !d_key_new) return MSA_OK;
+    }
     return hip_status(msa::launch_append(cache->idx_k, cache->idx_k_f16, cache->dsa_k, cache->k, cache->v, view(cache).pg,
-                                         d_stream, d_pos, n_new, d_idx_k_new, d_key_new, d_k_new,
-                                         d_v_new, static_cast<hipStream_t>(hip_stream)));
+                                         d_stream, d_pos, n_new, d_idx_k_new, d_key_new, quant ? nullptr : d_k_new,
+                                         quant ? nullptr : d_v_new, st));
 }
 
 }  // namespace
@@ -304,7 +317,8 @@ msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
     }
     msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q, d_stream, d_pos, n_q, d_sel,
-                      dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws};
+                      dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws,
+                      cache->kv_format, cache->k_scale, cache->v_scale};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
 
@@ -318,6 +332,7 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     if (nblk_of(static_cast<int32_t>(pos0 + n_q - 1)) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
+    if (cache->kv_format != 0) return MSA_ERR_UNSUPPORTED;   // quantized caches: decode attention only
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out, d_ws}));
     if (ws_bytes < msa::prefill_attend_ws_bytes(n_q, dims->top_k)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     return hip_status(msa::launch_prefill_attend(cache->k, cache->v, view(cache).pg, d_q, stream, pos0, n_q, d_sel,
@@ -375,7 +390,8 @@ msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
         if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
     }
     msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q, d_stream, d_pos, n_q, d_sel,
-                      dims->top_k, 0, 1, dims->scale, d_out, d_ws};
+                      dims->top_k, 0, 1, dims->scale, d_out, d_ws,
+                      cache->kv_format, cache->k_scale, cache->v_scale};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
 }
 

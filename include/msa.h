@@ -124,6 +124,21 @@ typedef struct msa_cache {
      * is a page inside all the pools the call reads or writes. */
     const int32_t* d_block_table;
     int32_t table_stride;
+    /* Quantized K/V caches ([QSA] Strata compare page, qsa_prompt_attn.hpp
+     * header: int8 KV, and Q4_0 KV whose codes enter as int8, with one FP32
+     * scale per 32 values).  kv_format 0: k, v are bf16 as above.  1: k, v
+     * hold int8 codes [rows][n_group][head_dim] (1 byte each).  2: 4-bit
+     * codes [rows][n_group][head_dim / 2]; byte j of each 32-value block
+     * holds values j (low nibble) and j + 16 (high nibble), stored as code + 8.
+     * k_scale, v_scale: [rows][n_group][head_dim / 32] f32; value = code *
+     * scale.  The append quantizes bf16 rows: s = max|x| / 127 (int8) or / 7
+     * (4-bit), code = rint(x / s) in f32 (a reading: the pages give the
+     * format, not the rule).  Supported by the appends and decode attention
+     * (msa_attend_decode, dsa_attend_decode); msa_attend_prefill returns
+     * MSA_ERR_UNSUPPORTED.  Other values -> MSA_ERR_UNSUPPORTED. */
+    int32_t kv_format;
+    float* k_scale;
+    float* v_scale;
 } msa_cache;
 
 /* Operations whose workspace size can be queried. */

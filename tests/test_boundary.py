@@ -215,6 +215,18 @@ def test_index_project_validation(L):
     assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 1000, 0) == 8 * 1000 * 1024 * 4
 
 
+def test_kv_format_validation(L):
+    d = M.msa_dims()
+    mk = lambda fmt, ks, vs: M.Cache(A, None, A, A, 4096, 2, None, None, 0, fmt, ks, vs)
+    att = lambda c: L.msa_attend_decode(ctypes.byref(d), ctypes.byref(c), A, A, A, 1, 100, A, A, A, 1 << 30, None)
+    assert att(mk(3, A, A)) == UNSUP and att(mk(-1, A, A)) == UNSUP
+    assert att(mk(1, None, A)) == NULL
+    assert att(mk(2, A, MIS)) == ALIGN
+    assert att(mk(1, A, A)) not in (NULL, ALIGN, SHAPE, UNSUP)     # accepted (fails later only for want of a GPU)
+    pre = lambda c: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 0, 10, A, A, A, 1 << 30, None)
+    assert pre(mk(1, A, A)) == UNSUP and pre(mk(0, None, None)) not in (NULL, ALIGN, SHAPE, UNSUP)
+
+
 def test_topk_block_limit(L):
     d = M.msa_dims()
     # 4096 blocks of 128 is the most a top-k wave ranks
