@@ -189,9 +189,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     // high nibbles of 8 bytes of the 32-value block) and that block's scale.
     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
     constexpr int kQSlots = kQ ? kCopiesPerUnit : 1;
-    u32x2_t kc[kQSlots], vc[kQSlots];
-    float kscl[kQSlots], vscl[kQSlots];
-    auto qload = [&](int u) __attribute__((always_inline)) {
+    // two register sets: unit u + 1 loads at the release of unit u - 1 and
+    // is written to the ring after the math of unit u
+    u32x2_t kc[2][kQSlots], vc[2][kQSlots];
+    float kscl[2][kQSlots], vscl[2][kQSlots];
+    auto qload = [&](int u, int set) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kQSlots; ++j) {
             const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
@@ -205,10 +207,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
             const int64_t rq = static_cast<int64_t>(bad ? r_own : r_e + (kTokenIds ? 0 : row)) * kGroups + g;
             const int64_t boff = kQ == 1 ? rq * kHeadDim + 8 * seg
                                          : rq * (kHeadDim / 2) + 16 * (seg >> 2) + 8 * ((seg & 3) & 1);
-            kc[j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.k) + boff);
-            vc[j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.v) + boff);
-            kscl[j] = a.k_scale[rq * (kHeadDim / 32) + (seg >> 2)];
-            vscl[j] = a.v_scale[rq * (kHeadDim / 32) + (seg >> 2)];
+            kc[set][j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.k) + boff);
+            vc[set][j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.v) + boff);
+            kscl[set][j] = a.k_scale[rq * (kHeadDim / 32) + (seg >> 2)];
+            vscl[set][j] = a.v_scale[rq * (kHeadDim / 32) + (seg >> 2)];
         }
     };
     auto dequant8 = [&](u32x2_t w, float sc, bool high) __attribute__((always_inline)) {
@@ -228,16 +230,16 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         o[3] = pack_bf16x2(f[6], f[7]);
         return o;
     };
-    auto qcommit = [&](char* kd, char* vd, float* ksd) __attribute__((always_inline)) {
+    auto qcommit = [&](int set, char* kd, char* vd, float* ksd) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kQSlots; ++j) {
             const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
             const int row = c >> 4;
             const int seg = (c & 15) ^ rowperm(row);
             const bool high = (seg & 3) >= 2;          // 4-bit: values 16 .. 31 of the block
-            *reinterpret_cast<u32x4*>(kd + 16 * c) = dequant8(kc[j], 1.f, high);   // codes, exact
-            *reinterpret_cast<u32x4*>(vd + 16 * c) = dequant8(vc[j], vscl[j], high);
-            if ((seg & 3) == 0) ksd[(seg >> 2) * kUnit + row] = kscl[j];
+            *reinterpret_cast<u32x4*>(kd + 16 * c) = dequant8(kc[set][j], 1.f, high);   // codes, exact
+            *reinterpret_cast<u32x4*>(vd + 16 * c) = dequant8(vc[set][j], vscl[set][j], high);
+            if ((seg & 3) == 0) ksd[(seg >> 2) * kUnit + row] = kscl[set][j];
         }
     };
     const float* ks_cur = kscl_s[0];           // scales of the unit being computed (quantized K)
@@ -374,25 +376,27 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
             step(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
         }
     } else {
-        // quantized: unit u + 2 loads into registers once every wave holds
-        // unit u's operands and is written to u's buffer after u's math
-        qload(0);
-        qcommit(kbuf0, vbuf0, kscl_s[0]);
-        qload(1);
-        qcommit(kbuf1, vbuf1, kscl_s[1]);
-        auto qstep = [&](int u, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
-            ks_cur = kscl_s[u & 1];
+        // quantized: unit u + 2 loads into register set u % 2 once every wave
+        // holds unit u's operands; unit u + 1 (loaded one unit earlier) is
+        // written to its buffer, freed at the release of unit u - 1, after the
+        // math of unit u
+        qload(0, 0);
+        qcommit(0, kbuf0, vbuf0, kscl_s[0]);
+        qload(1, 1);
+        auto qstep = [&](int u, int set, const char* kb, const char* vb, char* kn, char* vn, float* ksn)
+            __attribute__((always_inline)) {
+            ks_cur = kscl_s[set];
             lds_barrier();                         // unit u is in LDS (written by every wave)
             compute(u, kb, vb, [&]() __attribute__((always_inline)) {
                 lds_barrier();                     // every wave has its operands and scales
-                if (u + 2 < kMaxUnits) qload(u + 2);
+                if (u + 2 < kMaxUnits) qload(u + 2, set);
             });
-            if (u + 2 < kMaxUnits) qcommit(kn, vn, kscl_s[u & 1]);
+            if (u + 1 < kMaxUnits) qcommit(set ^ 1, kn, vn, ksn);
         };
 #pragma unroll
         for (int u = 0; u < kMaxUnits; u += 2) {
-            qstep(u, kbuf0, vbuf0, kbuf0, vbuf0);
-            qstep(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
+            qstep(u, 0, kbuf0, vbuf0, kbuf1, vbuf1, kscl_s[1]);
+            qstep(u + 1, 1, kbuf1, vbuf1, kbuf0, vbuf0, kscl_s[0]);
         }
     }
 
