@@ -84,9 +84,8 @@ def load_traffic(kernel_key, src):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards across GPUs without exchange by stream, group or query; see the design "
-              "notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path shards across "
+              "GPUs without exchange, by stream, group or query)", file=sys.stderr)
         sys.exit(2)
 
     import torch
