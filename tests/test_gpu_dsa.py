@@ -73,3 +73,30 @@ def test_dsa_all_scores_tied():
 
 def test_dsa_full_16x64k():
     _dsa_parity(W.CONFIGS["dsa_16x64k"])
+
+
+@pytest.mark.parametrize("top_k", [2048, 64])
+def test_dsa_topk_with_ties_exact(top_k):
+    """Integer keys and queries make every score an exact small integer, so
+    ties are everywhere (far more keys share the boundary score than the LDS
+    candidate list holds) and the selection must equal the oracle's bit for
+    bit (ties to the lower token id), including a query shorter than top_k."""
+    S, cap = 2, 40000
+    rng = np.random.default_rng(17)
+    k_rot = rng.integers(-2, 3, size=(S, cap, 128)).astype(np.float16)
+    pos = np.array([39999, 1500, 20000, 17000], np.int32)
+    stream = np.array([0, 1, 1, 0], np.int32)
+    q = rng.integers(-1, 2, size=(4, 128)).astype(np.float16)
+    log(f"[dsa] exact ties, top_k {top_k}")
+    dims = M.dsa_dims(top_k, W.SCALE)
+    dsa_k = torch.from_numpy(k_rot).to(DEV)
+    kv = torch.zeros((S, cap, 4, 128), dtype=torch.bfloat16, device=DEV)
+    cache = M.make_cache(k=kv, v=kv, dsa_k=dsa_k)
+    sel = torch.empty((4, top_k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty(4, dtype=torch.int32, device=DEV)
+    ws = torch.empty(M.workspace_bytes(dims, M.DSA_OP_SELECT, 4, int(pos.max())), dtype=torch.uint8, device=DEV)
+    M.dsa_select(dims, cache, torch.from_numpy(q).to(DEV), dev(stream), dev(pos), int(pos.max()), sel, n_sel, ws)
+    torch.cuda.synchronize()
+    o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
+    assert np.array_equal(n_sel.cpu().numpy(), o_nsel)
+    assert np.array_equal(sel.cpu().numpy(), o_sel), "selection differs from the oracle"
