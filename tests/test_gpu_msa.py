@@ -126,6 +126,19 @@ def test_decode_full_8x128k():
     _decode_parity(W.CONFIGS["decode_8x128k"])
 
 
+def test_decode_max_context_4096_blocks():
+    """The largest context the block top-k ranks: 4096 blocks (524288 keys)."""
+    cap = 4096 * 128
+    wl = W.Workload("max_ctx", "msa_decode", 1, cap, (0, 0, 0), (cap - 1, cap - 129, 300000))
+    _decode_parity(wl)
+
+
+def test_prefill_max_context_4096_blocks():
+    """A prefill chunk ending at the last key of a 4096-block context."""
+    cap = 4096 * 128
+    _prefill_parity(W.prefill_workload("pf_max_ctx", cap, cap - 100, 100))
+
+
 def test_empty_calls_launch_nothing():
     wl = W.decode_workload("e", 1, 256)
     gw = GpuWorkload(wl)
