@@ -26,11 +26,12 @@
 //  * Quantized caches (int8 or 4-bit codes, one f32 scale per 32 values; the
 //    Strata compare page's int8 / Q4_0 KV): a unit's codes and scales are
 //    loaded into registers while the previous unit is computed, then written
-//    to the ring buffer in the same permuted layout: K as its codes (exact in
-//    bf16) with the scales beside them, applied to each 32-dim slice of
-//    S^T = K Q^T after its matrix-core product (one slice is one scale
-//    block), and V as code * scale rounded to bf16 (it enters the output
-//    linearly, as the bf16 probabilities do).
+//    to the ring buffer in the same permuted layout as their codes (exact in
+//    bf16) with the scales beside them: K's scales multiply each 32-dim
+//    slice of S^T = K Q^T after its matrix-core product (one slice is one
+//    scale block), and V's are folded into the probabilities, one bf16 P
+//    operand per 32-dim block of the output, so the only rounding is that of
+//    the scaled probabilities, as in the bf16 path.
 #include "common.hpp"
 
 namespace msa {
@@ -113,8 +114,9 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     __shared__ float mrg_m[kAttWaves][kHeadsPerGroup];
     __shared__ float mrg_l[kAttWaves][kHeadsPerGroup];
     __shared__ int n_valid_s;
-    // quantized K: scales of the ring's two units, [slice][key] (4 keys of a lane contiguous)
+    // quantized K and V: scales of the ring's two units, [block][key] (4 keys of a lane contiguous)
     __shared__ __attribute__((aligned(16))) float kscl_s[2][kQ ? 4 * kUnit : 4];
+    __shared__ __attribute__((aligned(16))) float vscl_s[2][kQ ? 4 * kUnit : 4];
 
     const int64_t s = a.stream[i];
     const int p = a.pos[i];
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         o[3] = pack_bf16x2(f[6], f[7]);
         return o;
     };
-    auto qcommit = [&](int set, char* kd, char* vd, float* ksd) __attribute__((always_inline)) {
+    auto qcommit = [&](int set, char* kd, char* vd, float* ksd, float* vsd) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kQSlots; ++j) {
             const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
@@ -238,11 +240,15 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
             const int seg = (c & 15) ^ rowperm(row);
             const bool high = (seg & 3) >= 2;          // 4-bit: values 16 .. 31 of the block
             *reinterpret_cast<u32x4*>(kd + 16 * c) = dequant8(kc[set][j], 1.f, high);   // codes, exact
-            *reinterpret_cast<u32x4*>(vd + 16 * c) = dequant8(vc[set][j], vscl[set][j], high);
-            if ((seg & 3) == 0) ksd[(seg >> 2) * kUnit + row] = kscl[set][j];
+            *reinterpret_cast<u32x4*>(vd + 16 * c) = dequant8(vc[set][j], 1.f, high);   // codes, exact
+            if ((seg & 3) == 0) {
+                ksd[(seg >> 2) * kUnit + row] = kscl[set][j];
+                vsd[(seg >> 2) * kUnit + row] = vscl[set][j];
+            }
         }
     };
-    const float* ks_cur = kscl_s[0];           // scales of the unit being computed (quantized K)
+    const float* ks_cur = kscl_s[0];           // scales of the unit being computed (quantized K, V)
+    const float* vs_cur = vscl_s[0];
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 acc[8];
@@ -291,6 +297,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         }
         // S^T = K Q^T; lane gets keys 32w + 16t + 4*l4 + r of head l16
         f32x4 st[2];
+        f32x4 vsc[kQ ? 4 : 1][2];                  // quantized V: scale of block b for this lane's keys
         if constexpr (kQ != 0) {
             // quantized K: slice ks is scale block ks of every key row, so each
             // slice's product is scaled per key; done before the release,
@@ -306,6 +313,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
                         st[t] += sc * part;
                     }
                 }
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        vsc[b][t] = *reinterpret_cast<const f32x4*>(vs_cur + b * kUnit + 32 * wave + 16 * t + 4 * l4);
             }
         }
         release();
@@ -342,15 +354,30 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         m_run = m_new;
         // P^T operand (B: k = key, n = head); k-slot 8*l4 + j holds key
         // 4*l4 + j (j < 4) or 16 + 4*l4 + (j - 4) of this wave's 32
-        u32x4 pw;
-        pw[0] = pack_bf16x2(pr[0], pr[1]);
-        pw[1] = pack_bf16x2(pr[2], pr[3]);
-        pw[2] = pack_bf16x2(pr[4], pr[5]);
-        pw[3] = pack_bf16x2(pr[6], pr[7]);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-        // O^T += V^T P^T
+        if constexpr (kQ == 0) {
+            u32x4 pw;
+            pw[0] = pack_bf16x2(pr[0], pr[1]);
+            pw[1] = pack_bf16x2(pr[2], pr[3]);
+            pw[2] = pack_bf16x2(pr[4], pr[5]);
+            pw[3] = pack_bf16x2(pr[6], pr[7]);
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            // O^T += V^T P^T
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[dt] = mfma_16x16x32_bf16(va[dt], pb, acc[dt] * alpha);
+            for (int dt = 0; dt < 8; ++dt) acc[dt] = mfma_16x16x32_bf16(va[dt], pb, acc[dt] * alpha);
+        } else {
+            // dims 32b .. 32b + 31 (tiles 2b, 2b + 1): P scaled by V's block-b scale per key
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                u32x4 pw;
+                pw[0] = pack_bf16x2(pr[0] * vsc[b][0][0], pr[1] * vsc[b][0][1]);
+                pw[1] = pack_bf16x2(pr[2] * vsc[b][0][2], pr[3] * vsc[b][0][3]);
+                pw[2] = pack_bf16x2(pr[4] * vsc[b][1][0], pr[5] * vsc[b][1][1]);
+                pw[3] = pack_bf16x2(pr[6] * vsc[b][1][2], pr[7] * vsc[b][1][3]);
+                const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+                for (int dt = 2 * b; dt < 2 * b + 2; ++dt) acc[dt] = mfma_16x16x32_bf16(va[dt], pb, acc[dt] * alpha);
+            }
+        }
     };
 
     // Two-unit ring: unit u + 1 streams in while unit u is computed.  Every
@@ -381,22 +408,23 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         // written to its buffer, freed at the release of unit u - 1, after the
         // math of unit u
         qload(0, 0);
-        qcommit(0, kbuf0, vbuf0, kscl_s[0]);
+        qcommit(0, kbuf0, vbuf0, kscl_s[0], vscl_s[0]);
         qload(1, 1);
-        auto qstep = [&](int u, int set, const char* kb, const char* vb, char* kn, char* vn, float* ksn)
-            __attribute__((always_inline)) {
+        auto qstep = [&](int u, int set, const char* kb, const char* vb, char* kn, char* vn, float* ksn,
+                         float* vsn) __attribute__((always_inline)) {
             ks_cur = kscl_s[set];
+            vs_cur = vscl_s[set];
             lds_barrier();                         // unit u is in LDS (written by every wave)
             compute(u, kb, vb, [&]() __attribute__((always_inline)) {
                 lds_barrier();                     // every wave has its operands and scales
                 if (u + 2 < kMaxUnits) qload(u + 2, set);
             });
-            if (u + 1 < kMaxUnits) qcommit(set ^ 1, kn, vn, ksn);
+            if (u + 1 < kMaxUnits) qcommit(set ^ 1, kn, vn, ksn, vsn);
         };
 #pragma unroll
         for (int u = 0; u < kMaxUnits; u += 2) {
-            qstep(u, 0, kbuf0, vbuf0, kbuf1, vbuf1, kscl_s[1]);
-            qstep(u + 1, 1, kbuf1, vbuf1, kbuf0, vbuf0, kscl_s[0]);
+            qstep(u, 0, kbuf0, vbuf0, kbuf1, vbuf1, kscl_s[1], vscl_s[1]);
+            qstep(u + 1, 1, kbuf1, vbuf1, kbuf0, vbuf0, kscl_s[0], vscl_s[0]);
         }
     }
 
