@@ -246,14 +246,14 @@ __global__ __launch_bounds__(256) void project_epilogue_kernel(PeArgs a) {
 }  // namespace
 
 // Slices of d_model for n_tok tokens (the launch uses at most d_model / 32):
-// a few token tiles split the hidden size finely, so that every workgroup
-// makes one or two load round trips (a decode batch of 32 tokens at d_model
-// 3072: 96 slices of 32); a full prefill chunk needs no split.
+// a few token tiles split the hidden size (a decode batch of 32 tokens at
+// d_model 3072: 32 slices of 96, 256 workgroups); a full prefill chunk needs
+// no split.  96 slices of 32 ran slower (more partial sums to write and add).
 int project_n_split(int64_t n_tok) {
     const int64_t tiles = (n_tok + kPjTm - 1) / kPjTm;
     if (tiles >= 64) return 1;
-    const int64_t s = 128 / (tiles > 0 ? tiles : 1);
-    return static_cast<int>(s < 1 ? 1 : (s > 128 ? 128 : s));
+    const int64_t s = 32 / (tiles > 0 ? tiles : 1);
+    return static_cast<int>(s < 1 ? 1 : s);
 }
 
 size_t project_ws_bytes(int64_t n_tok) {

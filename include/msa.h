@@ -205,7 +205,7 @@ typedef struct msa_proj {
  * the keys to the index cache at (d_stream[t], d_pos[t]) (f32, or fp16
  * rounded to nearest even, paged or not), i.e. it replaces the idx_k part of
  * msa_index_append.  d_x [n_tok][d_model] f32.  Products and sums in f32
- * (matrix cores), d_model split into at most 128 slices summed in a fixed
+ * (matrix cores), d_model split into at most 32 slices summed in a fixed
  * order.  Workspace: MSA_OP_INDEX_PROJECT with n_q = n_tok.
  * Errors: d_model not a positive multiple of 32, rot_dim odd or > 64, eps < 0
  * or rope_theta <= 0 -> MSA_ERR_UNSUPPORTED.  Device preconditions as

@@ -210,9 +210,9 @@ def test_index_project_validation(L):
     assert call(ok, n=0) == OK
     assert L.msa_index_project(ctypes.byref(d), ctypes.byref(c), None, A, A, A, 4, 100, A, A, 1 << 30, None) == NULL
     # workspace: splits of the hidden size x tokens x 1024 f32
-    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 32, 0) == 128 * 32 * 1024 * 4
+    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 32, 0) == 32 * 32 * 1024 * 4
     assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 4096, 0) == 1 * 4096 * 1024 * 4
-    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 1000, 0) == 8 * 1000 * 1024 * 4
+    assert M.workspace_bytes(d, M.MSA_OP_INDEX_PROJECT, 1000, 0) == 2 * 1000 * 1024 * 4
 
 
 def test_kv_format_validation(L):

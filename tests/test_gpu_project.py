@@ -119,7 +119,7 @@ def test_project_paged_equals_per_stream():
 
 def test_project_decode_32_tokens_d3072():
     """Decode shape: one token per stream at position 32767 (32 streams); the
-    hidden size is split 96 ways."""
+    hidden size is split 32 ways."""
     S, cap = 32, 32768
     log("[project] decode 32 tokens, d_model 3072")
     gq, gk, oq, ok, _ = _run(W.PROJ_D_MODEL, np.arange(S, dtype=np.int32), np.full(S, cap - 1, np.int32), S, cap)
