@@ -186,6 +186,16 @@ def make_cache(*, k: torch.Tensor, v: torch.Tensor, idx_k: Optional[torch.Tensor
     The descriptor holds references to the tensors, so their memory stays
     allocated while it lives."""
     kv_dtype = torch.bfloat16 if kv_format == KV_BF16 else torch.uint8
+    if kv_format != KV_BF16:
+        width = 128 if kv_format == KV_INT8 else 64
+        for name, t in (("k", k), ("v", v)):
+            if t is not None and t.shape[-1] != width:
+                raise ValueError(f"{name}: a kv_format {kv_format} cache holds {width} code bytes per group row")
+        for name, t, ref in (("k_scale", k_scale, k), ("v_scale", v_scale, v)):
+            if t is None or ref is None:
+                continue
+            if tuple(t.shape) != tuple(ref.shape[:-1]) + (4,):
+                raise ValueError(f"{name}: expected shape {tuple(ref.shape[:-1]) + (4,)} (one f32 per 32 values)")
     if block_table is None:
         S, cap_ = k.shape[0], k.shape[1]
         table, stride = None, 0
