@@ -5,7 +5,9 @@ codes, one f32 scale per 32 values) against the fp64 oracle, through the C ABI.
   decisions are taken in f32 on both sides).
 * Decode attention (MSA blocks and DSA token ids): against fp64 attention on
   the oracle's dequantized caches, to the attention tolerances (the kernel
-  rounds code * scale to bf16 before the products, as it rounds P).
+  multiplies exact codes: K's scales scale each 32-dim slice of the scores, V's
+  are folded into the bf16 probabilities, the one rounding, as in the bf16
+  path), for splits of 2, 4 and 8 units.
 * Paged quantized caches: bit-identical to per-stream ones.
 """
 import numpy as np
@@ -81,6 +83,32 @@ def test_kv_quant_msa_decode(fmt, name):
     with pytest.raises(M.MsaError):
         M.msa_attend_prefill(dims, cache, dev_bits(qs["q"][:1], torch.bfloat16), 0, 5, dev(o_sel[:1]), out,
                              ws)
+
+
+@pytest.mark.parametrize("fmt,name", FMTS)
+def test_kv_quant_msa_decode_eight_units_per_split(fmt, name):
+    """32 queries x 16 selected blocks: two splits of eight units each, the
+    kernel instance the 32 x 32K decode step runs."""
+    S, cap = 32, 4096
+    wl = W.Workload(f"kvq8_{name}", "msa_decode", S, cap, tuple(range(S)), tuple([cap - 1] * 16 + [2500] * 16))
+    log(f"[kv quant {name}] 32 queries, 8 units per split")
+    host, qs = W.caches(wl), W.queries(wl)
+    k, v, ks, vs = _alloc(S, cap, fmt)
+    idx = torch.zeros((S, cap, 4, 128), dtype=torch.float32, device=DEV)
+    dims = M.msa_dims(wl.top_k, W.SCALE)
+    cache = M.make_cache(k=k, v=v, idx_k=idx, kv_format=fmt, k_scale=ks, v_scale=vs)
+    _append_all(cache, host, S, cap, dims)
+    _, kd, vd = _oracle_caches(host, fmt)
+    _, o_sel, _ = oracle.msa_select(host["idx_k"], qs["stream"], qs["pos"], qs["idx_q"])
+    out = torch.empty((wl.n_q, 64, 128), device=DEV)
+    ws = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_ATTEND_DECODE, wl.n_q, wl.max_pos), 256),
+                     dtype=torch.uint8, device=DEV)
+    M.msa_attend_decode(dims, cache, dev_bits(qs["q"], torch.bfloat16), dev(qs["stream"]), dev(qs["pos"]),
+                        wl.max_pos, dev(o_sel), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_attend_f64(kd, vd, qs["stream"], qs["pos"], qs["q"], o_sel, unit=128, scale=W.SCALE)
+    wa, wr = check_attention(out.cpu().numpy(), ref)
+    log(f"  attention max-abs {wa:.3e}, rel-L2 {wr:.3e}")
 
 
 @pytest.mark.parametrize("fmt,name", FMTS)
