@@ -9,6 +9,21 @@ library raises.  Errors from the library are raised as MsaError carrying the
 msa_status code.
 
 Build the library in-tree first:  python -m block_sparse_attention_msa_amd.build
+
+One decode step of an MSA layer (32 streams, one new token each):
+
+    dims = msa_dims()                                   # 4 groups x 16 heads, top-16 of 128-key blocks
+    cache = make_cache(k=k, v=v, idx_k=idx_k)           # [S][cap][4][128] bf16 / f32 tensors
+    msa_index_append(dims, cache, stream, pos, max_pos, idx_k_new, k_new, v_new)
+    msa_select(dims, cache, idx_q, stream, pos, max_pos, sel, n_sel,
+               ws=torch.empty(workspace_bytes(dims, MSA_OP_SELECT, n_q, max_pos), dtype=torch.uint8, device="cuda"))
+    msa_attend_decode(dims, cache, q, stream, pos, max_pos, sel, out, ws_attend)
+
+A prefill chunk of one stream uses msa_select_prefill / msa_attend_prefill;
+msa_index_project turns hidden states into idx_q and appends idx_k; the DSA
+variant uses dsa_dims, dsa_index_append, dsa_select (or dsa_select_heads)
+and dsa_attend_decode.  make_cache also describes paged caches (block_table),
+an fp16 index cache (idx_k_f16) and int8 / 4-bit K/V (kv_format).
 """
 from __future__ import annotations
 
