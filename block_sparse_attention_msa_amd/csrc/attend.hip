@@ -118,8 +118,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     __shared__ __attribute__((aligned(16))) float kscl_s[2][kQ ? 4 * kUnit : 4];
     __shared__ __attribute__((aligned(16))) float vscl_s[2][kQ ? 4 * kUnit : 4];
 
-    const int64_t s = a.stream[i];
-    const int p = a.pos[i];
+    const int64_t s = a.stream ? a.stream[i] : a.stream0;
+    const int p = a.stream ? a.pos[i] : a.pos0 + static_cast<int>(i);
     const int32_t* sel = a.sel + i * static_cast<int64_t>(a.sel_len) * (kTokenIds ? 1 : kGroups) +
                          g * a.sel_g_stride;
     const uint16_t* kg = a.k + g * kHeadDim;   // cache row r at + r*kGroups*kHeadDim

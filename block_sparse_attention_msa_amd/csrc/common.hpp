@@ -195,6 +195,8 @@ struct AttendArgs {
     int kv_format;           // 0 bf16; 1 int8, 2 4-bit codes with f32 scales per 32 values
     const float* k_scale;    // [rows][kGroups][kHeadDim / 32] (quantized caches)
     const float* v_scale;
+    int32_t stream0;         // stream == NULL: query i is at (stream0, pos0 + i) (a prefill chunk)
+    int32_t pos0;
 };
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);

@@ -134,8 +134,8 @@ typedef struct msa_cache {
      * scale.  The append quantizes bf16 rows: s = max|x| / 127 (int8) or / 7
      * (4-bit), code = rint(x / s) in f32 (a reading: the pages give the
      * format, not the rule).  Supported by the appends and decode attention
-     * (msa_attend_decode, dsa_attend_decode); msa_attend_prefill returns
-     * MSA_ERR_UNSUPPORTED.  Other values -> MSA_ERR_UNSUPPORTED. */
+     * (msa_attend_decode, dsa_attend_decode, msa_attend_prefill).  Other
+     * values -> MSA_ERR_UNSUPPORTED. */
     int32_t kv_format;
     float* k_scale;
     float* v_scale;
@@ -309,9 +309,13 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
  * Same arguments and output as msa_attend_decode.  Cache rows up to
  * pos0 + n_q - 1 must be written (the chunk's own keys included).
  * Workspace: msa_workspace_bytes(dims, MSA_OP_ATTEND_PREFILL, n_q, max_pos)
- * bytes at d_ws (16-byte aligned; MSA_ERR_WORKSPACE_TOO_SMALL otherwise):
- * per tile of 32 consecutive queries and group, the ascending list of the
- * blocks their selections hold, built on the device before the sweep.
+ * bytes at d_ws (16-byte aligned; MSA_ERR_WORKSPACE_TOO_SMALL otherwise),
+ * the larger of two needs, whatever the cache format: bf16 caches keep, per
+ * tile of 32 consecutive queries and group, the ascending list of the blocks
+ * their selections hold, built on the device before the sweep; quantized
+ * caches (kv_format 1, 2) run the queries through decode attention in
+ * launches of at most 256 consecutive queries, whose split partials the
+ * workspace holds (launches on one stream, so they reuse it in turn).
  */
 MSA_API msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
                               int32_t stream, int32_t pos0, int64_t n_q, const int32_t* d_sel,

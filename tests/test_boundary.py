@@ -224,7 +224,9 @@ def test_kv_format_validation(L):
     assert att(mk(2, A, MIS)) == ALIGN
     assert att(mk(1, A, A)) not in (NULL, ALIGN, SHAPE, UNSUP)     # accepted (fails later only for want of a GPU)
     pre = lambda c: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 0, 10, A, A, A, 1 << 30, None)
-    assert pre(mk(1, A, A)) == UNSUP and pre(mk(0, None, None)) not in (NULL, ALIGN, SHAPE, UNSUP)
+    assert pre(mk(1, A, A)) not in (NULL, ALIGN, SHAPE, UNSUP)     # accepted (fails later only for want of a GPU)
+    assert pre(mk(0, None, None)) not in (NULL, ALIGN, SHAPE, UNSUP)
+    assert pre(mk(2, None, A)) == NULL and pre(mk(3, A, A)) == UNSUP
 
 
 def test_topk_block_limit(L):
@@ -248,11 +250,27 @@ def test_workspace_sizes(L):
     # attention partials: per (query, group, split) 16 heads x (128 + 2) floats
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
-    # prefill attention: per (32-query tile, group) a step count (256-byte
-    # aligned array) and up to 32 * top_k 16-byte step entries
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 4096, 32767) == 2048 + 512 * 32 * 16 * 16
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 1, 100) == 256 + 4 * 32 * 16 * 16
-    assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 33, 100) == 256 + 8 * 32 * 16 * 16
+    # prefill attention, the larger of: bf16 caches, per (32-query tile,
+    # group) a step count (256-byte aligned array) and up to 32 * top_k
+    # 16-byte step entries; quantized caches, the decode split partials
+    # (16 heads x 130 floats per query, group and split) of a launch of at
+    # most 256 queries, or of the ragged last launch.
+    def splits(n, units=16):        # about 256 workgroups, at most 8 units per split
+        return max(min(-(-256 // (4 * n)), units), -(-units // 8))
+
+    def partials(n):
+        return n * 4 * splits(n) * 16 * 130 * 4
+
+    def prefill(n):
+        steps = -(-(-(-n // 32) * 4 * 4) // 256) * 256 + -(-n // 32) * 4 * 32 * 16 * 16
+        tail = partials(n % 256) if n > 256 and n % 256 else 0
+        return max(steps, -(-max(partials(min(n, 256)), tail) // 256) * 256)
+
+    assert prefill(4096) == 256 * 4 * 2 * 8320          # split partials of 256 queries
+    assert prefill(1) == 16 * 4 * 8320                  # one query: 16 splits of one block
+    assert 2048 + 512 * 32 * 16 * 16 < prefill(4096)
+    for n in (1, 33, 100, 256, 257, 300, 4096, 4100):
+        assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, 32767) == prefill(n), n
     dd = M.dsa_dims()
     assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
     with pytest.raises(M.MsaError):

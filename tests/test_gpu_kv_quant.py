@@ -8,6 +8,8 @@ codes, one f32 scale per 32 values) against the fp64 oracle, through the C ABI.
   multiplies exact codes: K's scales scale each 32-dim slice of the scores, V's
   are folded into the bf16 probabilities, the one rounding, as in the bf16
   path), for splits of 2, 4 and 8 units.
+* Prefill attention (msa_attend_prefill) on quantized caches: the same
+  tolerances, and bit-identical to the decode entry on the same queries.
 * Paged quantized caches: bit-identical to per-stream ones.
 """
 import numpy as np
@@ -79,10 +81,39 @@ def test_kv_quant_msa_decode(fmt, name):
     ref = oracle.sparse_attend_f64(kd, vd, qs["stream"], qs["pos"], qs["q"], o_sel, unit=128, scale=W.SCALE)
     wa, wr = check_attention(out.cpu().numpy(), ref)
     log(f"  codes and scales bit-exact; attention max-abs {wa:.3e}, rel-L2 {wr:.3e}")
-    # prefill attention does not take quantized caches
-    with pytest.raises(M.MsaError):
-        M.msa_attend_prefill(dims, cache, dev_bits(qs["q"][:1], torch.bfloat16), 0, 5, dev(o_sel[:1]), out,
-                             ws)
+
+
+@pytest.mark.parametrize("fmt,name", FMTS)
+def test_kv_quant_msa_prefill(fmt, name):
+    """A prefill chunk of 300 consecutive queries (two launches of the decode
+    kernel: 256, then a ragged 44) over a quantized cache whose capacity is
+    not a multiple of 128."""
+    wl = W.prefill_workload(f"kvq_pf_{name}", 3000, 1900, 300)
+    log(f"[kv quant {name}] msa prefill: cap={wl.cap} pos0={wl.pos[0]} n_q={wl.n_q}")
+    host, qs = W.caches(wl), W.queries(wl)
+    S, cap = wl.n_stream, wl.cap
+    k, v, ks, vs = _alloc(S, cap, fmt)
+    idx = torch.zeros((S, cap, 4, 128), dtype=torch.float32, device=DEV)
+    dims = M.msa_dims(wl.top_k, W.SCALE)
+    cache = M.make_cache(k=k, v=v, idx_k=idx, kv_format=fmt, k_scale=ks, v_scale=vs)
+    _append_all(cache, host, S, cap, dims)
+    _, kd, vd = _oracle_caches(host, fmt)
+    _, o_sel, _ = oracle.msa_select(host["idx_k"], qs["stream"], qs["pos"], qs["idx_q"])
+    q = dev_bits(qs["q"], torch.bfloat16)
+    out = torch.empty((wl.n_q, 64, 128), device=DEV)
+    ws = torch.empty(M.workspace_bytes(dims, M.MSA_OP_ATTEND_PREFILL, wl.n_q, wl.max_pos), dtype=torch.uint8,
+                     device=DEV)
+    M.msa_attend_prefill(dims, cache, q, wl.stream[0], wl.pos[0], dev(o_sel), out, ws)
+    # the decode entry on the same queries (one launch, the same split count)
+    out_d = torch.empty_like(out)
+    ws_d = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_ATTEND_DECODE, wl.n_q, wl.max_pos), 256),
+                       dtype=torch.uint8, device=DEV)
+    M.msa_attend_decode(dims, cache, q, dev(qs["stream"]), dev(qs["pos"]), wl.max_pos, dev(o_sel), out_d, ws_d)
+    torch.cuda.synchronize()
+    ref = oracle.sparse_attend_f64(kd, vd, qs["stream"], qs["pos"], qs["q"], o_sel, unit=128, scale=W.SCALE)
+    wa, wr = check_attention(out.cpu().numpy(), ref)
+    log(f"  attention max-abs {wa:.3e}, rel-L2 {wr:.3e}")
+    assert torch.equal(out.cpu(), out_d.cpu())
 
 
 @pytest.mark.parametrize("fmt,name", FMTS)
