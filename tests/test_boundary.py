@@ -227,6 +227,11 @@ def test_kv_format_validation(L):
     assert pre(mk(1, A, A)) not in (NULL, ALIGN, SHAPE, UNSUP)     # accepted (fails later only for want of a GPU)
     assert pre(mk(0, None, None)) not in (NULL, ALIGN, SHAPE, UNSUP)
     assert pre(mk(2, None, A)) == NULL and pre(mk(3, A, A)) == UNSUP
+    # the quantized path checks the same workspace amount
+    need = M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, 10, 9)
+    pw = lambda c, n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 0, 10, A, A, A, n, None)
+    assert pw(mk(1, A, A), need - 1) == WS and pw(mk(2, A, A), need - 1) == WS
+    assert pw(mk(1, A, A), need) != WS
 
 
 def test_topk_block_limit(L):

@@ -169,6 +169,8 @@ def test_kv_quant_dsa_decode(fmt, name):
 
 
 def test_kv_quant_paged_equals_per_stream():
+    """Decode and prefill attention over a paged int8 cache (blocks placed by a
+    random table) are bit-identical to those over per-stream caches."""
     fmt = M.KV_INT8
     wl = W.Workload("kvq_paged", "msa_decode", 2, 3000, (0, 1, 1), (2999, 2000, 128))
     log("[kv quant] paged vs per-stream")
@@ -180,6 +182,11 @@ def test_kv_quant_paged_equals_per_stream():
     n_pages = S * nb + 2
     dims = M.msa_dims(wl.top_k, W.SCALE)
     _, o_sel, _ = oracle.msa_select(host["idx_k"], qs["stream"], qs["pos"], qs["idx_q"])
+    pwl = W.prefill_workload("kvq_paged_pf", cap, 1700, 300, stream=1, n_stream=S)
+    pqs = W.queries(pwl)
+    _, p_sel, _ = oracle.msa_select(host["idx_k"], pqs["stream"], pqs["pos"], pqs["idx_q"])
+    pre_q = {paged: {"q": dev_bits(pqs["q"], torch.bfloat16), "sel": dev(p_sel),
+                     "out": torch.empty((300, 64, 128), device=DEV)} for paged in (False, True)}
     outs = []
     for paged in (False, True):
         if paged:
@@ -200,6 +207,13 @@ def test_kv_quant_paged_equals_per_stream():
                          dtype=torch.uint8, device=DEV)
         M.msa_attend_decode(dims, cache, dev_bits(qs["q"], torch.bfloat16), dev(qs["stream"]), dev(qs["pos"]),
                             wl.max_pos, dev(o_sel), out, ws)
+        # a prefill chunk of stream 1 (positions 1700 .. 1999) through the
+        # quantized prefill path, whose rows also resolve through the table
+        pre = pre_q[paged]
+        ws_p = torch.empty(M.workspace_bytes(dims, M.MSA_OP_ATTEND_PREFILL, 300, 1999), dtype=torch.uint8,
+                           device=DEV)
+        M.msa_attend_prefill(dims, cache, pre["q"], 1, 1700, pre["sel"], pre["out"], ws_p)
         torch.cuda.synchronize()
-        outs.append(out.cpu())
-    assert torch.equal(outs[0], outs[1])
+        outs.append((out.cpu(), pre["out"].cpu()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
