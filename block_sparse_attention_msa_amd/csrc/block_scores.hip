@@ -7,7 +7,7 @@
 // This file holds the decode form; the prefill form (matrix cores) is in
 // prefill_scores.hip.
 //
-// Decode: one workgroup per (query, two key blocks).  The F32 index-key cache is
+// Decode: one workgroup per (query, two key blocks; eight for an fp16 cache).  The F32 index-key cache is
 // streamed once with 128-bit loads; each 16-lane DPP row of a wavefront owns
 // one group's 512-byte slice of a token row, so a token's four group scores
 // come out of one DPP row reduction each and no scores are materialised.  An
@@ -25,9 +25,9 @@ constexpr int kRowF4 = kGroups * kIdxDim / 4;   // 128 float4 per token row
 // ---------------------------------------------------------------------------
 // Decode scan
 // ---------------------------------------------------------------------------
-constexpr int kScanBlocksPerWg = 2;                       // key blocks per workgroup
+constexpr int kScanWaves = 8;                                        // 512 threads
 constexpr int kScanWavesPerBlock = 4;
-constexpr int kScanWaves = kScanBlocksPerWg * kScanWavesPerBlock;   // 8 waves, 512 threads
+constexpr int kScanBlocksPerWg = kScanWaves / kScanWavesPerBlock;   // 2 key blocks per workgroup
 constexpr int kScanTokensPerWave = kBlock / kScanWavesPerBlock;     // 32
 constexpr int kScanUnroll = 8;
 
@@ -122,19 +122,27 @@ __device__ __forceinline__ float dot8h(const f32x4& q0, const f32x4& q1, const u
     return d;
 }
 
+// One wave per key block in the fp16 scan: a wave streams the block's 128
+// token rows (128 KiB), a workgroup eight blocks.  With four waves per block
+// (32 KiB per wave, the f32 scan's split) the scan ran 4.6 % slower at 32
+// streams x 32K; the f32 scan is fastest with four.
+constexpr int kScan16WavesPerBlock = 1;
+constexpr int kScan16BlocksPerWg = kScanWaves / kScan16WavesPerBlock;
+constexpr int kScan16TokensPerWave = kBlock / kScan16WavesPerBlock;
+
 __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kernel(
     const uint16_t* __restrict__ idx_k, Pager pg, const float* __restrict__ idx_q,
     const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
     float* __restrict__ bs, int64_t nblk_stride, int nblk) {
     const int64_t i = blockIdx.x;
-    const int b0 = blockIdx.y * kScanBlocksPerWg;
+    const int b0 = blockIdx.y * kScan16BlocksPerWg;
     const int p = q_pos[i];
     const int loc = p / kBlock;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar table reads
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int b = b0 + wave / kScanWavesPerBlock;
+    const int b = b0 + wave / kScan16WavesPerBlock;
     float m = -INFINITY;
     if (b < nblk && b <= loc) {
         const f32x4* qrow = reinterpret_cast<const f32x4*>(idx_q + i * kGroups * kIdxDim);
@@ -142,8 +150,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kerne
         const f32x4 q1 = qrow[g * 32 + 2 * c + 1];      // dims 8c+4 .. 8c+7
         const u32x4* rows = reinterpret_cast<const u32x4*>(
             idx_k + pg.block_row_uniform(q_stream[i], b) * (kGroups * kIdxDim)) + g * 16 + c;
-        const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
-        const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+        const int t_begin = (wave % kScan16WavesPerBlock) * kScan16TokensPerWave;
+        const int t_end = min(t_begin + kScan16TokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
         int t = t_begin;
         for (; t + kScanUnroll16 <= t_end; t += kScanUnroll16) {
             u32x4 a[kScanUnroll16];
@@ -157,14 +165,14 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kerne
     __shared__ float red[kScanWaves][kGroups];
     if (c == 0) red[wave][g] = m;
     __syncthreads();
-    if (threadIdx.x < kGroups * kScanBlocksPerWg) {
+    if (threadIdx.x < kGroups * kScan16BlocksPerWg) {
         const int gg = threadIdx.x % kGroups;
         const int bl = threadIdx.x / kGroups;
         const int bb2 = b0 + bl;
         if (bb2 < nblk) {
             float r = -INFINITY;    // stays -inf for blocks past the query's own block
 #pragma unroll
-            for (int w = 0; w < kScanWavesPerBlock; ++w) r = fmaxf(r, red[bl * kScanWavesPerBlock + w][gg]);
+            for (int w = 0; w < kScan16WavesPerBlock; ++w) r = fmaxf(r, red[bl * kScan16WavesPerBlock + w][gg]);
             bs[(i * kGroups + gg) * nblk_stride + bb2] = r;
         }
     }
@@ -176,8 +184,9 @@ hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, co
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
                                       int64_t nblk_stride, hipStream_t s) {
     const unsigned ny = static_cast<unsigned>((nblk + kScanBlocksPerWg - 1) / kScanBlocksPerWg);
+    const unsigned ny16 = static_cast<unsigned>((nblk + kScan16BlocksPerWg - 1) / kScan16BlocksPerWg);
     if (c.idx_k16)
-        hipLaunchKernelGGL(block_scores_decode_f16_kernel, dim3(static_cast<unsigned>(n_q), ny),
+        hipLaunchKernelGGL(block_scores_decode_f16_kernel, dim3(static_cast<unsigned>(n_q), ny16),
                            dim3(64 * kScanWaves), 0, s, c.idx_k16, c.pg, idx_q, stream, pos, bs, nblk_stride, nblk);
     else
         hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
