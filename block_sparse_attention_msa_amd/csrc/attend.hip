@@ -525,6 +525,7 @@ void launch_units(const KernelArgs& ka, bool blocks, int nu, dim3 grid, hipStrea
 
 int attend_num_splits(int64_t n_q, int sel_len, int unit) {
     const int64_t pairs = n_q * kGroups;
+    if (pairs <= 0) return 1;   // an empty call: nothing is split
     const int n_units = num_units(sel_len, unit);
     // about one workgroup per compute unit (256), each streaming >= 1 unit,
     // and at most kUnitsPerSplitMax units per split
@@ -537,6 +538,7 @@ int attend_num_splits(int64_t n_q, int sel_len, int unit) {
 }
 
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit) {
+    if (n_q <= 0) return 0;
     const int n_split = attend_num_splits(n_q, sel_len, unit);
     if (n_split == 1) return 0;
     return static_cast<size_t>(n_q) * kGroups * n_split * kPartFloats * sizeof(float);

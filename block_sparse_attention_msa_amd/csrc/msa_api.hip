@@ -157,6 +157,8 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
     if (n_q < 0 || max_pos < 0) return bad;
     const bool dsa = op == DSA_OP_SELECT || op == DSA_OP_ATTEND_DECODE;
     if (check_dims(dims, dsa ? Mode::Dsa : Mode::Msa) != MSA_OK) return bad;
+    if (op < MSA_OP_SELECT || op > MSA_OP_INDEX_PROJECT) return bad;
+    if (n_q == 0) return 0;   // an empty call launches nothing and needs no workspace
     switch (op) {
         case MSA_OP_SELECT:
             if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;

@@ -155,8 +155,8 @@ typedef enum msa_op {
 
 /* Bytes of workspace `op` needs for n_q queries whose positions are all
  * <= max_pos (msa_select_prefill / msa_attend_prefill: max_pos = pos0 +
- * n_q - 1).  Returns 0 when the op needs no workspace and (size_t)-1 for an
- * unsupported geometry, op or size. */
+ * n_q - 1).  Returns 0 when the op needs no workspace (always for n_q == 0,
+ * an empty call) and (size_t)-1 for an unsupported geometry, op or size. */
 MSA_API size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t max_pos);
 
 /* Human-readable name of a status code (static storage). */

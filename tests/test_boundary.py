@@ -280,3 +280,17 @@ def test_workspace_sizes(L):
     assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
     with pytest.raises(M.MsaError):
         M.workspace_bytes(d, M.DSA_OP_SELECT, 16, 65535)   # DSA op needs DSA dims
+
+
+def test_workspace_of_an_empty_call_is_zero(L):
+    """n_q == 0 is a valid empty call for every op: its workspace query
+    returns 0 bytes (it used to divide by the number of (query, group)
+    pairs on the host)."""
+    d, dd = M.msa_dims(), M.dsa_dims()
+    msa_ops = (M.MSA_OP_SELECT, M.MSA_OP_SELECT_PREFILL, M.MSA_OP_ATTEND_DECODE, M.MSA_OP_ATTEND_PREFILL,
+               M.MSA_OP_BLOCK_SCORES_PREFILL, M.MSA_OP_INDEX_PROJECT)
+    for op in msa_ops:
+        for max_pos in (0, 127, 32767):
+            assert M.workspace_bytes(d, op, 0, max_pos) == 0, (op, max_pos)
+    for op in (M.DSA_OP_SELECT, M.DSA_OP_ATTEND_DECODE):
+        assert M.workspace_bytes(dd, op, 0, 65535) == 0, op
