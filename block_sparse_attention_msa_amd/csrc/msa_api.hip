@@ -134,6 +134,29 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
                                          quant ? nullptr : d_v_new, st));
 }
 
+
+// msa_select's checks and launches; the block scores go to the workspace.
+msa_status select_impl(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                       const int32_t* d_stream, const int32_t* d_pos, int64_t n_q, int32_t max_pos,
+                       int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
+    if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
+    const size_t need = select_ws(n_q, max_pos);
+    MSA_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    float* bs = static_cast<float*>(d_ws);
+    const int nblk = nblk_of(max_pos);
+    MSA_TRY(hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q, nblk,
+                                                       bs, nblk, s)));
+    return hip_status(msa::launch_topk_blocks(bs, nblk, d_pos, n_q, nblk, dims->top_k, d_sel, d_n_sel, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,7 +178,8 @@ const char* msa_status_string(msa_status s) {
 size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t max_pos) {
     const size_t bad = static_cast<size_t>(-1);
     if (n_q < 0 || max_pos < 0) return bad;
-    const bool dsa = op == DSA_OP_SELECT || op == DSA_OP_ATTEND_DECODE;
+    const bool dsa = op == DSA_OP_SELECT || op == DSA_OP_ATTEND_DECODE ||
+                     (op == MSA_OP_ATTEND_DECODE && dims && dims->block == 1);
     if (check_dims(dims, dsa ? Mode::Dsa : Mode::Msa) != MSA_OK) return bad;
     if (op < MSA_OP_SELECT || op > MSA_OP_INDEX_PROJECT) return bad;
     if (n_q == 0) return 0;   // an empty call launches nothing and needs no workspace
@@ -169,7 +193,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
         case MSA_OP_BLOCK_SCORES_PREFILL:
             return align256(msa::prefill_scores_ws_bytes(max_pos));
         case MSA_OP_ATTEND_DECODE:
-            return align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
+            return align256(msa::attend_ws_bytes(n_q, dims->top_k, dims->block));
         case MSA_OP_ATTEND_PREFILL: {
             // the larger of the bf16 path's and the quantized-cache path's needs
             const size_t a = align256(msa::prefill_attend_ws_bytes(n_q, dims->top_k));
@@ -257,21 +281,8 @@ msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float*
                       const int32_t* d_stream, const int32_t* d_pos, int64_t n_q, int32_t max_pos,
                       int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes,
                       void* hip_stream) {
-    MSA_TRY(check_dims(dims, Mode::Msa));
-    MSA_TRY(check_cache(cache));
-    MSA_TRY(check_count_pos(n_q, max_pos, cache));
-    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
-    MSA_TRY(check_index_cache(cache));
-    MSA_TRY(check_ptrs({d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
-    if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
-    MSA_TRY(check_ptrs({d_ws}));
-    if (ws_bytes < select_ws(n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
-    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    float* bs = static_cast<float*>(d_ws);
-    const int nblk = nblk_of(max_pos);
-    MSA_TRY(hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q, nblk,
-                                                       bs, nblk, s)));
-    return hip_status(msa::launch_topk_blocks(bs, nblk, d_pos, n_q, nblk, dims->top_k, d_sel, d_n_sel, s));
+    return select_impl(dims, cache, d_idx_q, d_stream, d_pos, n_q, max_pos, d_sel, d_n_sel, d_ws, ws_bytes,
+                       hip_stream);
 }
 
 msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
@@ -325,6 +336,10 @@ msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
                              const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
                              int32_t max_pos, const int32_t* d_sel, float* d_out, void* d_ws,
                              size_t ws_bytes, void* hip_stream) {
+    // block 1: token ids shared by the groups (the DSA selection)
+    if (dims && dims->block == 1)
+        return dsa_attend_decode(dims, cache, d_q, d_stream, d_pos, n_q, max_pos, d_sel, d_out, d_ws, ws_bytes,
+                                 hip_stream);
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));

@@ -293,7 +293,11 @@ MSA_API msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cac
  * states are merged in a fixed order.
  *   d_q [n_q][n_group*heads_per_group][head_dim] bf16;
  *   d_sel as msa_select writes it; d_out [n_q][n_group*heads_per_group]
- *   [head_dim] f32.  Workspace: MSA_OP_ATTEND_DECODE.
+ *   [head_dim] f32.  Workspace: MSA_OP_ATTEND_DECODE (sized for the same
+ *   dims).
+ * Token-granular ids ([DSA-PR] "What this does"): with dims->block == 1
+ * (and 1 <= top_k <= 4096) d_sel [n_q][top_k] holds token ids shared by all
+ * groups, as dsa_select writes them, and the call is dsa_attend_decode.
  * Device precondition: at least one selected key per (query, group) (the
  * local block always provides key pos's block start).
  */
@@ -372,7 +376,9 @@ MSA_API msa_status dsa_select_heads(const msa_dims* dims, const msa_cache* cache
 /*
  * [DSA-PR] "What this does": attention over the kept keys only.  As
  * msa_attend_decode, but d_sel [n_q][top_k] holds token ids shared by all
- * groups (dims->block must be 1).  Workspace: DSA_OP_ATTEND_DECODE.
+ * groups (dims->block must be 1); msa_attend_decode with block 1 is this
+ * call.  Workspace: DSA_OP_ATTEND_DECODE (or MSA_OP_ATTEND_DECODE with the
+ * same dims: the same size).
  */
 MSA_API msa_status dsa_attend_decode(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
                              const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,

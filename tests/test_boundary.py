@@ -294,3 +294,22 @@ def test_workspace_of_an_empty_call_is_zero(L):
             assert M.workspace_bytes(d, op, 0, max_pos) == 0, (op, max_pos)
     for op in (M.DSA_OP_SELECT, M.DSA_OP_ATTEND_DECODE):
         assert M.workspace_bytes(dd, op, 0, 65535) == 0, op
+
+
+def test_attend_decode_takes_token_ids(L):
+    """msa_attend_decode with dims.block == 1 is the token-id (DSA) form:
+    its dims are validated as DSA dims and its workspace is the DSA one."""
+    c = _cache()
+    dd = M.dsa_dims(2048)
+    n_ws = M.workspace_bytes(dd, M.DSA_OP_ATTEND_DECODE, 16, 65535)
+    assert M.workspace_bytes(dd, M.MSA_OP_ATTEND_DECODE, 16, 65535) == n_ws
+    big = _cache(cap=65536, n_stream=16)
+    args = lambda ws, wsb, d: [ctypes.byref(d), ctypes.byref(big), A, A, A, 16, 65535, A, B, ws, wsb, None]
+    # past the dims check: a short workspace is reported, as by dsa_attend_decode
+    if n_ws:
+        assert L.msa_attend_decode(*args(A, n_ws - 1, dd)) == WS
+        assert L.dsa_attend_decode(*args(A, n_ws - 1, dd)) == WS
+    bad = M.Dims(4, 16, 128, 128, 1, 4097, 0.08)
+    assert L.msa_attend_decode(*args(A, 1 << 40, bad)) == UNSUP
+    # block 128 still needs an MSA top_k
+    assert L.msa_attend_decode(*args(A, 1 << 40, M.Dims(4, 16, 128, 128, 128, 2048, 0.08))) == UNSUP

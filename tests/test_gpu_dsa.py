@@ -45,9 +45,15 @@ def _dsa_parity(wl: W.Workload, host=None):
                             gw.ws(dims, M.DSA_OP_ATTEND_DECODE))
         return out.cpu().numpy()
 
-    wa, wr = check_attention(attend(dev(o_sel)), o_out)
+    out_o = attend(dev(o_sel))
+    wa, wr = check_attention(out_o, o_out)
     log(f"  attention on the oracle selection: max-abs {wa:.3e}, rel-L2 {wr:.3e}")
     check_attention(attend(sel), o_out, mask_qg=np.repeat(equal[:, None], 4, 1))
+    # msa_attend_decode with block 1 is the same call
+    out_m = torch.empty((wl.n_q, 64, 128), dtype=torch.float32, device=DEV)
+    M.msa_attend_decode(dims, gw.cache, gw.q, gw.stream, gw.pos, wl.max_pos, dev(o_sel), out_m,
+                        gw.ws(dims, M.MSA_OP_ATTEND_DECODE))
+    assert np.array_equal(out_m.cpu().numpy(), out_o)
 
 
 def test_dsa_small_ragged():
