@@ -52,7 +52,7 @@ EXPORTS = (
     "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",
     "msa_topk_blocks", "msa_select", "msa_block_scores_prefill", "msa_select_prefill",
     "msa_attend_decode", "msa_attend_prefill", "dsa_index_append", "dsa_select",
-    "dsa_select_heads", "dsa_attend_decode", "msa_index_project",
+    "dsa_select_heads", "dsa_attend_decode", "msa_index_project", "msa_select_static",
 )
 
 
@@ -120,6 +120,7 @@ def lib() -> ctypes.CDLL:
             "msa_block_scores": [D, C, P, P, P, I64, I32, P, I64, P],
             "msa_topk_blocks": [D, P, I64, P, I64, I32, P, P, P],
             "msa_select": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "msa_select_static": [D, C, P, P, P, I64, I32, P, P, P],
             "msa_block_scores_prefill": [D, C, P, I32, I32, I64, P, I64, P, ctypes.c_size_t, P],
             "msa_select_prefill": [D, C, P, I32, I32, I64, P, P, P, ctypes.c_size_t, P],
             "msa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
@@ -290,6 +291,19 @@ def msa_select(dims, cache, idx_q, stream, pos, max_pos, sel, n_sel, ws, hip_str
                             _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
                             _p(sel, torch.int32), _p(n_sel, torch.int32), wp, wn, _stream(hip_stream)),
            "msa_select")
+
+
+def msa_select_static(dims, cache, idx_q, stream, pos, max_pos, sel, n_sel, hip_stream=None):
+    """msa_select without a workspace: the block scores stay in the library's
+    per-device array (MSA_STATIC_SCRATCH_BYTES); calls on one GPU must not
+    overlap."""
+    _check(lib().msa_select_static(ctypes.byref(dims), ctypes.byref(cache), _p(idx_q, torch.float32),
+                                   _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
+                                   _p(sel, torch.int32), _p(n_sel, torch.int32), _stream(hip_stream)),
+           "msa_select_static")
+
+
+MSA_STATIC_SCRATCH_BYTES = 4 << 20
 
 
 def msa_block_scores_prefill(dims, cache, idx_q, stream_id, pos0, bs, ws, hip_stream=None):

@@ -5,6 +5,9 @@
 #include "../../include/msa.h"
 #include "common.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace {
 
 using msa::kBlock;
@@ -135,10 +138,43 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
 }
 
 
-// msa_select's checks and launches; the block scores go to the workspace.
+// ---------------------------------------------------------------------------
+// msa_select without a caller workspace (msa_select_static): the block scores
+// live in a library-owned device array of MSA_STATIC_SCRATCH_BYTES.  Each GPU
+// holds its own copy at its own address, resolved once per device with
+// hipGetSymbolAddress; host code uses only that address (the array's name is
+// a host-side stand-in, not a device address).  Every call on a GPU shares
+// that GPU's array, so calls that overlap on one GPU race.  The block scores
+// need no clearing: the scan writes every entry the top-k reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+msa_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_HIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSA_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MSA_OK;
+}
+
+// msa_select's checks and launches; the block scores go to the workspace, or
+// (use_static) to this device's scratch array.
 msa_status select_impl(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
                        const int32_t* d_stream, const int32_t* d_pos, int64_t n_q, int32_t max_pos,
-                       int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes, void* hip_stream) {
+                       int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes, bool use_static,
+                       void* hip_stream) {
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     MSA_TRY(check_count_pos(n_q, max_pos, cache));
@@ -147,8 +183,13 @@ msa_status select_impl(const msa_dims* dims, const msa_cache* cache, const float
     MSA_TRY(check_ptrs({d_idx_q, d_stream, d_pos, d_sel, d_n_sel}));
     if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     const size_t need = select_ws(n_q, max_pos);
-    MSA_TRY(check_ptrs({d_ws}));
-    if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    if (use_static) {
+        if (need > MSA_STATIC_SCRATCH_BYTES) return MSA_ERR_WORKSPACE_TOO_SMALL;
+        MSA_TRY(scratch_of_current_device(&d_ws));
+    } else {
+        MSA_TRY(check_ptrs({d_ws}));
+        if (ws_bytes < need) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    }
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     float* bs = static_cast<float*>(d_ws);
     const int nblk = nblk_of(max_pos);
@@ -282,6 +323,13 @@ msa_status msa_select(const msa_dims* dims, const msa_cache* cache, const float*
                       int32_t* d_sel, int32_t* d_n_sel, void* d_ws, size_t ws_bytes,
                       void* hip_stream) {
     return select_impl(dims, cache, d_idx_q, d_stream, d_pos, n_q, max_pos, d_sel, d_n_sel, d_ws, ws_bytes,
+                       false, hip_stream);
+}
+
+msa_status msa_select_static(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                             const int32_t* d_stream, const int32_t* d_pos, int64_t n_q, int32_t max_pos,
+                             int32_t* d_sel, int32_t* d_n_sel, void* hip_stream) {
+    return select_impl(dims, cache, d_idx_q, d_stream, d_pos, n_q, max_pos, d_sel, d_n_sel, nullptr, 0, true,
                        hip_stream);
 }
 

@@ -258,6 +258,28 @@ MSA_API msa_status msa_select(const msa_dims* dims, const msa_cache* cache, cons
                       int32_t max_pos, int32_t* d_sel, int32_t* d_n_sel,
                       void* d_ws, size_t ws_bytes, void* hip_stream);
 
+/* Size of the device array msa_select_static keeps its block scores in. */
+#define MSA_STATIC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/*
+ * For callers that cannot allocate or pass a workspace (code under HIP graph
+ * capture, serving loops that forbid allocation): msa_select with its block
+ * scores kept in a library-owned device array of MSA_STATIC_SCRATCH_BYTES
+ * (4 MiB) instead of d_ws.  Same arguments otherwise, same results.  The
+ * call allocates nothing.  Limit: n_q * n_group * (max_pos / block + 1) * 4
+ * bytes must fit the array (e.g. 1024 queries at 32K context, 256 queries at
+ * 128K), else MSA_ERR_WORKSPACE_TOO_SMALL and nothing is launched.  Each GPU
+ * the library runs on holds its own array until the process ends; its
+ * address is resolved on the first call on that device (make that first call
+ * outside a stream capture).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams, other threads) race and
+ * must be ordered by the caller.  MSA_ERR_HIP if the array cannot be
+ * resolved.
+ */
+MSA_API msa_status msa_select_static(const msa_dims* dims, const msa_cache* cache, const float* d_idx_q,
+                                     const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
+                                     int32_t max_pos, int32_t* d_sel, int32_t* d_n_sel, void* hip_stream);
+
 /*
  * Prefill form of msa_block_scores ([MSA-PR] Implementation, batch path;
  * [MSA-LOG] unified selection semantics): n_q consecutive queries at

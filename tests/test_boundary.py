@@ -313,3 +313,21 @@ def test_attend_decode_takes_token_ids(L):
     assert L.msa_attend_decode(*args(A, 1 << 40, bad)) == UNSUP
     # block 128 still needs an MSA top_k
     assert L.msa_attend_decode(*args(A, 1 << 40, M.Dims(4, 16, 128, 128, 128, 2048, 0.08))) == UNSUP
+
+
+def test_select_static_limits(L):
+    """msa_select_static validates like msa_select and rejects, before any
+    launch, a call whose block scores do not fit the library's array."""
+    d = M.msa_dims()
+    c = _cache(cap=1 << 20, n_stream=4)
+    call = lambda n_q, max_pos, **kw: L.msa_select_static(ctypes.byref(d), ctypes.byref(c), kw.get("idx_q", A),
+                                                          A, A, n_q, max_pos, A, B, None)
+    limit = M.MSA_STATIC_SCRATCH_BYTES
+    assert limit == 4 << 20
+    # 1025 queries at 32K context: 1025 * 4 * 256 * 4 B > 4 MiB
+    assert call(1025, 32767) == WS
+    assert call(257, 131071) == WS
+    assert call(1, 4095, idx_q=None) == NULL
+    assert call(1, 4095, idx_q=MIS) == ALIGN
+    assert call(0, 4095) == OK
+    assert call(1, 1 << 20) == RANGE
