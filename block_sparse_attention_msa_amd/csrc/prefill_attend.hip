@@ -25,9 +25,14 @@
 // would pass 2^64 is recomputed against a raised reference (rare).  Row sums
 // come from the matrix cores (a ones operand against the same bf16
 // probabilities), so the normalisation sums exactly the weights applied.
-// K, V and the step's queries are copied HBM -> LDS with global_load_lds (no
-// registers): V one step ahead into a second buffer, K and Q while the
-// previous step's products run.  Two barriers per step.
+// V and the step's queries are copied HBM -> LDS with global_load_lds into
+// two-deep rings, and each wave loads its 16 keys of K straight into
+// registers (K never passes through LDS).  Step i + 1's copies are issued
+// during step i and spread over its phases (half of V as it begins, K and
+// the other half once its scores are done, its queries during P V): the
+// copy engine accepts about 49 bytes per clock per compute unit, so copies
+// issued all at once stall every wave until they drain.  Two barriers per
+// step.
 #include "common.hpp"
 
 namespace msa {
@@ -175,13 +180,19 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     const int l4 = lane >> 4;
     const int n_steps = a.counts[blockIdx.x];
     const u32x4* steps = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
+    // the same list read through the scalar cache (entries are wave-uniform)
+    const __attribute__((address_space(4))) u32x4* steps_s =
+        (const __attribute__((address_space(4))) u32x4*)(reinterpret_cast<uintptr_t>(steps));
 
-    // Separate objects, so that reads of one are not made to wait for copies
-    // in flight into another.
-    __shared__ __attribute__((aligned(16))) char kbuf[kBufBytes];
+    // Two-deep rings for V and the step's queries: step i + 1's copies are
+    // issued as step i begins, so they have a whole step to land.  Separate
+    // objects, so that reads of one are not made to wait for copies in
+    // flight into another.  K does not pass through LDS: each wave loads its
+    // own 16 keys straight into the registers the score products read.
     __shared__ __attribute__((aligned(16))) char vbuf0[kBufBytes];
     __shared__ __attribute__((aligned(16))) char vbuf1[kBufBytes];
-    __shared__ __attribute__((aligned(16))) char qbuf[kPb][kQBytes];
+    __shared__ __attribute__((aligned(16))) char qbuf0[kPb][kQBytes];
+    __shared__ __attribute__((aligned(16))) char qbuf1[kPb][kQBytes];
     __shared__ __attribute__((aligned(16))) char pbuf[kPb][kQBytes];
     __shared__ __attribute__((aligned(16))) float pmax[kPb][kHeadsPerGroup][kPaWaves];
     __shared__ float rnew[kPb][kHeadsPerGroup];    // redo: raised reference of the step's queries
@@ -234,13 +245,9 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
 
     // Lane offsets inside staged buffers (the row permutation depends on
     // row & 15 only, so multiples of 16 rows are added as constants).
-    int koff[4];                                // K rows 16w + l16, dims 32*ks4 + 8*l4 ..
-    int qoff[4];                                // Q rows (heads) l16, same dims
+    int qoff[4];                                // Q rows (heads) l16, dims 32*ks4 + 8*l4 ..
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
-        koff[ks4] = swz(16 * wave + l16, 4 * ks4 + l4);
-        qoff[ks4] = swz(l16, 4 * ks4 + l4);
-    }
+    for (int ks4 = 0; ks4 < 4; ++ks4) qoff[ks4] = swz(l16, 4 * ks4 + l4);
     // V: row 4*l4 + l16/4 (+ 32c, + 16), dims 16w + 4*(l16 % 4) .. +3
     const int voff = swz(4 * l4 + (l16 >> 2), 2 * wave + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
     // P exchange: chunk c = keys 32c .. 32c+31 is written by waves 2c (keys
@@ -249,9 +256,9 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     const int pw_off = (((wave >> 1) * 4 + l4) * 16 + l16) * 16 + (wave & 1) * 8;
     const int pr_off = (l4 * 16 + l16) * 16;   // + 1 KiB per chunk
 
-    // Copies.  Slot s (16 bytes) of a staged 256-byte-row buffer holds
+    // Copies of V.  Slot s (16 bytes) of a staged 256-byte-row buffer holds
     // segment (s % 16) ^ f(row) of row s / 16.  One call issues instruction j
-    // (of 4) of this wave's share of a K or V block.
+    // (of 4) of this wave's share of the block.
     const int last_row = static_cast<int>(a.last_row);       // positions are int32
     uint32_t soff[4];                                          // lane's source offset (elements) in a block
 #pragma unroll
@@ -261,10 +268,10 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         soff[j] = static_cast<uint32_t>(row * kGroups * kHeadDim + 8 * ((slot & 15) ^ rowperm(row)));
     }
     // e: the block's step entry (block id, mask, first cache row)
-    auto stage_row_j = [&](const uint16_t* cache, const u32x4& e, char* dst, int j) {
+    auto stage_v = [&](const u32x4& e, char* dst, int j) {
         const int row0 = static_cast<int>(e[0]) * kBlock;
         const int64_t rb = static_cast<int64_t>((static_cast<uint64_t>(e[3]) << 32) | e[2]);
-        const uint16_t* src = cache + (rb * kGroups + g) * kHeadDim;
+        const uint16_t* src = a.v + (rb * kGroups + g) * kHeadDim;
         uint32_t o = soff[j];
         if (row0 + kBlock - 1 > last_row) {                   // wave-uniform: the chunk's last block
             // rows past the chunk's last key are read from that key's row:
@@ -274,23 +281,45 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         }
         __builtin_amdgcn_global_load_lds(src + o, LDS_PTR(void, dst + (256 * wave + 64 * j) * 16), 16, 0, 0);
     };
-    // Q of query t into slot p: instruction j (of 4) is issued by wave (4p + j) % 8.
-    auto stage_q = [&](int p, int t) {
+    // K of this wave's keys 16w + l16 into registers: lane (l16, l4) holds
+    // dims 32*ks4 + 8*l4 .. +7 in kr[ks4], the A operand of the score products.
+    auto load_k = [&](const u32x4& e, bf16x8 (&kr)[4]) {
+        const int row0 = static_cast<int>(e[0]) * kBlock;
+        const int64_t rb = static_cast<int64_t>((static_cast<uint64_t>(e[3]) << 32) | e[2]);
+        int row = 16 * wave + l16;
+        if (row0 + kBlock - 1 > last_row) row = min(row, last_row - row0);   // past the chunk's last key: masked
+        const uint16_t* src = a.k + ((rb + row) * kGroups + g) * kHeadDim + 8 * l4;
+#pragma unroll
+        for (int ks4 = 0; ks4 < 4; ++ks4) kr[ks4] = *reinterpret_cast<const bf16x8*>(src + 32 * ks4);
+    };
+    // Q of query t into slot p of qdst: instruction j (of 4) is issued by wave (4p + j) % 8.
+    auto stage_q = [&](char (*qdst)[kQBytes], int p, int t) {
         const int j = (wave - 4 * p) & 7;
         if (j < 4) {
             const int slot = 64 * j + lane;
             const int row = slot >> 4;
             const int seg = (slot & 15) ^ rowperm(row);
             __builtin_amdgcn_global_load_lds(a.q + q_base + t * kQStride + row * kHeadDim + 8 * seg,
-                                             LDS_PTR(void, &qbuf[p][64 * j * 16]), 16, 0, 0);
+                                             LDS_PTR(void, &qdst[p][64 * j * 16]), 16, 0, 0);
+        }
+    };
+    // every copy step i + 1 needs: K into registers, V and its queries into LDS
+    auto prefetch = [&](const u32x4& e, bf16x8 (&kr)[4], char* vdst, char (*qdst)[kQBytes]) {
+        load_k(e, kr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stage_v(e, vdst, j);
+        uint32_t m = e[1];
+        for (int p = 0; m != 0u; ++p) {
+            stage_q(qdst, p, __builtin_ctz(m));
+            m &= m - 1u;
         }
     };
 
     // This wave's S^T tile (keys 16w + 4*l4 + r, head l16) of query p of the
-    // step, from K in kbuf and Q in qbuf[p]; keys past the query masked.
-    auto load_q = [&](int p, bf16x8 (&qop)[4]) {
+    // step, from K in registers and Q in qcur[p]; keys past the query masked.
+    auto load_q = [&](const char (*qcur)[kQBytes], int p, bf16x8 (&qop)[4]) {
 #pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) qop[ks4] = *reinterpret_cast<const bf16x8*>(qbuf[p] + qoff[ks4]);
+        for (int ks4 = 0; ks4 < 4; ++ks4) qop[ks4] = *reinterpret_cast<const bf16x8*>(qcur[p] + qoff[ks4]);
     };
     auto score_q = [&](const bf16x8 (&kop)[4], const bf16x8 (&qop)[4], int qpos, int b) {
         f32x4 s0 = mfma_16x16x32_bf16(kop[0], qop[0], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -306,9 +335,9 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         }
         return s;
     };
-    auto score = [&](const bf16x8 (&kop)[4], int p, int qpos, int b) {
+    auto score = [&](const bf16x8 (&kop)[4], const char (*qcur)[kQBytes], int p, int qpos, int b) {
         bf16x8 qop[4];
-        load_q(p, qop);
+        load_q(qcur, p, qop);
         return score_q(kop, qop, qpos, b);
     };
     // P = 2^(scale' s - ref) for this wave's keys -> bf16 into pbuf[p];
@@ -326,28 +355,29 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     // sums: such a step is recomputed against a raised reference.
     constexpr float kOverflow = 64.f;
 
-    // One step: block b, tile queries `mask` (at most kPb), V in vcur; the
-    // next step's V goes to vnext.
-    auto step = [&](int i, const char* vcur, char* vnext) {
-        const u32x4 e = steps[i];
-        const int b = static_cast<int>(e[0]);
-        const uint32_t mask = e[1];
+    // One step: block b, tile queries `mask` (at most kPb); its K in kcur, V
+    // in vcur, queries in qcur.  Step i + 1's copies go to knext, vnext, qnext.
+    // ec holds step i's entry and receives step i + 2's (loaded during the
+    // step, so that it has landed by the next barrier); en holds step i + 1's.
+    auto step = [&](int i, u32x4& ec, const u32x4& en, const char (*qcur)[kQBytes], char (*qnext)[kQBytes],
+                    const char* vcur, char* vnext, const bf16x8 (&kcur)[4], bf16x8 (&knext)[4]) {
+        const int b = static_cast<int>(ec[0]);
+        const uint32_t mask = ec[1];
         const int np = __builtin_popcount(mask);
         const bool more = i + 1 < n_steps;
-        const u32x4 en = steps[more ? i + 1 : i];
         const int qpos0 = a.pos0 + static_cast<int>(q_first);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                                        // B0: this step's K, Q, V are in LDS
-
-        // ---- S, P for this wave's 16 keys, every query of the step; the
-        // next step's V is copied meanwhile
-        bf16x8 kop[4];
-#pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) kop[ks4] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks4]);
+        __syncthreads();                                        // B0: this step's K, V and queries have landed
+        if (i + 2 < n_steps) ec = steps_s[i + 2];               // scalar load: waited for at the next barrier
+        // step i + 1's copies are spread over this step (V now, K once the
+        // scores are done, its queries during P V), so that the copy engine
+        // drains them while this step computes
         if (more) {
-            stage_row_j(a.v, en, vnext, 0);
-            stage_row_j(a.v, en, vnext, 1);
+            stage_v(en, vnext, 0);
+            stage_v(en, vnext, 1);
         }
+
+        // ---- S, P for this wave's 16 keys, every query of the step
         float xmax = -INFINITY;
         {
             // two queries per iteration, so that their read / product /
@@ -361,37 +391,35 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                 m &= m - 1u;
                 const float r0 = m_ref[t0][l16], r1 = m_ref[t1][l16];
                 bf16x8 q0[4], q1[4];
-                load_q(p, q0);
-                load_q(p + 1, q1);
-                const f32x4 s0 = score_q(kop, q0, qpos0 + t0, b);
-                const f32x4 s1 = score_q(kop, q1, qpos0 + t1, b);
+                load_q(qcur, p, q0);
+                load_q(qcur, p + 1, q1);
+                const f32x4 s0 = score_q(kcur, q0, qpos0 + t0, b);
+                const f32x4 s1 = score_q(kcur, q1, qpos0 + t1, b);
                 xmax = fmaxf(xmax, fmaxf(write_p(s0, p, r0), write_p(s1, p + 1, r1)));
             }
             if (p < np) {
                 const int t = __builtin_ctz(m);
-                xmax = fmaxf(xmax, write_p(score(kop, p, qpos0 + t, b), p, m_ref[t][l16]));
+                xmax = fmaxf(xmax, write_p(score(kcur, qcur, p, qpos0 + t, b), p, m_ref[t][l16]));
             }
         }
         if (more) {
-            stage_row_j(a.v, en, vnext, 2);
-            stage_row_j(a.v, en, vnext, 3);
+            load_k(en, knext);
+            stage_v(en, vnext, 2);
+            stage_v(en, vnext, 3);
         }
         if (__builtin_amdgcn_ballot_w64(xmax > kOverflow) != 0 && lane == 0) redo_flag = 1;
-        lds_barrier();                                          // B1: P is in LDS; K, Q free
+        lds_barrier();                                          // B1: P is in LDS
 
         const bool redo = redo_flag != 0;                       // workgroup-uniform, rare
         if (redo) {
             // Raise the reference of the step's queries to max(ref, block
-            // max) and recompute P (K and Q are still in place); the
-            // accumulators are scaled by 2^(old - new) below.
-            bf16x8 kre[4];
-#pragma unroll
-            for (int ks4 = 0; ks4 < 4; ++ks4) kre[ks4] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks4]);
+            // max) and recompute P (K is still in registers, the queries in
+            // qcur); the accumulators are scaled by 2^(old - new) below.
             uint32_t m = mask;
             for (int p = 0; p < np; ++p) {
                 const int t = __builtin_ctz(m);
                 m &= m - 1u;
-                const f32x4 s = score(kre, p, qpos0 + t, b);
+                const f32x4 s = score(kcur, qcur, p, qpos0 + t, b);
                 const float mx = max_xor32(max_xor16(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
                 if (lane < 16) pmax[p][l16][wave] = mx;
             }
@@ -406,7 +434,7 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                                        fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3]))) * qk_scale;
                 const float old = m_ref[t][l16];
                 const float ref = fmaxf(old, mb);
-                write_p(score(kre, p, qpos0 + t, b), p, ref);
+                write_p(score(kcur, qcur, p, qpos0 + t, b), p, ref);
                 if (wave == 0 && lane < 16) {
                     rnew[p][l16] = ref;
                     alph[p][l16] = __builtin_amdgcn_exp2f(old - ref);
@@ -425,8 +453,7 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         }
 
         // ---- O^T += V^T P^T for this wave's 16 dims, every query of the
-        // step, and the row sums of its own queries; the next step's K and Q
-        // are copied meanwhile
+        // step, and the row sums of its own queries
         bf16x8 vop[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -438,11 +465,9 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                                              0, 1, 2, 3, 4, 5, 6, 7);
         }
         if (more) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) stage_row_j(a.k, en, kbuf, j);
             uint32_t mn = en[1];
             for (int p = 0; mn != 0u; ++p) {
-                stage_q(p, __builtin_ctz(mn));
+                stage_q(qnext, p, __builtin_ctz(mn));
                 mn &= mn - 1u;
             }
         }
@@ -478,22 +503,13 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         }
     };
 
-    if (n_steps > 0) {
-        const u32x4 e0 = steps[0];
-        uint32_t m = e0[1];
-        for (int j = 0; j < 4; ++j) {
-            stage_row_j(a.k, e0, kbuf, j);
-            stage_row_j(a.v, e0, vbuf0, j);
-        }
-        for (int p = 0; m != 0u; ++p) {
-            stage_q(p, __builtin_ctz(m));
-            m &= m - 1u;
-        }
-    }
+    bf16x8 kA[4], kB[4];
+    u32x4 eA = steps[0], eB = steps[n_steps > 1 ? 1 : 0];   // every tile has a step (its local block)
+    if (n_steps > 0) prefetch(eA, kA, vbuf0, qbuf0);
     for (int i = 0; i < n_steps; i += 2) {
-        step(i, vbuf0, vbuf1);
+        step(i, eA, eB, qbuf0, qbuf1, vbuf0, vbuf1, kA, kB);
         if (i + 1 >= n_steps) break;
-        step(i + 1, vbuf1, vbuf0);
+        step(i + 1, eB, eA, qbuf1, qbuf0, vbuf1, vbuf0, kB, kA);
     }
     // row sums to LDS (lane (l16, 0) of the owner wave holds head l16's)
 #pragma unroll
