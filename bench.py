@@ -545,14 +545,40 @@ def bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name, iters=30):
     step = seg.sum(1)
     scan_bytes = S * (p + 1) * 4 * 128 * 4
     t_sel = seg[:, 1].mean()
+    # The same step captured once into a HIP graph and replayed: the kernels
+    # are the same, the host's launch gaps between them (which dominate a
+    # step of small kernels) are gone.
+    out_eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g_ms = []
+    for _ in range(iters):
+        g0.record()
+        graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        g_ms.append(g0.elapsed_time(g1))
+    g_ms = np.array(g_ms)
+    graph_ok = bool(torch.equal(out, out_eager))
     log(f"[bench] {name}: step {step.mean() * 1e3:.1f} us (p10 {np.percentile(step, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(step, 90) * 1e3:.1f}): append {seg[:, 0].mean() * 1e3:.1f} select "
-        f"{t_sel * 1e3:.1f} attend {seg[:, 2].mean() * 1e3:.1f} us; indexer {scan_bytes / (t_sel * 1e-3) / 1e9:.0f} GB/s")
+        f"{t_sel * 1e3:.1f} attend {seg[:, 2].mean() * 1e3:.1f} us; indexer {scan_bytes / (t_sel * 1e-3) / 1e9:.0f} GB/s; "
+        f"graph replay {np.median(g_ms) * 1e3:.1f} us (p10 {np.percentile(g_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(g_ms, 90) * 1e3:.1f}; output {'identical' if graph_ok else 'DIFFERS'})")
     key = name.replace("decode_", "")
     return {
         f"decode_{key}_queries_s": round(S / (step.mean() * 1e-3), 1),
+        f"decode_{key}_graph_queries_s": round(S / (np.median(g_ms) * 1e-3), 1) if graph_ok else None,
         f"decode_{key}_us": {"step": round(step.mean() * 1e3, 2), "step_p10": round(np.percentile(step, 10) * 1e3, 2),
                              "step_p90": round(np.percentile(step, 90) * 1e3, 2),
+                             "step_graph_median": round(np.median(g_ms) * 1e3, 2),
+                             "step_graph_p10": round(np.percentile(g_ms, 10) * 1e3, 2),
+                             "step_graph_p90": round(np.percentile(g_ms, 90) * 1e3, 2),
                              "append": round(seg[:, 0].mean() * 1e3, 2), "select": round(t_sel * 1e3, 2),
                              "attend": round(seg[:, 2].mean() * 1e3, 2)},
         f"decode_{key}_indexer_GBps": round(scan_bytes / (t_sel * 1e-3) / 1e9, 1),

@@ -384,10 +384,10 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     // thread issues 2 * kCopiesPerUnit copies per unit, so waiting until at
     // most that many are outstanding means unit u has landed.  Only copies
     // into LDS are in flight in the loop.
-    static_assert(kMaxUnits % 2 == 0, "units alternate between the two ring buffers");
+    static_assert(kMaxUnits == 1 || kMaxUnits % 2 == 0, "units alternate between the two ring buffers");
     if constexpr (kQ == 0) {
         stage(0, kbuf0, vbuf0);
-        stage(1, kbuf1, vbuf1);
+        if constexpr (kMaxUnits > 1) stage(1, kbuf1, vbuf1);
         auto step = [&](int u, const char* kb, const char* vb, char* kn, char* vn) __attribute__((always_inline)) {
             if (u + 1 < kMaxUnits) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kCopiesPerUnit));   // compile-time
             else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -400,13 +400,14 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
 #pragma unroll
         for (int u = 0; u < kMaxUnits; u += 2) {
             step(u, kbuf0, vbuf0, kbuf0, vbuf0);
-            step(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
+            if constexpr (kMaxUnits > 1) step(u + 1, kbuf1, vbuf1, kbuf1, vbuf1);
         }
     } else {
         // quantized: unit u + 2 loads into register set u % 2 once every wave
         // holds unit u's operands; unit u + 1 (loaded one unit earlier) is
         // written to its buffer, freed at the release of unit u - 1, after the
         // math of unit u
+        static_assert(kMaxUnits % 2 == 0, "the quantized ring is instantiated for even unit counts");
         qload(0, 0);
         qcommit(0, kbuf0, vbuf0, kscl_s[0], vscl_s[0]);
         qload(1, 1);
@@ -471,7 +472,11 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     }
 }
 
-// Fixed-order merge of the split partials of one (query, group).
+// Fixed-order merge of the split partials of one (query, group).  A thread
+// owns 8 dims of one head; the partials of up to kCombineBatch splits are
+// loaded together (one round trip to memory per batch, not per split).
+constexpr int kCombineBatch = 16;
+
 __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ ws,
                                                              int n_split, float* __restrict__ out) {
     const int g = static_cast<int>(blockIdx.x % kGroups);
@@ -479,20 +484,36 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
     const int hh = threadIdx.x >> 4;
     const int d0 = 8 * (threadIdx.x & 15);
     const float* part0 = ws + (i * kGroups + g) * n_split * static_cast<int64_t>(kPartFloats);
+    constexpr int kMl = kHeadsPerGroup * kHeadDim;   // (m, l) of head h at kMl + 2h
     float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp)
-        M = fmaxf(M, part0[sp * kPartFloats + kHeadsPerGroup * kHeadDim + 2 * hh]);
+    for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+        float ms[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            ms[j] = s0 + j < n_split ? part0[(s0 + j) * kPartFloats + kMl + 2 * hh] : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) M = fmaxf(M, ms[j]);
+    }
     float L = 0.f;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < n_split; ++sp) {
-        const float* part = part0 + sp * kPartFloats;
-        const float ms = part[kHeadsPerGroup * kHeadDim + 2 * hh];
-        const float wt = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-        L += wt * part[kHeadsPerGroup * kHeadDim + 2 * hh + 1];
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0 + 4);
-        o[0] += wt * a0.x; o[1] += wt * a0.y; o[2] += wt * a0.z; o[3] += wt * a0.w;
-        o[4] += wt * a1.x; o[5] += wt * a1.y; o[6] += wt * a1.z; o[7] += wt * a1.w;
+    for (int s0 = 0; s0 < n_split; s0 += kCombineBatch) {
+        float ms[kCombineBatch], ls[kCombineBatch];
+        f32x4 a0[kCombineBatch], a1[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) {
+            const float* part = part0 + (s0 + j < n_split ? s0 + j : s0) * kPartFloats;
+            ms[j] = s0 + j < n_split ? part[kMl + 2 * hh] : -INFINITY;
+            ls[j] = part[kMl + 2 * hh + 1];
+            a0[j] = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0);
+            a1[j] = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0 + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) {      // in split order
+            const float wt = (ms[j] == -INFINITY) ? 0.f : exp2f(ms[j] - M);
+            L += wt * ls[j];
+            o[0] += wt * a0[j].x; o[1] += wt * a0[j].y; o[2] += wt * a0[j].z; o[3] += wt * a0[j].w;
+            o[4] += wt * a1[j].x; o[5] += wt * a1[j].y; o[6] += wt * a1[j].z; o[7] += wt * a1[j].w;
+        }
     }
     const float inv = 1.f / L;
     float* dst = out + (i * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + hh) * kHeadDim + d0;
@@ -511,11 +532,13 @@ static_assert(kMaxSplitEntries == kUnitsPerSplitMax * kUnit, "ids one split stag
 template <int kQ>
 void launch_units(const KernelArgs& ka, bool blocks, int nu, dim3 grid, hipStream_t s) {
     if (blocks) {
-        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<false, 2, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+        if (nu == 1 && kQ == 0) hipLaunchKernelGGL((attend_kernel<false, 1, 0>), grid, dim3(kAttThreads), 0, s, ka);
+        else if (nu <= 2) hipLaunchKernelGGL((attend_kernel<false, 2, kQ>), grid, dim3(kAttThreads), 0, s, ka);
         else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<false, 4, kQ>), grid, dim3(kAttThreads), 0, s, ka);
         else hipLaunchKernelGGL((attend_kernel<false, kUnitsPerSplitMax, kQ>), grid, dim3(kAttThreads), 0, s, ka);
     } else {
-        if (nu <= 2) hipLaunchKernelGGL((attend_kernel<true, 2, kQ>), grid, dim3(kAttThreads), 0, s, ka);
+        if (nu == 1 && kQ == 0) hipLaunchKernelGGL((attend_kernel<true, 1, 0>), grid, dim3(kAttThreads), 0, s, ka);
+        else if (nu <= 2) hipLaunchKernelGGL((attend_kernel<true, 2, kQ>), grid, dim3(kAttThreads), 0, s, ka);
         else if (nu <= 4) hipLaunchKernelGGL((attend_kernel<true, 4, kQ>), grid, dim3(kAttThreads), 0, s, ka);
         else hipLaunchKernelGGL((attend_kernel<true, kUnitsPerSplitMax, kQ>), grid, dim3(kAttThreads), 0, s, ka);
     }

@@ -178,7 +178,71 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_f16_kerne
     }
 }
 
+// Small problems (a few queries over a short context: fewer workgroups than
+// compute units in the scan above) split every block over kFineSub
+// workgroups of four waves, four tokens per wave, so that the whole scan is
+// one round of loads in flight; each workgroup writes the partial maximum
+// of its 16 tokens per group, and the top-k takes the maximum of a block's
+// kFineSub partials (a max is exact in any order, so the block scores are
+// those of the scan above, bit for bit).
+constexpr int kFineWaves = 4;
+constexpr int kFineTokPerWave = kBlock / (kFineSub * kFineWaves);   // 4
+
+__global__ __launch_bounds__(64 * kFineWaves) void block_scores_decode_fine_kernel(
+    const float* __restrict__ idx_k, Pager pg, const float* __restrict__ idx_q,
+    const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
+    float* __restrict__ bs_part, int nblk) {
+    const int64_t i = blockIdx.x;
+    const int b = blockIdx.y;
+    const int sub = blockIdx.z;
+    const int p = q_pos[i];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    float m = -INFINITY;
+    const int t_begin = (sub * kFineWaves + wave) * kFineTokPerWave;
+    const int t_end = min(t_begin + kFineTokPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+    if (t_begin < t_end) {
+        const f32x4* qrow = reinterpret_cast<const f32x4*>(idx_q + i * kGroups * kIdxDim);
+        const f32x4 q0 = qrow[g * 32 + c];
+        const f32x4 q1 = qrow[g * 32 + 16 + c];
+        const f32x4* rows = reinterpret_cast<const f32x4*>(
+            idx_k + pg.block_row_uniform(q_stream[i], b) * (kGroups * kIdxDim)) + g * 32 + c;
+        f32x4 a[kFineTokPerWave], bb[kFineTokPerWave];
+#pragma unroll
+        for (int u = 0; u < kFineTokPerWave; ++u) {
+            const int t = min(t_begin + u, t_end - 1);           // past the query: its last visible token again
+            a[u] = __builtin_nontemporal_load(rows + t * kRowF4);
+            bb[u] = __builtin_nontemporal_load(rows + t * kRowF4 + 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kFineTokPerWave; ++u) m = fmaxf(m, row16_sum(dot8(q0, q1, a[u], bb[u])));
+    }
+    __shared__ float red[kFineWaves][kGroups];
+    if (c == 0) red[wave][g] = m;
+    __syncthreads();
+    if (threadIdx.x < kGroups) {
+        float r = red[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kFineWaves; ++w) r = fmaxf(r, red[w][threadIdx.x]);
+        bs_part[((i * kGroups + threadIdx.x) * nblk + b) * kFineSub + sub] = r;
+    }
+}
+
 }  // namespace
+
+bool scan_is_fine(int64_t n_q, int nblk) {
+    return n_q * ((nblk + kScanBlocksPerWg - 1) / kScanBlocksPerWg) < kFineBelowWorkgroups;
+}
+
+hipError_t launch_block_scores_decode_fine(const CacheView& c, const float* idx_q, const int32_t* stream,
+                                           const int32_t* pos, int64_t n_q, int nblk, float* bs_part,
+                                           hipStream_t s) {
+    hipLaunchKernelGGL(block_scores_decode_fine_kernel, dim3(static_cast<unsigned>(n_q), nblk, kFineSub),
+                       dim3(64 * kFineWaves), 0, s, c.idx_k, c.pg, idx_q, stream, pos, bs_part, nblk);
+    return hipGetLastError();
+}
 
 hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,

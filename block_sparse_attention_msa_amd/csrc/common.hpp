@@ -160,6 +160,16 @@ hipError_t launch_append_kv_quant(int kv_format, uint8_t* k, uint8_t* v, float* 
 hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
                                       int64_t nblk_stride, hipStream_t s);
+// Small decode problems over an f32 index cache: each block is scanned by
+// kFineSub workgroups, which write partial maxima
+// bs_part[query][group][block][kFineSub]; launch_topk_blocks with
+// n_sub = kFineSub ranks their maxima.  Used when scan_is_fine(n_q, nblk).
+constexpr int kFineSub = 8;
+constexpr int64_t kFineBelowWorkgroups = 256;   // the regular scan's grid below this size
+bool scan_is_fine(int64_t n_q, int nblk);
+hipError_t launch_block_scores_decode_fine(const CacheView& c, const float* idx_q, const int32_t* stream,
+                                           const int32_t* pos, int64_t n_q, int nblk, float* bs_part,
+                                           hipStream_t s);
 
 // ws: prefill_scores_ws_bytes(pos0 + n_q - 1) bytes (the split keys).
 size_t prefill_scores_ws_bytes(int32_t max_pos);
@@ -167,9 +177,11 @@ hipError_t launch_block_scores_prefill(const CacheView& c, const float* idx_q, i
                                        int32_t pos0, int64_t n_q, int nblk, float* bs,
                                        int64_t nblk_stride, void* ws, hipStream_t s);
 
+// n_sub > 1: block b's score is the maximum of bs[row + b * n_sub + 0 .. n_sub - 1]
+// (partial maxima of a fine scan; nblk_stride = nblk * n_sub).
 hipError_t launch_topk_blocks(const float* bs, int64_t nblk_stride, const int32_t* pos,
                               int64_t n_q, int nblk, int top_k, int32_t* sel, int32_t* n_sel,
-                              hipStream_t s);
+                              hipStream_t s, int n_sub = 1);
 // Same, for the consecutive positions pos0 .. pos0 + n_q - 1.
 hipError_t launch_topk_blocks_range(const float* bs, int64_t nblk_stride, int32_t pos0, int64_t n_q,
                                     int nblk, int top_k, int32_t* sel, int32_t* n_sel, hipStream_t s);

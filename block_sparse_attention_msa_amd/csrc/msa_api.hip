@@ -88,8 +88,12 @@ int nblk_of(int32_t max_pos) { return max_pos / kBlock + 1; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// block scores of msa_select: one f32 per (query, group, block), or kFineSub
+// partial maxima per block for the small problems the fine scan takes
 size_t select_ws(int64_t n_q, int32_t max_pos) {
-    return align256(static_cast<size_t>(n_q) * kGroups * nblk_of(max_pos) * sizeof(float));
+    const int nblk = nblk_of(max_pos);
+    const size_t per = msa::scan_is_fine(n_q, nblk) ? msa::kFineSub : 1;
+    return align256(static_cast<size_t>(n_q) * kGroups * nblk * per * sizeof(float));
 }
 
 // msa_select_prefill: block scores, then the split keys of the scorer.
@@ -193,6 +197,12 @@ msa_status select_impl(const msa_dims* dims, const msa_cache* cache, const float
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     float* bs = static_cast<float*>(d_ws);
     const int nblk = nblk_of(max_pos);
+    if (cache->idx_k && msa::scan_is_fine(n_q, nblk)) {   // few queries over a short context
+        MSA_TRY(hip_status(msa::launch_block_scores_decode_fine(view(cache), d_idx_q, d_stream, d_pos, n_q, nblk,
+                                                                bs, s)));
+        return hip_status(msa::launch_topk_blocks(bs, int64_t(nblk) * msa::kFineSub, d_pos, n_q, nblk, dims->top_k,
+                                                  d_sel, d_n_sel, s, msa::kFineSub));
+    }
     MSA_TRY(hip_status(msa::launch_block_scores_decode(view(cache), d_idx_q, d_stream, d_pos, n_q, nblk,
                                                        bs, nblk, s)));
     return hip_status(msa::launch_topk_blocks(bs, nblk, d_pos, n_q, nblk, dims->top_k, d_sel, d_n_sel, s));

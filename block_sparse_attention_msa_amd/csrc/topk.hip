@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
                                                          const int32_t* __restrict__ q_pos,
                                                          int32_t pos0, int top_k,
                                                          int32_t* __restrict__ sel,
-                                                         int32_t* __restrict__ n_sel) {
+                                                         int32_t* __restrict__ n_sel, int n_sub) {
     extern __shared__ uint64_t keys[];             // [nblk] candidate keys
     __shared__ int32_t chosen[kMaxTopkBlocks];
     const int64_t qg = blockIdx.x;                 // query * kGroups + group
@@ -76,13 +76,31 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
     // Build keys; lane owns blocks lane, lane + 64, ...
     uint64_t best = 0;
     for (int b = lane; b < nvis; b += 64) {
-        uint64_t key = (static_cast<uint64_t>(ordered_key(row[b])) << 31) |
+        float sc = row[b * n_sub];
+        for (int j = 1; j < n_sub; ++j) sc = fmaxf(sc, row[b * n_sub + j]);
+        uint64_t key = (static_cast<uint64_t>(ordered_key(sc)) << 31) |
                        static_cast<uint64_t>(0x7fffffff - b);
         if (b == loc) key |= 1ull << 63;
         keys[b] = key;
         best = key > best ? key : best;
     }
     const int k = min(top_k, nvis);
+    int32_t* out = sel + qg * top_k;
+    if (nvis <= 64) {
+        // short contexts: lane b holds block b's key; its rank is the number
+        // of larger keys (keys are distinct), the k smallest ranks win, and a
+        // winner's output slot is the number of winners with a lower id
+        __syncthreads();
+        const uint64_t mine = best;
+        int rank = 0;
+        for (int c = 0; c < nvis; ++c) rank += keys[c] > mine;
+        const bool win = lane < nvis && rank < k;
+        const uint64_t wins = __builtin_amdgcn_ballot_w64(win);
+        if (win) out[__builtin_popcountll(wins & ((1ull << lane) - 1ull))] = lane;
+        for (int t = k + lane; t < top_k; t += 64) out[t] = -1;
+        if (lane == 0) n_sel[qg] = k;
+        return;
+    }
     for (int r = 0; r < k; ++r) {
         const uint64_t w = wave_max_u64(best);
         const int b = 0x7fffffff - static_cast<int>(w & 0x7fffffff);
@@ -95,7 +113,6 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
     }
     __syncthreads();
     // ascending order: a winner's rank is the number of smaller winners
-    int32_t* out = sel + qg * top_k;
     for (int t = lane; t < top_k; t += 64) {
         if (t < k) {
             const int b = chosen[t];
@@ -113,10 +130,10 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
 
 hipError_t launch_topk_blocks(const float* bs, int64_t nblk_stride, const int32_t* pos,
                               int64_t n_q, int nblk, int top_k, int32_t* sel, int32_t* n_sel,
-                              hipStream_t s) {
+                              hipStream_t s, int n_sub) {
     const size_t lds = static_cast<size_t>(nblk) * sizeof(uint64_t);
     hipLaunchKernelGGL(topk_blocks_kernel, dim3(static_cast<unsigned>(n_q * kGroups)), dim3(64), lds, s,
-                       bs, nblk_stride, pos, 0, top_k, sel, n_sel);
+                       bs, nblk_stride, pos, 0, top_k, sel, n_sel, n_sub);
     return hipGetLastError();
 }
 
@@ -124,7 +141,7 @@ hipError_t launch_topk_blocks_range(const float* bs, int64_t nblk_stride, int32_
                                     int nblk, int top_k, int32_t* sel, int32_t* n_sel, hipStream_t s) {
     const size_t lds = static_cast<size_t>(nblk) * sizeof(uint64_t);
     hipLaunchKernelGGL(topk_blocks_kernel, dim3(static_cast<unsigned>(n_q * kGroups)), dim3(64), lds, s,
-                       bs, nblk_stride, nullptr, pos0, top_k, sel, n_sel);
+                       bs, nblk_stride, nullptr, pos0, top_k, sel, n_sel, 1);
     return hipGetLastError();
 }
 
