@@ -59,7 +59,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="decode step only (for profiling)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="for rocprofv3 counter runs: one plain 1 GiB device copy (calibration of the "
-                         "byte counters), then 3 decode steps and one prefill chunk; prints no result line")
+                         "byte counters), then 3 decode steps, one prefill chunk and one DSA step; prints no "
+                         "result line")
     return ap.parse_args()
 
 
@@ -161,6 +162,8 @@ def main():
         del idx_k, k, v, cache
         torch.cuda.empty_cache()
         bench_prefill(M, W, torch, dev, bits, tens, wsbuf, profile=True)
+        torch.cuda.empty_cache()
+        bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=1, profile=True)
         log("[bench] profile pass done")
         return
 
@@ -586,7 +589,7 @@ def bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name, iters=30):
     }
 
 
-def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20):
+def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20, profile=False):
     wl = W.CONFIGS["dsa_16x64k"]
     host = W.caches(wl)
     qs = W.queries(wl)
@@ -624,9 +627,11 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20):
         M.dsa_attend_decode(dims, cache, q, stream, pos, p, sel, out, ws_att)
         if e: e[3].record()
 
-    for _ in range(3):
+    for _ in range(3 if not profile else 1):
         run()
     torch.cuda.synchronize()
+    if profile:
+        return {}
     for i in range(iters):
         run(ev[i])
     torch.cuda.synchronize()

@@ -141,6 +141,11 @@ __global__ __launch_bounds__(kScThreads, 1) void block_scores_prefill_kernel(ScA
 
     __shared__ __attribute__((aligned(16))) char sbuf0[kScStageBytes];
     __shared__ __attribute__((aligned(16))) char sbuf1[kScStageBytes];
+    // the tile's block maxima, written to bs as one 64-byte row per query at
+    // the end (a store per (query, block) would land 4 KiB from the next)
+    __shared__ __attribute__((aligned(16))) float bs_tile[kScQueryTile][kScBlocksPerWg];
+    for (int idx = threadIdx.x; idx < kScQueryTile * kScBlocksPerWg; idx += kScThreads)
+        bs_tile[idx / kScBlocksPerWg][idx % kScBlocksPerWg] = -INFINITY;
 
     // Query operands (A: m = query, k = dim): lane holds query
     // q_wave + 16*st + l16, dims 32*ks + 8*l4 + 0..7, as hi and lo parts.
@@ -268,8 +273,7 @@ __global__ __launch_bounds__(kScThreads, 1) void block_scores_prefill_kernel(ScA
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float mx = row16_max(blkmax[st][r]);
-                        const int64_t qi = q_wave + 16 * st + 4 * l4 + r;
-                        if (l16 == r && qi < a.n_q) a.bs[(qi * kGroups + g) * a.nblk_stride + b] = mx;
+                        if (l16 == r) bs_tile[wave * 16 * kScSub + 16 * st + 4 * l4 + r][b - b_begin] = mx;
                         blkmax[st][r] = -INFINITY;
                     }
                 }
@@ -293,6 +297,22 @@ __global__ __launch_bounds__(kScThreads, 1) void block_scores_prefill_kernel(ScA
         stage(s_idx + 3, sbuf1);
     }
     __builtin_amdgcn_s_waitcnt(sc_waitcnt_vm(0));   // the last two copies land before the exit
+    __syncthreads();
+    // blocks b_begin .. b_vis_end - 1 of the tile's queries (the rest was
+    // written as -inf above): a thread writes 4 consecutive blocks of a query
+    const int nbv = b_vis_end - b_begin;
+    for (int idx = threadIdx.x; idx < kScQueryTile * (kScBlocksPerWg / 4); idx += kScThreads) {
+        const int ql = idx / (kScBlocksPerWg / 4);
+        const int b4 = 4 * (idx % (kScBlocksPerWg / 4));
+        const int64_t qi = q_first + ql;
+        if (qi >= a.n_q || b4 >= nbv) continue;
+        float* dst = a.bs + (qi * kGroups + g) * a.nblk_stride + b_begin + b4;
+        if (b4 + 4 <= nbv && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+            *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(&bs_tile[ql][b4]);
+        } else {
+            for (int e = 0; e < 4 && b4 + e < nbv; ++e) dst[e] = bs_tile[ql][b4 + e];
+        }
+    }
 }
 
 }  // namespace

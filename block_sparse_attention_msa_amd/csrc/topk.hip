@@ -10,9 +10,13 @@
 // f32 block score, bits 30..0 = ~block id.  The maximum key is therefore the
 // local block first, then the highest score, then the LOWER id on equal
 // scores -- a total order, so the selection is unique and deterministic.
-// Keys live in LDS (8 bytes per candidate block); each lane keeps the best key of its own slice, the wave
-// takes the maximum over lanes k times and only the winning lane rescans its
-// slice.  The k winners are written in ascending id order, padded with -1.
+// Up to 1024 candidates live in registers (a lane's 16 at most): each of the
+// k rounds is a wave maximum after which every lane clears the winner if it
+// holds it.  Longer contexts (up to 4096 blocks) keep the keys in LDS; each
+// lane keeps the best key of its own slice, the wave takes the maximum over
+// lanes k times and only the winning lane rescans its slice.  Up to 64 blocks
+// are ranked directly (a block's rank is the number of larger keys).  The k
+// winners are written in ascending id order, padded with -1.
 #include "common.hpp"
 
 namespace msa {
@@ -58,6 +62,51 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
     return x;
 }
 
+// Writes the k winners of one (query, group) in ascending id order, padded
+// with -1: a winner's slot is the number of smaller winners.
+__device__ __forceinline__ void write_ascending(const int32_t* chosen, int k, int top_k, int lane, int32_t* out) {
+    for (int t = lane; t < top_k; t += 64) {
+        if (t < k) {
+            const int b = chosen[t];
+            int rank = 0;
+            for (int u = 0; u < k; ++u) rank += chosen[u] < b;
+            out[rank] = b;
+        } else {
+            out[t] = -1;
+        }
+    }
+}
+
+// Candidates held in registers: lane l owns blocks l, l + 64, ..., kPer of
+// them (nvis <= 64 * kPer).  Each round takes the wave maximum and every lane
+// clears the key equal to it (only its owner has it), so no round waits on
+// memory.
+template <int kPer>
+__device__ __forceinline__ void topk_in_registers(const float* row, int n_sub, int nvis, int loc, int k, int lane,
+                                                  int32_t* chosen) {
+    uint64_t key[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int b = lane + 64 * j;
+        key[j] = 0;
+        if (b < nvis) {
+            float sc = row[b * n_sub];
+            for (int e = 1; e < n_sub; ++e) sc = fmaxf(sc, row[b * n_sub + e]);
+            key[j] = (static_cast<uint64_t>(ordered_key(sc)) << 31) | static_cast<uint64_t>(0x7fffffff - b) |
+                     (b == loc ? 1ull << 63 : 0ull);
+        }
+    }
+    for (int r = 0; r < k; ++r) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int j = 1; j < kPer; ++j) best = max_u64(best, key[j]);
+        const uint64_t w = wave_max_u64(best);
+        if (lane == 0) chosen[r] = 0x7fffffff - static_cast<int>(w & 0x7fffffff);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) key[j] = key[j] == w ? 0ull : key[j];
+    }
+}
+
 __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict__ bs,
                                                          int64_t nblk_stride,
                                                          const int32_t* __restrict__ q_pos,
@@ -73,6 +122,16 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
     const int nvis = loc + 1;
     const float* row = bs + qg * nblk_stride;
 
+    if (nvis > 64 && nvis <= 64 * 16) {
+        const int k = min(top_k, nvis);
+        if (nvis <= 64 * 4) topk_in_registers<4>(row, n_sub, nvis, loc, k, lane, chosen);
+        else if (nvis <= 64 * 8) topk_in_registers<8>(row, n_sub, nvis, loc, k, lane, chosen);
+        else topk_in_registers<16>(row, n_sub, nvis, loc, k, lane, chosen);
+        __syncthreads();
+        write_ascending(chosen, k, top_k, lane, sel + qg * top_k);
+        if (lane == 0) n_sel[qg] = k;
+        return;
+    }
     // Build keys; lane owns blocks lane, lane + 64, ...
     uint64_t best = 0;
     for (int b = lane; b < nvis; b += 64) {
@@ -112,17 +171,7 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
         }
     }
     __syncthreads();
-    // ascending order: a winner's rank is the number of smaller winners
-    for (int t = lane; t < top_k; t += 64) {
-        if (t < k) {
-            const int b = chosen[t];
-            int rank = 0;
-            for (int u = 0; u < k; ++u) rank += chosen[u] < b;
-            out[rank] = b;
-        } else {
-            out[t] = -1;
-        }
-    }
+    write_ascending(chosen, k, top_k, lane, out);
     if (lane == 0) n_sel[qg] = k;
 }
 
