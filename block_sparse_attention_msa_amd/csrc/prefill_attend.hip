@@ -22,17 +22,21 @@
 // 16 x 16 slice per wave and query.  The softmax needs no exchange of maxima:
 // each (query, head) uses one fixed reference for the whole sweep (its score
 // against its own key, always selected), and a block whose probabilities
-// would pass 2^64 is recomputed against a raised reference (rare).  Row sums
-// come from the matrix cores (a ones operand against the same bf16
-// probabilities), so the normalisation sums exactly the weights applied.
-// V and the step's queries are copied HBM -> LDS with global_load_lds into
-// two-deep rings, and each wave loads its 16 keys of K straight into
-// registers (K never passes through LDS).  Step i + 1's copies are issued
-// during step i and spread over its phases (half of V as it begins, K and
-// the other half once its scores are done, its queries during P V): the
-// copy engine accepts about 49 bytes per clock per compute unit, so copies
-// issued all at once stall every wave until they drain.  Two barriers per
-// step.
+// would pass 2^64 is recomputed against a raised reference (rare).  The
+// owner wave of each query sums the bf16 probabilities it reads as P V
+// operands (v_dot2 against ones), so the normalisation sums exactly the
+// weights applied.
+//
+// The sweep is pipelined by one step with a single barrier per step: the
+// interval between barriers i - 1 and i holds the scores of step i and the
+// products P V of step i - 1, with probabilities, V and the step's queries
+// in two-deep LDS rings (K goes straight from memory into the registers of
+// the wave that uses it and never passes through LDS).  During the interval
+// the copies for the next interval are issued, spread over its phases (step
+// i + 1's queries as it begins, half of step i's V, then step i + 1's K and
+// the other half of V once the scores are done): the copy engine accepts
+// about 49 bytes per clock per compute unit, so copies issued all at once
+// stall every wave until they drain.
 #include "common.hpp"
 
 namespace msa {
@@ -41,7 +45,7 @@ namespace {
 constexpr int kPaWaves = 8;
 constexpr int kPaThreads = 64 * kPaWaves;
 constexpr int kTq = 32;                     // queries per tile (one mask bit each)
-constexpr int kPb = 6;                      // queries per step
+constexpr int kPb = 5;                      // queries per step
 constexpr int kRowBytes = kHeadDim * 2;     // one group's K or V row, one head's Q row: 256 B
 constexpr int kBufBytes = kBlock * kRowBytes;        // 32 KiB: K (or V) of one block
 constexpr int kQBytes = kHeadsPerGroup * kRowBytes;  // 4 KiB: one query's 16 heads
@@ -50,6 +54,7 @@ constexpr int kStepsThreads = 256;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -184,22 +189,23 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     const __attribute__((address_space(4))) u32x4* steps_s =
         (const __attribute__((address_space(4))) u32x4*)(reinterpret_cast<uintptr_t>(steps));
 
-    // Two-deep rings for V and the step's queries: step i + 1's copies are
-    // issued as step i begins, so they have a whole step to land.  Separate
-    // objects, so that reads of one are not made to wait for copies in
-    // flight into another.  K does not pass through LDS: each wave loads its
-    // own 16 keys straight into the registers the score products read.
+    // Two-deep rings (by step parity) for V, the step's queries and its
+    // probabilities.  Separate objects, so that reads of one are not made to
+    // wait for copies in flight into another.  K does not pass through LDS:
+    // each wave loads its own 16 keys straight into the registers the score
+    // products read.
     __shared__ __attribute__((aligned(16))) char vbuf0[kBufBytes];
     __shared__ __attribute__((aligned(16))) char vbuf1[kBufBytes];
     __shared__ __attribute__((aligned(16))) char qbuf0[kPb][kQBytes];
     __shared__ __attribute__((aligned(16))) char qbuf1[kPb][kQBytes];
-    __shared__ __attribute__((aligned(16))) char pbuf[kPb][kQBytes];
+    __shared__ __attribute__((aligned(16))) char pbuf0[kPb][kQBytes];
+    __shared__ __attribute__((aligned(16))) char pbuf1[kPb][kQBytes];
     __shared__ __attribute__((aligned(16))) float pmax[kPb][kHeadsPerGroup][kPaWaves];
     __shared__ float rnew[kPb][kHeadsPerGroup];    // redo: raised reference of the step's queries
     __shared__ float alph[kPb][kHeadsPerGroup];    // redo: accumulator factor
     __shared__ float m_ref[kTq][kHeadsPerGroup];   // reference of each (query, head), log2 units
     __shared__ float l_fin[kTq][kHeadsPerGroup];
-    __shared__ int redo_flag;
+    __shared__ int redo_step[2];                   // last step of each parity whose probabilities overflowed
 
     const float qk_scale = a.scale * kLog2eP;
     const int64_t q_base = (q_first * kGroups + g) * kHeadsPerGroup * kHeadDim;   // query q_first's 16 heads
@@ -230,18 +236,18 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
             r = (s0 + s1) * qk_scale;
         }
         m_ref[t][h] = r;
-        if (threadIdx.x == 0) redo_flag = 0;
+        if (threadIdx.x < 2) redo_step[threadIdx.x] = -1;
     }
-    // O^T slices (dims 16w + 4*l4 + r, head l16) of all tile queries, and the
-    // row sums of the queries t with t % 8 == w (every row of the tile holds
-    // the same sum)
+    // O^T slices (dims 16w + 4*l4 + r, head l16) of all tile queries, and
+    // the row sums of the queries t with t % 8 == w: lane (l16, l4) sums the
+    // bf16 probabilities of head l16 it reads as operands (keys 32c + 8*l4
+    // .. +7), so that the normalisation sums exactly the weights applied
     f32x4 acc[kTq];
-    f32x4 lacc[kTq / kPaWaves];
+    float lsum[kTq / kPaWaves];
 #pragma unroll
     for (int t = 0; t < kTq; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kTq / kPaWaves; ++k) lacc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    for (int k = 0; k < kTq / kPaWaves; ++k) lsum[k] = 0.f;
 
     // Lane offsets inside staged buffers (the row permutation depends on
     // row & 15 only, so multiples of 16 rows are added as constants).
@@ -303,23 +309,24 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                                              LDS_PTR(void, &qdst[p][64 * j * 16]), 16, 0, 0);
         }
     };
-    // every copy step i + 1 needs: K into registers, V and its queries into LDS
-    auto prefetch = [&](const u32x4& e, bf16x8 (&kr)[4], char* vdst, char (*qdst)[kQBytes]) {
-        load_k(e, kr);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) stage_v(e, vdst, j);
+    // (unrolled over the slots, so that every copy's LDS destination is a
+    // known object and reads of other buffers need not wait for it)
+    auto stage_queries = [&](const u32x4& e, char (*qdst)[kQBytes]) {
         uint32_t m = e[1];
-        for (int p = 0; m != 0u; ++p) {
-            stage_q(qdst, p, __builtin_ctz(m));
-            m &= m - 1u;
+#pragma unroll
+        for (int p = 0; p < kPb; ++p) {
+            if (m != 0u) {
+                stage_q(qdst, p, __builtin_ctz(m));
+                m &= m - 1u;
+            }
         }
     };
 
     // This wave's S^T tile (keys 16w + 4*l4 + r, head l16) of query p of the
-    // step, from K in registers and Q in qcur[p]; keys past the query masked.
-    auto load_q = [&](const char (*qcur)[kQBytes], int p, bf16x8 (&qop)[4]) {
+    // step, from K in registers and Q in qs[p]; keys past the query masked.
+    auto load_q = [&](const char (*qs)[kQBytes], int p, bf16x8 (&qop)[4]) {
 #pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) qop[ks4] = *reinterpret_cast<const bf16x8*>(qcur[p] + qoff[ks4]);
+        for (int ks4 = 0; ks4 < 4; ++ks4) qop[ks4] = *reinterpret_cast<const bf16x8*>(qs[p] + qoff[ks4]);
     };
     auto score_q = [&](const bf16x8 (&kop)[4], const bf16x8 (&qop)[4], int qpos, int b) {
         f32x4 s0 = mfma_16x16x32_bf16(kop[0], qop[0], f32x4{0.f, 0.f, 0.f, 0.f});
@@ -327,105 +334,70 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         s0 = mfma_16x16x32_bf16(kop[2], qop[2], s0);
         s1 = mfma_16x16x32_bf16(kop[3], qop[3], s1);
         f32x4 s = s0 + s1;
+        // causal mask (it only bites in the query's own block; applied
+        // without a branch so that two queries' products can interleave)
         const int key0 = b * kBlock + 16 * wave + 4 * l4;
-        if (b * kBlock + kBlock - 1 > qpos) {                 // the query's own block: causal mask
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (key0 + r > qpos) s[r] = -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) s[r] = key0 + r > qpos ? -INFINITY : s[r];
         return s;
     };
-    auto score = [&](const bf16x8 (&kop)[4], const char (*qcur)[kQBytes], int p, int qpos, int b) {
+    auto score = [&](const bf16x8 (&kop)[4], const char (*qs)[kQBytes], int p, int qpos, int b) {
         bf16x8 qop[4];
-        load_q(qcur, p, qop);
+        load_q(qs, p, qop);
         return score_q(kop, qop, qpos, b);
     };
-    // P = 2^(scale' s - ref) for this wave's keys -> bf16 into pbuf[p];
+    // P = 2^(scale' s - ref) for this wave's keys -> bf16 into ps[p];
     // returns the largest exponent.
-    auto write_p = [&](const f32x4& s, int p, float ref) {
+    auto write_p = [&](const f32x4& s, char (*ps)[kQBytes], int p, float ref) {
         float x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(s[r], qk_scale, -ref);
         const uint32_t w01 = pack2_bf16(__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]));
         const uint32_t w23 = pack2_bf16(__builtin_amdgcn_exp2f(x[2]), __builtin_amdgcn_exp2f(x[3]));
-        *reinterpret_cast<u32x2*>(pbuf[p] + pw_off) = u32x2{w01, w23};
+        *reinterpret_cast<u32x2*>(ps[p] + pw_off) = u32x2{w01, w23};
         return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     };
     // Probabilities above 2^kOverflow could leave the f32 / bf16 range in the
     // sums: such a step is recomputed against a raised reference.
     constexpr float kOverflow = 64.f;
 
-    // One step: block b, tile queries `mask` (at most kPb); its K in kcur, V
-    // in vcur, queries in qcur.  Step i + 1's copies go to knext, vnext, qnext.
-    // ec holds step i's entry and receives step i + 2's (loaded during the
-    // step, so that it has landed by the next barrier); en holds step i + 1's.
-    auto step = [&](int i, u32x4& ec, const u32x4& en, const char (*qcur)[kQBytes], char (*qnext)[kQBytes],
-                    const char* vcur, char* vnext, const bf16x8 (&kcur)[4], bf16x8 (&knext)[4]) {
-        const int b = static_cast<int>(ec[0]);
-        const uint32_t mask = ec[1];
-        const int np = __builtin_popcount(mask);
+    // Interval i, between barriers i - 1 and i: the scores and probabilities
+    // of step i and the products O += P V of step i - 1, so that the two
+    // overlap and each step costs one barrier.  ep, ec, en hold the entries
+    // of steps i - 1, i, i + 1 and move on by one at the end.  Buffers by
+    // parity: qs / ps / vs hold step i's queries, probabilities and V (copied
+    // during this interval); po / vo step i - 1's probabilities and V; qo
+    // receives step i + 1's queries once step i - 1 is finished with them.
+    // kr holds step i's K and receives step i + 1's once the scores are done.
+    auto interval = [&](int i, u32x4& ep, u32x4& ec, u32x4& en, char (*qs)[kQBytes], char (*qo)[kQBytes],
+                        char (*ps)[kQBytes], char (*po)[kQBytes], char* vs, const char* vo, bf16x8 (&kr)[4]) {
+        const bool has_s = i < n_steps;
+        const bool has_pv = i >= 1;
         const bool more = i + 1 < n_steps;
         const int qpos0 = a.pos0 + static_cast<int>(q_first);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                                        // B0: this step's K, V and queries have landed
-        if (i + 2 < n_steps) ec = steps_s[i + 2];               // scalar load: waited for at the next barrier
-        // step i + 1's copies are spread over this step (V now, K once the
-        // scores are done, its queries during P V), so that the copy engine
-        // drains them while this step computes
-        if (more) {
-            stage_v(en, vnext, 0);
-            stage_v(en, vnext, 1);
-        }
 
-        // ---- S, P for this wave's 16 keys, every query of the step
-        float xmax = -INFINITY;
-        {
-            // two queries per iteration, so that their read / product /
-            // exponent chains overlap
-            uint32_t m = mask;
-            int p = 0;
-            for (; p + 1 < np; p += 2) {
-                const int t0 = __builtin_ctz(m);
-                m &= m - 1u;
-                const int t1 = __builtin_ctz(m);
-                m &= m - 1u;
-                const float r0 = m_ref[t0][l16], r1 = m_ref[t1][l16];
-                bf16x8 q0[4], q1[4];
-                load_q(qcur, p, q0);
-                load_q(qcur, p + 1, q1);
-                const f32x4 s0 = score_q(kcur, q0, qpos0 + t0, b);
-                const f32x4 s1 = score_q(kcur, q1, qpos0 + t1, b);
-                xmax = fmaxf(xmax, fmaxf(write_p(s0, p, r0), write_p(s1, p + 1, r1)));
-            }
-            if (p < np) {
-                const int t = __builtin_ctz(m);
-                xmax = fmaxf(xmax, write_p(score(kcur, qcur, p, qpos0 + t, b), p, m_ref[t][l16]));
-            }
-        }
-        if (more) {
-            load_k(en, knext);
-            stage_v(en, vnext, 2);
-            stage_v(en, vnext, 3);
-        }
-        if (__builtin_amdgcn_ballot_w64(xmax > kOverflow) != 0 && lane == 0) redo_flag = 1;
-        lds_barrier();                                          // B1: P is in LDS
-
-        const bool redo = redo_flag != 0;                       // workgroup-uniform, rare
+        // ---- step i - 1 overflowed (workgroup-uniform, rare): raise the
+        // reference of its queries to max(ref, block max) and recompute its
+        // probabilities (its queries are still in qo; its K is fetched
+        // again); the accumulators are scaled by 2^(old - new) below.
+        const bool redo = has_pv && redo_step[(i - 1) & 1] == i - 1;
         if (redo) {
-            // Raise the reference of the step's queries to max(ref, block
-            // max) and recompute P (K is still in registers, the queries in
-            // qcur); the accumulators are scaled by 2^(old - new) below.
-            uint32_t m = mask;
-            for (int p = 0; p < np; ++p) {
+            const int bp = static_cast<int>(ep[0]);
+            const uint32_t mp = ep[1];
+            const int npp = __builtin_popcount(mp);
+            bf16x8 ko[4];
+            load_k(ep, ko);
+            uint32_t m = mp;
+            for (int p = 0; p < npp; ++p) {
                 const int t = __builtin_ctz(m);
                 m &= m - 1u;
-                const f32x4 s = score(kcur, qcur, p, qpos0 + t, b);
+                const f32x4 s = score(ko, qo, p, qpos0 + t, bp);
                 const float mx = max_xor32(max_xor16(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))));
                 if (lane < 16) pmax[p][l16][wave] = mx;
             }
             lds_barrier();
-            m = mask;
-            for (int p = 0; p < np; ++p) {
+            m = mp;
+            for (int p = 0; p < npp; ++p) {
                 const int t = __builtin_ctz(m);
                 m &= m - 1u;
                 const f32x4 m0 = *reinterpret_cast<const f32x4*>(&pmax[p][l16][0]);
@@ -434,49 +406,85 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                                        fmaxf(fmaxf(m1[0], m1[1]), fmaxf(m1[2], m1[3]))) * qk_scale;
                 const float old = m_ref[t][l16];
                 const float ref = fmaxf(old, mb);
-                write_p(score(kcur, qcur, p, qpos0 + t, b), p, ref);
+                write_p(score(ko, qo, p, qpos0 + t, bp), po, p, ref);
                 if (wave == 0 && lane < 16) {
                     rnew[p][l16] = ref;
                     alph[p][l16] = __builtin_amdgcn_exp2f(old - ref);
                 }
             }
-            lds_barrier();
-            if (wave == 0 && lane < 16) {                       // read again only after the next B0
-                m = mask;
-                for (int p = 0; p < np; ++p) {
+            lds_barrier();                                      // every read of the old references is done
+            if (wave == 0 && lane < 16) {
+                m = mp;
+                for (int p = 0; p < npp; ++p) {
                     const int t = __builtin_ctz(m);
                     m &= m - 1u;
                     m_ref[t][l16] = rnew[p][l16];
                 }
             }
-            if (threadIdx.x == 0) redo_flag = 0;                // next read after the next step's B1
+            lds_barrier();                                      // step i reads the new references
+            __builtin_amdgcn_s_waitcnt(0);                      // (nothing of this path stays in flight)
         }
+        // step i + 1's queries first (qo is free now): they have the whole
+        // interval to land
+        if (more) stage_queries(en, qo);
 
-        // ---- O^T += V^T P^T for this wave's 16 dims, every query of the
-        // step, and the row sums of its own queries
-        bf16x8 vop[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                LDS_PTR(v4i16, vcur + kChunk * c * kRowBytes + voff));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                LDS_PTR(v4i16, vcur + (kChunk * c + 16) * kRowBytes + voff));
-            vop[c] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
-                                             0, 1, 2, 3, 4, 5, 6, 7);
+        // ---- step i: S, P for this wave's 16 keys, every query of the step
+        if (has_s) {
+            stage_v(ec, vs, 0);
+            stage_v(ec, vs, 1);
         }
-        if (more) {
-            uint32_t mn = en[1];
-            for (int p = 0; mn != 0u; ++p) {
-                stage_q(qnext, p, __builtin_ctz(mn));
-                mn &= mn - 1u;
+        float xmax = -INFINITY;
+        if (has_s) {
+            const int b = static_cast<int>(ec[0]);
+            uint32_t m = ec[1];
+            const int np = __builtin_popcount(m);
+            // two queries per iteration, so that their read / product /
+            // exponent chains overlap
+            int p = 0;
+            for (; p + 1 < np; p += 2) {
+                const int t0 = __builtin_ctz(m);
+                m &= m - 1u;
+                const int t1 = __builtin_ctz(m);
+                m &= m - 1u;
+                const float r0 = m_ref[t0][l16], r1 = m_ref[t1][l16];
+                bf16x8 q0[4], q1[4];
+                load_q(qs, p, q0);
+                load_q(qs, p + 1, q1);
+                const f32x4 s0 = score_q(kr, q0, qpos0 + t0, b);
+                const f32x4 s1 = score_q(kr, q1, qpos0 + t1, b);
+                xmax = fmaxf(xmax, fmaxf(write_p(s0, ps, p, r0), write_p(s1, ps, p + 1, r1)));
+            }
+            if (p < np) {
+                const int t = __builtin_ctz(m);
+                xmax = fmaxf(xmax, write_p(score(kr, qs, p, qpos0 + t, b), ps, p, m_ref[t][l16]));
             }
         }
-        {
+        if (more) load_k(en, kr);                               // step i's keys are no longer needed
+        if (has_s) {
+            stage_v(ec, vs, 2);
+            stage_v(ec, vs, 3);
+        }
+
+        // ---- step i - 1: O^T += V^T P^T for this wave's 16 dims, every
+        // query of the step, and the row sums of its own queries
+        if (has_pv) {
+            const uint32_t mask = ep[1];
+            const int np = __builtin_popcount(mask);
+            bf16x8 vop[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    LDS_PTR(v4i16, vo + kChunk * c * kRowBytes + voff));
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    LDS_PTR(v4i16, vo + (kChunk * c + 16) * kRowBytes + voff));
+                vop[c] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+            }
             // the next query's P operand is read as soon as this one's
             // products have been issued
             bf16x8 pt[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) pt[c] = *reinterpret_cast<const bf16x8*>(pbuf[0] + pr_off + 1024 * c);
+            for (int c = 0; c < 4; ++c) pt[c] = *reinterpret_cast<const bf16x8*>(po[0] + pr_off + 1024 * c);
             int p = 0;
 #pragma unroll
             for (int t = 0; t < kTq; ++t) {
@@ -485,36 +493,67 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                     if (redo) {
                         const float al = alph[p][l16];
                         acc[t] = acc[t] * al;
-                        if (own) lacc[t / kPaWaves] = lacc[t / kPaWaves] * al;
+                        if (own) lsum[t / kPaWaves] *= al;
                     }
 #pragma unroll
                     for (int c = 0; c < 4; ++c) acc[t] = mfma_16x16x32_bf16(vop[c], pt[c], acc[t]);
                     if (own) {
+                        const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);   // {1, 1}
+                        float su = lsum[t / kPaWaves];
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) lacc[t / kPaWaves] = mfma_16x16x32_bf16(ones, pt[c], lacc[t / kPaWaves]);
+                        for (int c = 0; c < 4; ++c) {
+                            const u32x4 w = __builtin_bit_cast(u32x4, pt[c]);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const uint32_t wj = w[j];   // (a vector element is not an object to bit-cast)
+                                su = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj), ones2, su, false);
+                            }
+                        }
+                        lsum[t / kPaWaves] = su;
                     }
                     ++p;
                     if (p < np) {
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) pt[c] = *reinterpret_cast<const bf16x8*>(pbuf[p] + pr_off + 1024 * c);
+                        for (int c = 0; c < 4; ++c) pt[c] = *reinterpret_cast<const bf16x8*>(po[p] + pr_off + 1024 * c);
                     }
                 }
             }
         }
+        if (__builtin_amdgcn_ballot_w64(xmax > kOverflow) != 0 && lane == 0) redo_step[i & 1] = i;
+        // step i + 2's entry: a scalar load, issued last because every
+        // wait for an LDS read would also wait for it
+        u32x4 e2 = en;
+        if (i + 2 < n_steps) e2 = steps_s[i + 2];
+        // barrier i: step i's probabilities and V, step i + 1's K and
+        // queries have landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        ep = ec;
+        ec = en;
+        en = e2;
     };
 
-    bf16x8 kA[4], kB[4];
-    u32x4 eA = steps[0], eB = steps[n_steps > 1 ? 1 : 0];   // every tile has a step (its local block)
-    if (n_steps > 0) prefetch(eA, kA, vbuf0, qbuf0);
-    for (int i = 0; i < n_steps; i += 2) {
-        step(i, eA, eB, qbuf0, qbuf1, vbuf0, vbuf1, kA, kB);
-        if (i + 1 >= n_steps) break;
-        step(i + 1, eB, eA, qbuf1, qbuf0, vbuf1, vbuf0, kB, kA);
+    bf16x8 kr[4];
+    u32x4 ep = steps[0], ec = steps[0], en = steps[n_steps > 1 ? 1 : 0];   // every tile has a step (its local block)
+    if (n_steps > 0) {
+        load_k(ec, kr);
+        stage_queries(ec, qbuf0);
     }
-    // row sums to LDS (lane (l16, 0) of the owner wave holds head l16's)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = 0; i <= n_steps; i += 2) {
+        interval(i, ep, ec, en, qbuf0, qbuf1, pbuf0, pbuf1, vbuf0, vbuf1, kr);
+        if (i + 1 > n_steps) break;
+        interval(i + 1, ep, ec, en, qbuf1, qbuf0, pbuf1, pbuf0, vbuf1, vbuf0, kr);
+    }
+    // row sums to LDS: the owner wave adds its four lane groups' partial sums
 #pragma unroll
-    for (int k = 0; k < kTq / kPaWaves; ++k)
-        if (lane < 16) l_fin[k * kPaWaves + wave][l16] = lacc[k][0];
+    for (int k = 0; k < kTq / kPaWaves; ++k) {
+        float su = lsum[k];
+        su += __shfl_xor(su, 16, 64);
+        su += __shfl_xor(su, 32, 64);
+        if (lane < 16) l_fin[k * kPaWaves + wave][l16] = su;
+    }
     __syncthreads();
 
     // ---- normalise and write: lane holds O^T[dim 16w + 4*l4 + r][head l16]
