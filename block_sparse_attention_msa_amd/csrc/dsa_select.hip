@@ -16,7 +16,9 @@
 // Kernel 2 is an exact radix select on order-preserving u32 keys (digits of
 // 12, 12 and 8 bits) that finds the k-th largest key T, then an order-
 // preserving compaction writes every key > T and the lowest-id keys == T, so
-// the output is already in ascending id order and unique.
+// the output is already in ascending id order and unique.  Contexts of up to
+// 65536 keys run it with every key in registers (one burst of loads, no
+// further pass over memory); longer ones stream the scores for each pass.
 #include "common.hpp"
 
 namespace msa {
@@ -190,31 +192,34 @@ __global__ __launch_bounds__(64 * kMhWaves) void dsa_score_heads_kernel(
     }
 }
 
-// Inclusive prefix sum over the 1024 threads of the workgroup.
-__device__ int block_inclusive_scan(int v, int* wave_sums) {
+// Inclusive prefix sum over the kThreads threads of the workgroup (T: int,
+// or a u64 holding two counts that never carry into each other).
+template <int kThreads, typename T>
+__device__ T block_scan(T v, T* wave_sums) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(v, o, 64);
+        const T y = __shfl_up(v, o, 64);
         if (lane >= o) v += y;
     }
     if (lane == 63) wave_sums[wave] = v;
     __syncthreads();
     if (wave == 0) {
-        int sum = lane < kSelThreads / 64 ? wave_sums[lane] : 0;
+        T sum = lane < kThreads / 64 ? wave_sums[lane] : T(0);
 #pragma unroll
-        for (int o = 1; o < kSelThreads / 64; o <<= 1) {
-            const int y = __shfl_up(sum, o, 64);
+        for (int o = 1; o < kThreads / 64; o <<= 1) {
+            const T y = __shfl_up(sum, o, 64);
             if (lane >= o) sum += y;
         }
-        if (lane < kSelThreads / 64) wave_sums[lane] = sum;
+        if (lane < kThreads / 64) wave_sums[lane] = sum;
     }
     __syncthreads();
     if (wave > 0) v += wave_sums[wave - 1];
     __syncthreads();
     return v;
 }
+__device__ int block_inclusive_scan(int v, int* wave_sums) { return block_scan<kSelThreads>(v, wave_sums); }
 
 // Digits of the radix select, most significant first: 12 + 12 + 8 bits.
 // Wide first digits spread the (exponent-concentrated) f32 scores over many
@@ -267,24 +272,26 @@ __device__ __forceinline__ void for_each_score(const float* t, int n, F&& f) {
 
 // Finds the digit (bits `bits` wide) of the rank-`remaining` largest among
 // the histogram counts; returns it through s_digit / s_remaining.
-__device__ __forceinline__ void pick_digit(const int* hist, int bits, int remaining, int* wave_sums,
-                                           uint32_t* s_digit, int* s_remaining) {
+template <int kThreads>
+__device__ __forceinline__ void pick_digit_t(const int* hist, int bits, int remaining, int* wave_sums,
+                                             uint32_t* s_digit, int* s_remaining) {
+    constexpr int kPer = kBins / kThreads;
     const int nb = 1 << bits;
-    int c[kBinsPerThread];
+    int c[kPer];
     int csum = 0;
 #pragma unroll
-    for (int e = 0; e < kBinsPerThread; ++e) {
-        const int dd = kBinsPerThread * threadIdx.x + e;    // descending bin order
+    for (int e = 0; e < kPer; ++e) {
+        const int dd = kPer * threadIdx.x + e;    // descending bin order
         c[e] = dd < nb ? hist[nb - 1 - dd] : 0;
         csum += c[e];
     }
-    const int incl = block_inclusive_scan(csum, wave_sums);
+    const int incl = block_scan<kThreads>(csum, wave_sums);
     if (incl >= remaining && incl - csum < remaining) {
         int before = incl - csum;
 #pragma unroll
-        for (int e = 0; e < kBinsPerThread; ++e) {
+        for (int e = 0; e < kPer; ++e) {
             if (before + c[e] >= remaining) {
-                *s_digit = static_cast<uint32_t>(nb - 1 - (kBinsPerThread * threadIdx.x + e));
+                *s_digit = static_cast<uint32_t>(nb - 1 - (kPer * threadIdx.x + e));
                 *s_remaining = remaining - before;
                 break;
             }
@@ -292,6 +299,10 @@ __device__ __forceinline__ void pick_digit(const int* hist, int bits, int remain
         }
     }
     __syncthreads();
+}
+__device__ __forceinline__ void pick_digit(const int* hist, int bits, int remaining, int* wave_sums,
+                                           uint32_t* s_digit, int* s_remaining) {
+    pick_digit_t<kSelThreads>(hist, bits, remaining, wave_sums, s_digit, s_remaining);
 }
 
 __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __restrict__ scores,
@@ -437,8 +448,184 @@ __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __re
     if (tid == 0) n_sel[i] = top_k;
 }
 
+// ---------------------------------------------------------------------------
+// Contexts of at most 65536 keys: the same selection with every key held in
+// registers.  1024 threads; lane l of wave w holds the keys of ids 4096 w +
+// 256 r + 4 l + c (round r < 16, c < 4), read in one burst of coalesced
+// 16-byte loads (the scores come from other compute units' writes, so each
+// pass over memory would cost a full memory latency).  The three digits are
+// histogrammed from the registers: the first over eight copies (by lane),
+// because the exponent-heavy keys pile into few bins, the next two only for
+// the keys that match the prefix found so far.  The compaction counts each
+// wave's keys above T and equal to T (one scan over the waves gives each
+// wave its output offset), then walks the rounds in id order: a scan of the
+// lanes' counts places every kept key, into an LDS copy of the output that is
+// written out coalesced at the end.  No step branches per
+// key: a key that is not counted or kept goes to a spare bin or slot of its
+// lane instead.
+// ---------------------------------------------------------------------------
+constexpr int kRegThreads = 1024;
+constexpr int kRegWaves = kRegThreads / 64;
+constexpr int kRegRounds = 16;
+constexpr int kRegPer = 4 * kRegRounds;                   // keys per lane
+constexpr int kRegKeys = kRegThreads * kRegPer;           // 65536
+constexpr int kHistCopies = 8;
+constexpr int kTopKMax = 4096;
+
+__global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float* __restrict__ scores,
+                                                                    int64_t stride,
+                                                                    const int32_t* __restrict__ q_pos,
+                                                                    int top_k, int32_t* __restrict__ sel,
+                                                                    int32_t* __restrict__ n_sel) {
+    __shared__ int hist[kHistCopies][kBins + 64];    // + one spare bin per lane: where keys past the last go
+    __shared__ int32_t ostage[kTopKMax + 64];        // the output, in order (+ one spare slot per lane)
+    __shared__ int wave_sums[kRegWaves];
+    __shared__ uint32_t wave_tot[kRegWaves];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_remaining;
+    __shared__ uint32_t s_T;
+    const int64_t i = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n = q_pos[i] + 1;
+    const float* t = scores + i * stride;
+    int32_t* out = sel + i * top_k;
+    if (n <= top_k) {                                   // every visible key is kept
+        for (int j = tid; j < top_k; j += kRegThreads) out[j] = j < n ? j : -1;
+        if (tid == 0) n_sel[i] = n;
+        return;
+    }
+    // keys past the last are 0, below the key of every score (that of -inf
+    // is 0x007fffff), so they never match a prefix or the threshold.  Every
+    // load is unconditional (from inside the row), so that all are in
+    // flight together.
+    const int base = 4096 * wave + 4 * lane;            // id of this lane's key (r, c): base + 256 r + c
+    uint32_t rk[kRegPer];
+    const int last4 = static_cast<int>(stride) - 4;    // the row holds stride >= n scores
+    {
+        f32x4 x[kRegRounds];
+#pragma unroll
+        for (int r = 0; r < kRegRounds; ++r) x[r] = *reinterpret_cast<const f32x4*>(t + min(base + 256 * r, last4));
+        // (a mask, not a select: a select becomes a branch per key with a
+        // wait for its load inside, which serialises the loads)
+#pragma unroll
+        for (int r = 0; r < kRegRounds; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                rk[4 * r + c] = ordered_key(x[r][c]) & (0u - static_cast<uint32_t>(base + 256 * r + c < n));
+    }
+    // ---- digit 1: top 12 bits (keys past the last go to the lane's spare bin)
+    for (int b = tid; b < kHistCopies * (kBins + 64); b += kRegThreads) (&hist[0][0])[b] = 0;
+    __syncthreads();
+    {
+        int* hc = hist[lane % kHistCopies];
+#pragma unroll
+        for (int e = 0; e < kRegPer; ++e) {
+            const uint32_t key = rk[e];
+            atomicAdd(&hc[key != 0u ? static_cast<int>(key >> 20) : kBins + lane], 1);
+        }
+    }
+    __syncthreads();
+    for (int b = tid; b < kBins; b += kRegThreads) {
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kHistCopies; ++k) sum += hist[k][b];
+        hist[0][b] = sum;
+    }
+    __syncthreads();
+    pick_digit_t<kRegThreads>(hist[0], 12, top_k, wave_sums, &s_digit, &s_remaining);
+    uint32_t prefix = s_digit << 20, mask = 0xfff00000u;
+    int remaining = s_remaining;
+    // ---- digits 2 and 3 (12 and 8 bits) over the keys with the prefix
+#pragma unroll
+    for (int pass = 1; pass < 3; ++pass) {
+        const int bits = kDigitBits[pass];
+        const int shift = pass == 1 ? 8 : 0;
+        const uint32_t dmask = (1u << bits) - 1;
+        for (int b = tid; b < kBins; b += kRegThreads) hist[0][b] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < kRegPer; ++e) {
+            const uint32_t key = rk[e];
+            atomicAdd(&hist[0][(key & mask) == prefix ? static_cast<int>((key >> shift) & dmask) : kBins + lane], 1);
+        }
+        __syncthreads();
+        pick_digit_t<kRegThreads>(hist[0], bits, remaining, wave_sums, &s_digit, &s_remaining);
+        prefix |= s_digit << shift;
+        mask |= dmask << shift;
+        remaining = s_remaining;
+    }
+    const uint32_t T = prefix;          // the top_k-th largest key; `remaining` keys equal to it are kept
+    // ---- compaction: each wave's counts, packed as (keys > T) + (keys == T)
+    // << 16 (at most 4096 per wave, and below 2^16 summed over the earlier
+    // waves)
+    uint32_t v = 0;
+#pragma unroll
+    for (int e = 0; e < kRegPer; ++e) v += (rk[e] > T ? 1u : 0u) + (rk[e] == T ? 0x10000u : 0u);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) wave_tot[wave] = v;
+    if (tid == 0) s_T = T;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kRegWaves; ++w)
+        if (w < wave) before += wave_tot[w];
+    int G = static_cast<int>(before & 0xffffu), Q = static_cast<int>(before >> 16);   // keys before this round
+    // T read back from LDS, so that the compares are redone here rather than
+    // kept from the count above (the lane masks would not fit in SGPRs); the
+    // ids likewise are computed afresh from an opaque copy of `base` (kept
+    // from the loads, their 16 registers would push keys out to scratch)
+    const uint32_t T2 = s_T;
+    int base2 = base;
+    asm volatile("" : "+v"(base2));
+#pragma unroll
+    for (int r = 0; r < kRegRounds; ++r) {
+        // this lane's counts in the round, packed; their exclusive prefix
+        // over the lanes places its keys after the round's earlier ones
+        uint32_t lc = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lc += (rk[4 * r + c] > T2 ? 1u : 0u) + (rk[4 * r + c] == T2 ? 0x10000u : 0u);
+        uint32_t sc = lc;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(sc, o, 64);
+            if (lane >= o) sc += y;
+        }
+        const uint32_t round_tot = __shfl(sc, 63, 64);
+        int gb = G + static_cast<int>((sc - lc) & 0xffffu), qb = Q + static_cast<int>((sc - lc) >> 16);
+        G += static_cast<int>(round_tot & 0xffffu);
+        Q += static_cast<int>(round_tot >> 16);
+        const int j = base2 + 256 * r;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t key = rk[4 * r + c];
+            const bool gt = key > T2, eq = key == T2;
+            const int slot = gt ? gb + min(qb, remaining) : (eq && qb < remaining) ? gb + qb : kTopKMax + lane;
+            ostage[slot] = j + c;
+            gb += gt;
+            qb += eq;
+        }
+    }
+    __syncthreads();
+    for (int k = tid; k < top_k; k += kRegThreads) out[k] = ostage[k];
+    if (tid == 0) n_sel[i] = top_k;
+}
+
 int64_t score_stride(int32_t max_pos) {
     return ((static_cast<int64_t>(max_pos) + 1 + 63) / 64) * 64;
+}
+
+hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int64_t n_q, int32_t max_pos,
+                       int top_k, int32_t* sel, int32_t* n_sel, hipStream_t s) {
+    if (static_cast<int64_t>(max_pos) + 1 <= kRegKeys)
+        hipLaunchKernelGGL(dsa_topk_regs_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kRegThreads), 0, s, scores,
+                           stride, pos, top_k, sel, n_sel);
+    else
+        hipLaunchKernelGGL(dsa_topk_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kSelThreads), 0, s, scores,
+                           stride, pos, top_k, sel, n_sel);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -458,9 +645,7 @@ hipError_t launch_dsa_select(const uint16_t* dsa_k, const Pager& pg, const uint1
                        pg, q_idx, stream, pos, scores, stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dsa_topk_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kSelThreads), 0, s, scores,
-                       stride, pos, top_k, sel, n_sel);
-    return hipGetLastError();
+    return launch_topk(scores, stride, pos, n_q, max_pos, top_k, sel, n_sel, s);
 }
 
 hipError_t launch_dsa_select_heads(const uint16_t* dsa_k, const Pager& pg, const uint16_t* q_idx_h,
@@ -484,9 +669,7 @@ hipError_t launch_dsa_select_heads(const uint16_t* dsa_k, const Pager& pg, const
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dsa_topk_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kSelThreads), 0, s, scores,
-                       stride, pos, top_k, sel, n_sel);
-    return hipGetLastError();
+    return launch_topk(scores, stride, pos, n_q, max_pos, top_k, sel, n_sel, s);
 }
 
 }  // namespace msa

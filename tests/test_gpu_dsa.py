@@ -81,6 +81,31 @@ def test_dsa_full_16x64k():
     _dsa_parity(W.CONFIGS["dsa_16x64k"])
 
 
+def test_dsa_topk_context_over_64k_exact():
+    """Contexts above 65536 keys take the streaming top-k (the register one
+    holds at most 65536 keys per query): integer scores, ties everywhere,
+    bit-exact against the oracle, one query below and one above 65536."""
+    S, cap, top_k = 1, 70000, 2048
+    rng = np.random.default_rng(23)
+    k_rot = rng.integers(-2, 3, size=(S, cap, 128)).astype(np.float16)
+    pos = np.array([69999, 40000], np.int32)
+    stream = np.array([0, 0], np.int32)
+    q = rng.integers(-1, 2, size=(2, 128)).astype(np.float16)
+    log("[dsa] exact ties, context 70000")
+    dims = M.dsa_dims(top_k, W.SCALE)
+    cache = M.make_cache(k=torch.zeros((S, cap, 4, 128), dtype=torch.bfloat16, device=DEV),
+                         v=torch.zeros((S, cap, 4, 128), dtype=torch.bfloat16, device=DEV),
+                         dsa_k=torch.from_numpy(k_rot).to(DEV))
+    sel = torch.empty((2, top_k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty(2, dtype=torch.int32, device=DEV)
+    ws = torch.empty(M.workspace_bytes(dims, M.DSA_OP_SELECT, 2, int(pos.max())), dtype=torch.uint8, device=DEV)
+    M.dsa_select(dims, cache, torch.from_numpy(q).to(DEV), dev(stream), dev(pos), int(pos.max()), sel, n_sel, ws)
+    torch.cuda.synchronize()
+    o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
+    assert np.array_equal(n_sel.cpu().numpy(), o_nsel)
+    assert np.array_equal(sel.cpu().numpy(), o_sel), "selection differs from the oracle"
+
+
 @pytest.mark.parametrize("top_k", [2048, 64])
 def test_dsa_topk_with_ties_exact(top_k):
     """Integer keys and queries make every score an exact small integer, so
