@@ -213,8 +213,6 @@ struct AttendArgs {
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
-// Prefill attention for the consecutive positions pos0 .. pos0 + n_q - 1 of
-// one stream (MSA blocks); ws holds the per-tile step lists.
 // Indexer projection: split-K GEMM into the workspace, then norm + RoPE +
 // writes (q to idx_q, k appended to the f32 or fp16 index cache).
 int project_n_split(int64_t n_tok);
@@ -223,7 +221,11 @@ hipError_t launch_index_project(const float* x, int d_model, const float* w_q, c
                                 const float* g_q, const float* g_k, float eps, float theta, int rot_dim,
                                 const int32_t* stream, const int32_t* pos, int64_t n_tok, float* idx_q,
                                 float* idx_k, uint16_t* idx_k16, const Pager& pg, void* ws, hipStream_t s);
-size_t prefill_attend_ws_bytes(int64_t n_q, int top_k);
+// Prefill attention for the consecutive positions pos0 .. pos0 + n_q - 1 of
+// one stream (MSA blocks); ws (prefill_attend_ws_bytes(n_q, top_k,
+// pos0 + n_q - 1) bytes) holds the per-tile step lists and V of the used
+// blocks transposed.
+size_t prefill_attend_ws_bytes(int64_t n_q, int top_k, int32_t max_pos);
 hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pager& pg, const uint16_t* q,
                                  int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
                                  float scale, float* out, void* ws, hipStream_t s);

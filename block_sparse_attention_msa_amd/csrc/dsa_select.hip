@@ -226,7 +226,6 @@ __device__ int block_inclusive_scan(int v, int* wave_sums) { return block_scan<k
 // histogram bins, which keeps LDS atomic collisions rare.
 constexpr int kDigitBits[3] = {12, 12, 8};
 constexpr int kBins = 4096;
-constexpr int kBinsPerThread = kBins / kSelThreads;   // 4
 
 // One workgroup of 1024 threads per query, three streaming passes over the
 // query's scores (16-byte loads, coalesced across the workgroup):

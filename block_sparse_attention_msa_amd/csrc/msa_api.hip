@@ -247,7 +247,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, dims->block));
         case MSA_OP_ATTEND_PREFILL: {
             // the larger of the bf16 path's and the quantized-cache path's needs
-            const size_t a = align256(msa::prefill_attend_ws_bytes(n_q, dims->top_k));
+            const size_t a = align256(msa::prefill_attend_ws_bytes(n_q, dims->top_k, max_pos));
             const size_t b = align256(prefill_quant_ws(n_q, dims->top_k));
             return a > b ? a : b;
         }

@@ -12,31 +12,37 @@
 // from that XCD's L2).  A small pre-kernel turns the selections into each
 // tile's step list: one step per union block and up to kPb of the tile's
 // queries that selected it (a block chosen by more queries, e.g. the shared
-// local block, becomes several steps).
+// local block, becomes several steps), and marks the blocks any tile uses;
+// a second one copies K and V of each marked block into the order in which
+// the matrix-core operands take them (64 KiB per block and group), so that
+// the sweep loads every operand as whole contiguous KiB.
 //
 // Every step is spread evenly over all eight waves, whatever queries it
 // holds: for S = Q K^T wave w takes keys 16w .. 16w+15 of the block for every
 // query of the step and writes its bf16 probabilities to LDS; for O += P V
 // wave w owns output dims 16w .. 16w+15 of all 32 queries of the tile, so the
 // 16-head x 128-dim accumulators of the whole tile live in registers, one
-// 16 x 16 slice per wave and query.  The softmax needs no exchange of maxima:
-// each (query, head) uses one fixed reference for the whole sweep (its score
-// against its own key, always selected), and a block whose probabilities
-// would pass 2^64 is recomputed against a raised reference (rare).  The
-// owner wave of each query sums the bf16 probabilities it reads as P V
-// operands (v_dot2 against ones), so the normalisation sums exactly the
-// weights applied.
+// 16 x 16 slice per wave and query.  Both operands a wave needs from the
+// block -- its 16 keys of K and its 16 dims of V^T, 4 KiB each -- are loaded
+// from the rearranged copy straight into its registers: no K or V passes
+// through LDS, and each wave waits only for its own loads.  K of the next
+// step is loaded once this step's scores are formed, V^T of this step once
+// the previous step's products are done, so each load has the other half of
+// a step to land.  LDS carries only the step's queries (copied in with
+// global_load_lds one step ahead) and the probabilities exchanged between
+// the two halves.
+//
+// The softmax needs no exchange of maxima: each (query, head) uses one fixed
+// reference for the whole sweep (its score against its own key, always
+// selected), and a block whose probabilities would pass 2^64 is recomputed
+// against a raised reference (rare).  The owner wave of each query sums the
+// bf16 probabilities it reads as P V operands (v_dot2 against ones), so the
+// normalisation sums exactly the weights applied.
 //
 // The sweep is pipelined by one step with a single barrier per step: the
 // interval between barriers i - 1 and i holds the scores of step i and the
-// products P V of step i - 1, with probabilities, V and the step's queries
-// in two-deep LDS rings (K goes straight from memory into the registers of
-// the wave that uses it and never passes through LDS).  During the interval
-// the copies for the next interval are issued, spread over its phases (step
-// i + 1's queries as it begins, half of step i's V, then step i + 1's K and
-// the other half of V once the scores are done): the copy engine accepts
-// about 49 bytes per clock per compute unit, so copies issued all at once
-// stall every wave until they drain.
+// products P V of step i - 1, with probabilities and the step's queries in
+// two-deep LDS rings.
 #include "common.hpp"
 
 namespace msa {
@@ -45,24 +51,21 @@ namespace {
 constexpr int kPaWaves = 8;
 constexpr int kPaThreads = 64 * kPaWaves;
 constexpr int kTq = 32;                     // queries per tile (one mask bit each)
-constexpr int kPb = 5;                      // queries per step
+constexpr int kPb = 8;                      // queries per step
 constexpr int kRowBytes = kHeadDim * 2;     // one group's K or V row, one head's Q row: 256 B
-constexpr int kBufBytes = kBlock * kRowBytes;        // 32 KiB: K (or V) of one block
+constexpr int kVtElems = kBlock * kHeadDim;           // V^T of one block and group: 32 KiB
 constexpr int kQBytes = kHeadsPerGroup * kRowBytes;  // 4 KiB: one query's 16 heads
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr int kStepsThreads = 256;
+constexpr int kVtThreads = 256;
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// Rows are stored with their 16 segments permuted by seg ^ f(row & 15), f a
-// 4-bit rotate: f is one-to-one on 16 consecutive rows (operand reads of 16
-// rows at one segment) and f >> 1 is one-to-one on 8 consecutive rows (the
-// transposing V reads take a 32-byte pair of segments from each of 8 rows per
-// half-wave), so neither read pattern has bank conflicts.
+// Query rows are stored with their 16 segments permuted by seg ^ f(row & 15),
+// f a 4-bit rotate, one-to-one on 16 consecutive rows, so that the operand
+// reads of 16 rows at one segment have no bank conflicts.
 __device__ __forceinline__ int rowperm(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 // Byte offset of 16-byte segment `seg` of row `row` in a staged buffer.
 __device__ __forceinline__ int swz(int row, int seg) { return row * kRowBytes + ((seg ^ rowperm(row)) << 4); }
@@ -84,11 +87,14 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
 
+
 // ---------------------------------------------------------------------------
 // Step lists.  Workgroup (tile, g): entry = {block id, mask of tile queries,
 // first cache row of the block (low, high word)}, ascending block order, at
 // most kPb mask bits per entry.  The row is resolved here, through the block
-// table of a paged cache, so that the sweep does no table lookups.
+// table of a paged cache, so that the sweep does no table lookups.  Every
+// block in the tile's union is marked in used[g][block] (cleared first by
+// prefill_clear_kernel), so that only those blocks of V are transposed.
 // ---------------------------------------------------------------------------
 struct StepArgs {
     const int32_t* sel;
@@ -101,7 +107,13 @@ struct StepArgs {
     int32_t stream;
     int32_t* counts;
     u32x4* steps;
+    uint32_t* used;
 };
+
+__global__ __launch_bounds__(256) void prefill_clear_kernel(uint32_t* used, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) used[i] = 0u;
+}
 
 __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a) {
     const int g = blockIdx.x % kGroups;
@@ -141,7 +153,9 @@ __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a
     u32x4* out = a.steps + static_cast<int64_t>(blockIdx.x) * a.max_steps;
     for (int b = b0; b < b1; ++b) {
         uint32_t m = qmask[b];
-        const uint64_t row = m != 0u ? static_cast<uint64_t>(a.pg.block_row(a.stream, b)) : 0u;
+        if (m == 0u) continue;
+        a.used[g * a.nblk + b] = 1u;           // every tile that uses the block writes the same value
+        const uint64_t row = static_cast<uint64_t>(a.pg.block_row(a.stream, b));
         while (m != 0u) {
             uint32_t sub = 0u;
             for (int i = 0; i < kPb && m != 0u; ++i) {
@@ -157,23 +171,101 @@ __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a
 }
 
 // ---------------------------------------------------------------------------
+// K and V of the used blocks, rearranged into matrix-core operand order so
+// that the sweep reads each wave's operands as four contiguous KiB (a load
+// instruction then covers eight whole 128-byte lines; the 16 rows x 64 bytes
+// of a load straight from the cache rows cost the load unit about 2.5 times
+// as much).  Block b of group g occupies 2 * kVtElems bf16 at
+// kv + (g * nblk + b) * 2 * kVtElems, each half 2048 slots of 16 bytes,
+// slot (4w + c) * 64 + lane (lane = 16 * l4 + l16):
+//   K half: K[key 16w + l16][dims 32c + 8*l4 .. +7], the A operand of wave
+//           w's score product with dims 32c .. 32c + 31;
+//   V half: V[key][dim 16w + l16] for keys 32c + 4*l4 + j (j = 0..3) and
+//           32c + 16 + 4*l4 + j, the A operand of wave w's product with
+//           chunk c of the probabilities, in the key order the score
+//           products write them.
+// Keys past the chunk's last key are zero (they are masked, and their
+// probabilities are zero).
+// ---------------------------------------------------------------------------
+struct KvArgs {
+    const uint16_t* k;
+    const uint16_t* v;
+    Pager pg;
+    int32_t stream;
+    int nblk;
+    int last_row;
+    const uint32_t* used;
+    uint16_t* kv;
+};
+
+__global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
+    const int g = blockIdx.x % kGroups;
+    const int b = blockIdx.x / kGroups;
+    if (a.used[g * a.nblk + b] == 0u) return;           // workgroup-uniform
+    constexpr int kPitch = kHeadDim + 8;                 // 272-byte rows: the gathers below hit distinct banks
+    __shared__ __attribute__((aligned(16))) uint16_t tk[kBlock][kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t tv[kBlock][kPitch];
+    const int64_t row0 = a.pg.block_row(a.stream, b);
+    const int key0 = b * kBlock;
+    for (int s = threadIdx.x; s < kBlock * 16; s += kVtThreads) {
+        const int r = s >> 4, seg = s & 15;
+        u32x4 xk = u32x4{0u, 0u, 0u, 0u}, xv = xk;
+        if (key0 + r <= a.last_row) {
+            const int64_t off = ((row0 + r) * kGroups + g) * kHeadDim + 8 * seg;
+            xk = *reinterpret_cast<const u32x4*>(a.k + off);
+            xv = *reinterpret_cast<const u32x4*>(a.v + off);
+        }
+        *reinterpret_cast<u32x4*>(&tk[r][8 * seg]) = xk;
+        *reinterpret_cast<u32x4*>(&tv[r][8 * seg]) = xv;
+    }
+    __syncthreads();
+    uint16_t* dst = a.kv + (static_cast<int64_t>(g) * a.nblk + b) * 2 * kVtElems;
+    for (int o = threadIdx.x; o < kVtElems / 8; o += kVtThreads) {
+        const int lane = o & 63, c = (o >> 6) & 3, w = o >> 8;
+        const int l16 = lane & 15, l4 = lane >> 4;
+        *reinterpret_cast<u32x4*>(dst + 8 * o) = *reinterpret_cast<const u32x4*>(&tk[16 * w + l16][32 * c + 8 * l4]);
+        const int dim = 16 * w + l16;
+        const int k0 = 32 * c + 4 * l4;
+        uint32_t x[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            x[j] = static_cast<uint32_t>(tv[k0 + 2 * j][dim]) | (static_cast<uint32_t>(tv[k0 + 2 * j + 1][dim]) << 16);
+            x[2 + j] = static_cast<uint32_t>(tv[k0 + 16 + 2 * j][dim]) |
+                       (static_cast<uint32_t>(tv[k0 + 16 + 2 * j + 1][dim]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + kVtElems + 8 * o) = u32x4{x[0], x[1], x[2], x[3]};
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Attention sweep.
 // ---------------------------------------------------------------------------
 struct PaArgs {
     const uint16_t* k;
-    const uint16_t* v;
+    const uint16_t* kv;
     Pager pg;
     const uint16_t* q;
     int32_t stream;
     int32_t pos0;
     int64_t n_q;
-    int64_t last_row;
+    int nblk;
     int max_steps;
     const int32_t* counts;
     const u32x4* steps;
     float scale;
     float* out;
 };
+
+// Waits until at most 4 vector-memory loads of this wave are in flight (the
+// four V^T loads issued last), its LDS accesses are done, then the
+// workgroup barrier.  Loads return in issue order, so everything issued
+// before those four -- the next step's query copies and keys -- has landed.
+__device__ __forceinline__ void step_barrier() {
+    __builtin_amdgcn_s_waitcnt(0x0074);        // vmcnt 4, expcnt 7, lgkmcnt 0
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a) {
     const int g = blockIdx.x % kGroups;
@@ -189,13 +281,9 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     const __attribute__((address_space(4))) u32x4* steps_s =
         (const __attribute__((address_space(4))) u32x4*)(reinterpret_cast<uintptr_t>(steps));
 
-    // Two-deep rings (by step parity) for V, the step's queries and its
+    // Two-deep rings (by step parity) for the step's queries and its
     // probabilities.  Separate objects, so that reads of one are not made to
-    // wait for copies in flight into another.  K does not pass through LDS:
-    // each wave loads its own 16 keys straight into the registers the score
-    // products read.
-    __shared__ __attribute__((aligned(16))) char vbuf0[kBufBytes];
-    __shared__ __attribute__((aligned(16))) char vbuf1[kBufBytes];
+    // wait for copies in flight into another.
     __shared__ __attribute__((aligned(16))) char qbuf0[kPb][kQBytes];
     __shared__ __attribute__((aligned(16))) char qbuf1[kPb][kQBytes];
     __shared__ __attribute__((aligned(16))) char pbuf0[kPb][kQBytes];
@@ -240,8 +328,8 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     }
     // O^T slices (dims 16w + 4*l4 + r, head l16) of all tile queries, and
     // the row sums of the queries t with t % 8 == w: lane (l16, l4) sums the
-    // bf16 probabilities of head l16 it reads as operands (keys 32c + 8*l4
-    // .. +7), so that the normalisation sums exactly the weights applied
+    // bf16 probabilities of head l16 it reads as operands, so that the
+    // normalisation sums exactly the weights applied
     f32x4 acc[kTq];
     float lsum[kTq / kPaWaves];
 #pragma unroll
@@ -254,49 +342,28 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     int qoff[4];                                // Q rows (heads) l16, dims 32*ks4 + 8*l4 ..
 #pragma unroll
     for (int ks4 = 0; ks4 < 4; ++ks4) qoff[ks4] = swz(l16, 4 * ks4 + l4);
-    // V: row 4*l4 + l16/4 (+ 32c, + 16), dims 16w + 4*(l16 % 4) .. +3
-    const int voff = swz(4 * l4 + (l16 >> 2), 2 * wave + ((l16 & 3) >> 1)) + (l16 & 1) * 8;
     // P exchange: chunk c = keys 32c .. 32c+31 is written by waves 2c (keys
     // 32c + 4*l4 + r) and 2c+1 (keys 32c + 16 + 4*l4 + r) and read as the
-    // 8-key B operand of lane (l16, l4) of every wave.
+    // 8-key B operand of lane (l16, l4) of every wave; V^T holds the same
+    // key order.
     const int pw_off = (((wave >> 1) * 4 + l4) * 16 + l16) * 16 + (wave & 1) * 8;
     const int pr_off = (l4 * 16 + l16) * 16;   // + 1 KiB per chunk
 
-    // Copies of V.  Slot s (16 bytes) of a staged 256-byte-row buffer holds
-    // segment (s % 16) ^ f(row) of row s / 16.  One call issues instruction j
-    // (of 4) of this wave's share of the block.
-    const int last_row = static_cast<int>(a.last_row);       // positions are int32
-    uint32_t soff[4];                                          // lane's source offset (elements) in a block
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int slot = 256 * wave + 64 * j + lane;
-        const int row = slot >> 4;
-        soff[j] = static_cast<uint32_t>(row * kGroups * kHeadDim + 8 * ((slot & 15) ^ rowperm(row)));
-    }
-    // e: the block's step entry (block id, mask, first cache row)
-    auto stage_v = [&](const u32x4& e, char* dst, int j) {
-        const int row0 = static_cast<int>(e[0]) * kBlock;
-        const int64_t rb = static_cast<int64_t>((static_cast<uint64_t>(e[3]) << 32) | e[2]);
-        const uint16_t* src = a.v + (rb * kGroups + g) * kHeadDim;
-        uint32_t o = soff[j];
-        if (row0 + kBlock - 1 > last_row) {                   // wave-uniform: the chunk's last block
-            // rows past the chunk's last key are read from that key's row:
-            // they are masked for every query
-            const int row = (256 * wave + 64 * j + lane) >> 4;
-            o -= static_cast<uint32_t>((row - min(row, last_row - row0)) * kGroups * kHeadDim);
-        }
-        __builtin_amdgcn_global_load_lds(src + o, LDS_PTR(void, dst + (256 * wave + 64 * j) * 16), 16, 0, 0);
-    };
-    // K of this wave's keys 16w + l16 into registers: lane (l16, l4) holds
-    // dims 32*ks4 + 8*l4 .. +7 in kr[ks4], the A operand of the score products.
+    // e: a step entry (block id, mask, first cache row).  This wave's
+    // operands of the block from the rearranged copy, four contiguous KiB
+    // each: K of keys 16w .. 16w + 15 (kr[c] the A operand of the score
+    // product over dims 32c .. 32c + 31) and V^T of dims 16w .. 16w + 15
+    // (vr[c] the A operand of the product with probability chunk c).
+    const uint16_t* kv_g = a.kv + static_cast<int64_t>(g) * a.nblk * 2 * kVtElems + (wave * 4 * 64 + lane) * 8;
     auto load_k = [&](const u32x4& e, bf16x8 (&kr)[4]) {
-        const int row0 = static_cast<int>(e[0]) * kBlock;
-        const int64_t rb = static_cast<int64_t>((static_cast<uint64_t>(e[3]) << 32) | e[2]);
-        int row = 16 * wave + l16;
-        if (row0 + kBlock - 1 > last_row) row = min(row, last_row - row0);   // past the chunk's last key: masked
-        const uint16_t* src = a.k + ((rb + row) * kGroups + g) * kHeadDim + 8 * l4;
+        const uint16_t* src = kv_g + static_cast<int64_t>(e[0]) * 2 * kVtElems;
 #pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) kr[ks4] = *reinterpret_cast<const bf16x8*>(src + 32 * ks4);
+        for (int c = 0; c < 4; ++c) kr[c] = *reinterpret_cast<const bf16x8*>(src + c * 64 * 8);
+    };
+    auto load_v = [&](const u32x4& e, bf16x8 (&vr)[4]) {
+        const uint16_t* src = kv_g + static_cast<int64_t>(e[0]) * 2 * kVtElems + kVtElems;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vr[c] = *reinterpret_cast<const bf16x8*>(src + c * 64 * 8);
     };
     // Q of query t into slot p of qdst: instruction j (of 4) is issued by wave (4p + j) % 8.
     auto stage_q = [&](char (*qdst)[kQBytes], int p, int t) {
@@ -365,12 +432,13 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
     // of step i and the products O += P V of step i - 1, so that the two
     // overlap and each step costs one barrier.  ep, ec, en hold the entries
     // of steps i - 1, i, i + 1 and move on by one at the end.  Buffers by
-    // parity: qs / ps / vs hold step i's queries, probabilities and V (copied
-    // during this interval); po / vo step i - 1's probabilities and V; qo
-    // receives step i + 1's queries once step i - 1 is finished with them.
-    // kr holds step i's K and receives step i + 1's once the scores are done.
+    // parity: qs / ps hold step i's queries and probabilities; po step
+    // i - 1's probabilities; qo receives step i + 1's queries once step
+    // i - 1 is finished with them.  kr holds step i's K and receives step
+    // i + 1's once the scores are done; vr holds step i - 1's V^T and
+    // receives step i's once the products are done.
     auto interval = [&](int i, u32x4& ep, u32x4& ec, u32x4& en, char (*qs)[kQBytes], char (*qo)[kQBytes],
-                        char (*ps)[kQBytes], char (*po)[kQBytes], char* vs, const char* vo, bf16x8 (&kr)[4]) {
+                        char (*ps)[kQBytes], char (*po)[kQBytes], bf16x8 (&kr)[4], bf16x8 (&vr)[4]) {
         const bool has_s = i < n_steps;
         const bool has_pv = i >= 1;
         const bool more = i + 1 < n_steps;
@@ -429,10 +497,6 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         if (more) stage_queries(en, qo);
 
         // ---- step i: S, P for this wave's 16 keys, every query of the step
-        if (has_s) {
-            stage_v(ec, vs, 0);
-            stage_v(ec, vs, 1);
-        }
         float xmax = -INFINITY;
         if (has_s) {
             const int b = static_cast<int>(ec[0]);
@@ -459,27 +523,19 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                 xmax = fmaxf(xmax, write_p(score(kr, qs, p, qpos0 + t, b), ps, p, m_ref[t][l16]));
             }
         }
-        if (more) load_k(en, kr);                               // step i's keys are no longer needed
-        if (has_s) {
-            stage_v(ec, vs, 2);
-            stage_v(ec, vs, 3);
-        }
+        // step i + 1's keys (or, past the end, step i's again: the loads are
+        // unconditional so that the wait counts stay static)
+        load_k(en, kr);
 
         // ---- step i - 1: O^T += V^T P^T for this wave's 16 dims, every
         // query of the step, and the row sums of its own queries
         if (has_pv) {
+            // this wave's V^T of step i - 1 (loaded before this interval's
+            // query copies and keys) is in place once at most the four key
+            // loads are outstanding
+            __builtin_amdgcn_s_waitcnt(0x0074);         // vmcnt 4, expcnt 7, lgkmcnt 0
             const uint32_t mask = ep[1];
             const int np = __builtin_popcount(mask);
-            bf16x8 vop[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(v4i16, vo + kChunk * c * kRowBytes + voff));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(v4i16, vo + (kChunk * c + 16) * kRowBytes + voff));
-                vop[c] = __builtin_shufflevector(__builtin_bit_cast(bf16x4_t, lo), __builtin_bit_cast(bf16x4_t, hi),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
-            }
             // the next query's P operand is read as soon as this one's
             // products have been issued
             bf16x8 pt[4];
@@ -496,7 +552,7 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                         if (own) lsum[t / kPaWaves] *= al;
                     }
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[t] = mfma_16x16x32_bf16(vop[c], pt[c], acc[t]);
+                    for (int c = 0; c < 4; ++c) acc[t] = mfma_16x16x32_bf16(vr[c], pt[c], acc[t]);
                     if (own) {
                         const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);   // {1, 1}
                         float su = lsum[t / kPaWaves];
@@ -519,32 +575,39 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
                 }
             }
         }
+        // step i's V^T for the products of the next interval (past the end:
+        // the last step's again)
+        load_v(ec, vr);
         if (__builtin_amdgcn_ballot_w64(xmax > kOverflow) != 0 && lane == 0) redo_step[i & 1] = i;
         // step i + 2's entry: a scalar load, issued last because every
         // wait for an LDS read would also wait for it
         u32x4 e2 = en;
         if (i + 2 < n_steps) e2 = steps_s[i + 2];
-        // barrier i: step i's probabilities and V, step i + 1's K and
-        // queries have landed
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        // barrier i: step i's probabilities, step i + 1's queries and keys
+        // are in place (step i's V^T may still be on its way)
+        step_barrier();
         ep = ec;
         ec = en;
         en = e2;
     };
 
-    bf16x8 kr[4];
-    u32x4 ep = steps[0], ec = steps[0], en = steps[n_steps > 1 ? 1 : 0];   // every tile has a step (its local block)
+    // (every tile has a step, its local block, when the selection holds it;
+    // a tile without steps skips the sweep rather than read an entry)
     if (n_steps > 0) {
+        bf16x8 kr[4], vr[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vr[c] = bf16x8{};   // first loaded at the end of interval 0
+        u32x4 ep = steps[0], ec = steps[0], en = steps[n_steps > 1 ? 1 : 0];
         load_k(ec, kr);
         stage_queries(ec, qbuf0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int i = 0; i <= n_steps; i += 2) {
-        interval(i, ep, ec, en, qbuf0, qbuf1, pbuf0, pbuf1, vbuf0, vbuf1, kr);
-        if (i + 1 > n_steps) break;
-        interval(i + 1, ep, ec, en, qbuf1, qbuf0, pbuf1, pbuf0, vbuf1, vbuf0, kr);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int i = 0; i <= n_steps; i += 2) {
+            interval(i, ep, ec, en, qbuf0, qbuf1, pbuf0, pbuf1, kr, vr);
+            if (i + 1 > n_steps) break;
+            interval(i + 1, ep, ec, en, qbuf1, qbuf0, pbuf1, pbuf0, kr, vr);
+        }
+        __builtin_amdgcn_s_waitcnt(0);                  // the last (unused) loads
     }
     // row sums to LDS: the owner wave adds its four lane groups' partial sums
 #pragma unroll
@@ -568,23 +631,49 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
 }
 
 int64_t n_tiles_of(int64_t n_q) { return (n_q + kTq - 1) / kTq; }
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Workspace layout: step counts [n_wg] i32 | used flags [4][nblk] u32 |
+// step lists [n_wg][kTq * top_k] of 16 bytes | rearranged K and V
+// [4][nblk][2][kVtElems] bf16.
+struct WsLayout {
+    size_t counts, used, steps, kv, total;
+};
+WsLayout ws_layout(int64_t n_q, int top_k, int nblk) {
+    const int64_t n_wg = n_tiles_of(n_q) * kGroups;
+    WsLayout l;
+    l.counts = 0;
+    l.used = align256(static_cast<size_t>(n_wg) * sizeof(int32_t));
+    l.steps = l.used + align256(static_cast<size_t>(kGroups) * nblk * sizeof(uint32_t));
+    l.kv = l.steps + align256(static_cast<size_t>(n_wg) * kTq * top_k * sizeof(u32x4));
+    l.total = l.kv + static_cast<size_t>(kGroups) * nblk * 2 * kVtElems * sizeof(uint16_t);
+    return l;
+}
 
 }  // namespace
 
-size_t prefill_attend_ws_bytes(int64_t n_q, int top_k) {
-    const int64_t n_wg = n_tiles_of(n_q) * kGroups;
-    const size_t counts = (static_cast<size_t>(n_wg) * sizeof(int32_t) + 255) & ~size_t(255);
-    return counts + static_cast<size_t>(n_wg) * kTq * top_k * sizeof(u32x4);
+size_t prefill_attend_ws_bytes(int64_t n_q, int top_k, int32_t max_pos) {
+    return ws_layout(n_q, top_k, max_pos / kBlock + 1).total;
 }
 
 hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pager& pg, const uint16_t* q,
                                  int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
                                  float scale, float* out, void* ws, hipStream_t s) {
     const int64_t n_wg = n_tiles_of(n_q) * kGroups;
-    const size_t counts_bytes = (static_cast<size_t>(n_wg) * sizeof(int32_t) + 255) & ~size_t(255);
-    int32_t* counts = static_cast<int32_t*>(ws);
-    u32x4* steps = reinterpret_cast<u32x4*>(static_cast<char*>(ws) + counts_bytes);
-    const int nblk = (pos0 + static_cast<int>(n_q) - 1) / kBlock + 1;
+    const int last_row = static_cast<int>(pos0 + n_q - 1);
+    const int nblk = last_row / kBlock + 1;
+    const WsLayout l = ws_layout(n_q, top_k, nblk);
+    char* base = static_cast<char*>(ws);
+    int32_t* counts = reinterpret_cast<int32_t*>(base + l.counts);
+    uint32_t* used = reinterpret_cast<uint32_t*>(base + l.used);
+    u32x4* steps = reinterpret_cast<u32x4*>(base + l.steps);
+    uint16_t* kv = reinterpret_cast<uint16_t*>(base + l.kv);
+
+    const int n_used = kGroups * nblk;
+    hipLaunchKernelGGL(prefill_clear_kernel, dim3(static_cast<unsigned>((n_used + 255) / 256)), dim3(256), 0, s,
+                       used, n_used);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
 
     StepArgs sa;
     sa.sel = sel;
@@ -597,20 +686,34 @@ hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pag
     sa.stream = stream;
     sa.counts = counts;
     sa.steps = steps;
+    sa.used = used;
     hipLaunchKernelGGL(prefill_steps_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(kStepsThreads),
                        static_cast<size_t>(nblk) * sizeof(uint32_t), s, sa);
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    KvArgs ka;
+    ka.k = k;
+    ka.v = v;
+    ka.pg = pg;
+    ka.stream = stream;
+    ka.nblk = nblk;
+    ka.last_row = last_row;
+    ka.used = used;
+    ka.kv = kv;
+    hipLaunchKernelGGL(prefill_kv_kernel, dim3(static_cast<unsigned>(n_used)), dim3(kVtThreads), 0, s, ka);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     PaArgs a;
     a.k = k;
-    a.v = v;
+    a.kv = kv;
     a.pg = pg;
     a.q = q;
     a.stream = stream;
     a.pos0 = pos0;
     a.n_q = n_q;
-    a.last_row = pos0 + n_q - 1;
+    a.nblk = nblk;
     a.max_steps = kTq * top_k;
     a.counts = counts;
     a.steps = steps;

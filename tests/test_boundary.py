@@ -256,26 +256,33 @@ def test_workspace_sizes(L):
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
     # prefill attention, the larger of: bf16 caches, per (32-query tile,
-    # group) a step count (256-byte aligned array) and up to 32 * top_k
-    # 16-byte step entries; quantized caches, the decode split partials
-    # (16 heads x 130 floats per query, group and split) of a launch of at
-    # most 256 queries, or of the ragged last launch.
+    # group) a step count (256-byte aligned array), a used flag per (group,
+    # block) (256-byte aligned), up to 32 * top_k 16-byte step entries
+    # (256-byte aligned) and K and V of every block rearranged (64 KiB per
+    # group and block); quantized caches, the decode split partials (16 heads x 130
+    # floats per query, group and split) of a launch of at most 256 queries,
+    # or of the ragged last launch.
     def splits(n, units=16):        # about 256 workgroups, at most 8 units per split
         return max(min(-(-256 // (4 * n)), units), -(-units // 8))
 
     def partials(n):
         return n * 4 * splits(n) * 16 * 130 * 4
 
-    def prefill(n):
-        steps = -(-(-(-n // 32) * 4 * 4) // 256) * 256 + -(-n // 32) * 4 * 32 * 16 * 16
-        tail = partials(n % 256) if n > 256 and n % 256 else 0
-        return max(steps, -(-max(partials(min(n, 256)), tail) // 256) * 256)
+    def up(x):
+        return -(-x // 256) * 256
 
-    assert prefill(4096) == 256 * 4 * 2 * 8320          # split partials of 256 queries
-    assert prefill(1) == 16 * 4 * 8320                  # one query: 16 splits of one block
-    assert 2048 + 512 * 32 * 16 * 16 < prefill(4096)
+    def prefill(n, max_pos=32767):
+        nblk = max_pos // 128 + 1
+        n_wg = -(-n // 32) * 4
+        steps = up(n_wg * 4) + up(4 * nblk * 4) + up(n_wg * 32 * 16 * 16) + 4 * nblk * 2 * 128 * 128 * 2
+        tail = partials(n % 256) if n > 256 and n % 256 else 0
+        return max(up(steps), up(max(partials(min(n, 256)), tail)))
+
+    assert prefill(4096) == 2048 + 4096 + 512 * 32 * 16 * 16 + 4 * 256 * 65536   # K and V of 256 blocks
+    assert prefill(1, 127) == 16 * 4 * 8320            # one query over one block: 16 one-block splits
     for n in (1, 33, 100, 256, 257, 300, 4096, 4100):
         assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, 32767) == prefill(n), n
+        assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, n - 1) == prefill(n, n - 1), n
     dd = M.dsa_dims()
     assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
     with pytest.raises(M.MsaError):
