@@ -472,12 +472,52 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
     }
 }
 
-// Fixed-order merge of the split partials of one (query, group).  A thread
-// owns 8 dims of one head; the partials of up to kCombineBatch splits are
-// loaded together (one round trip to memory per batch, not per split).
+// Fixed-order merge of the split partials of one (query, group), in one
+// pass: a thread owns 8 dims of one head and loads the (m, l, acc) of all
+// kNs splits at once (one round trip to memory), then combines them in
+// split order against their largest m.
+template <int kNs>
+__global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ ws, float* __restrict__ out) {
+    const int g = static_cast<int>(blockIdx.x % kGroups);
+    const int64_t i = blockIdx.x / kGroups;
+    const int hh = threadIdx.x >> 4;
+    const int d0 = 8 * (threadIdx.x & 15);
+    const float* part0 = ws + (i * kGroups + g) * kNs * static_cast<int64_t>(kPartFloats);
+    constexpr int kMl = kHeadsPerGroup * kHeadDim;   // (m, l) of head h at kMl + 2h
+    float ms[kNs], ls[kNs];
+    f32x4 a0[kNs], a1[kNs];
+#pragma unroll
+    for (int j = 0; j < kNs; ++j) {
+        const float* part = part0 + j * kPartFloats;
+        ms[j] = part[kMl + 2 * hh];
+        ls[j] = part[kMl + 2 * hh + 1];
+        a0[j] = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0);
+        a1[j] = *reinterpret_cast<const f32x4*>(part + hh * kHeadDim + d0 + 4);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kNs; ++j) M = fmaxf(M, ms[j]);
+    float L = 0.f;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kNs; ++j) {                  // in split order
+        const float wt = (ms[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[j] - M);
+        L += wt * ls[j];
+        o[0] += wt * a0[j].x; o[1] += wt * a0[j].y; o[2] += wt * a0[j].z; o[3] += wt * a0[j].w;
+        o[4] += wt * a1[j].x; o[5] += wt * a1[j].y; o[6] += wt * a1[j].z; o[7] += wt * a1[j].w;
+    }
+    const float inv = 1.f / L;
+    float* dst = out + (i * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + hh) * kHeadDim + d0;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+}
+
+// The same merge for any number of splits (more than 16: one query over many
+// blocks); the partials of up to kCombineBatch splits are loaded together
+// (one round trip to memory per batch, not per split).
 constexpr int kCombineBatch = 16;
 
-__global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ ws,
+__global__ __launch_bounds__(256) void attend_combine_any_kernel(const float* __restrict__ ws,
                                                              int n_split, float* __restrict__ out) {
     const int g = static_cast<int>(blockIdx.x % kGroups);
     const int64_t i = blockIdx.x / kGroups;
@@ -509,7 +549,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
         }
 #pragma unroll
         for (int j = 0; j < kCombineBatch; ++j) {      // in split order
-            const float wt = (ms[j] == -INFINITY) ? 0.f : exp2f(ms[j] - M);
+            const float wt = (ms[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[j] - M);
             L += wt * ls[j];
             o[0] += wt * a0[j].x; o[1] += wt * a0[j].y; o[2] += wt * a0[j].z; o[3] += wt * a0[j].w;
             o[4] += wt * a1[j].x; o[5] += wt * a1[j].y; o[6] += wt * a1[j].z; o[7] += wt * a1[j].w;
@@ -583,8 +623,16 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || ka.n_split == 1) return e;
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(static_cast<unsigned>(a.n_q * kGroups)), dim3(256), 0,
-                       s, static_cast<const float*>(a.ws), ka.n_split, a.out);
+    const dim3 cgrid(static_cast<unsigned>(a.n_q * kGroups));
+    const float* part = static_cast<const float*>(a.ws);
+    switch (ka.n_split) {
+#define MSA_COMBINE_CASE(N) case N: hipLaunchKernelGGL(attend_combine_kernel<N>, cgrid, dim3(256), 0, s, part, a.out); break;
+        MSA_COMBINE_CASE(2) MSA_COMBINE_CASE(3) MSA_COMBINE_CASE(4) MSA_COMBINE_CASE(5) MSA_COMBINE_CASE(6)
+        MSA_COMBINE_CASE(7) MSA_COMBINE_CASE(8) MSA_COMBINE_CASE(9) MSA_COMBINE_CASE(10) MSA_COMBINE_CASE(11)
+        MSA_COMBINE_CASE(12) MSA_COMBINE_CASE(13) MSA_COMBINE_CASE(14) MSA_COMBINE_CASE(15) MSA_COMBINE_CASE(16)
+#undef MSA_COMBINE_CASE
+        default: hipLaunchKernelGGL(attend_combine_any_kernel, cgrid, dim3(256), 0, s, part, ka.n_split, a.out);
+    }
     return hipGetLastError();
 }
 
