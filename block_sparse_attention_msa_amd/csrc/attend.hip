@@ -186,64 +186,84 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         }
     };
 
-    // Quantized caches: slot j of this thread (as in stage) holds dims
-    // 8 * seg .. + 7 of row `row`: 8 codes (int8: 8 bytes; 4-bit: the low or
-    // high nibbles of 8 bytes of the 32-value block) and that block's scale.
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    constexpr int kQSlots = kQ ? kCopiesPerUnit : 1;
+    // Quantized caches: a unit's codes are loaded in 16-byte chunks, eight
+    // (int8: 128-byte rows) or four (4-bit: 64-byte rows) lanes per row, so
+    // that one load instruction covers whole 128-byte lines, plus one 16-byte
+    // load of a row's four block scales for K and for V by the threads
+    // tid < kUnit.  Chunk c = kAttThreads * j + tid of K (and of V) is
+    // (row c / 8, values 16 * (c % 8) ..) for int8, (row c / 4, scale block
+    // c % 4) for 4-bit.
+    constexpr int kQPerRow = kQ == 2 ? 4 : 8;                 // chunks per row
+    constexpr int kQChunks = kQ ? kUnit * kQPerRow / kAttThreads : 1;
     // two register sets: unit u + 1 loads at the release of unit u - 1 and
     // is written to the ring after the math of unit u
-    u32x2_t kc[2][kQSlots], vc[2][kQSlots];
-    float kscl[2][kQSlots], vscl[2][kQSlots];
+    u32x4 kc[2][kQChunks], vc[2][kQChunks];
+    f32x4 kscl[2], vscl[2];
+    // cache row of key `row` of unit u (padding and keys past the query read
+    // the query's own row: finite, and masked)
+    auto qrow = [&](int u, int row) __attribute__((always_inline)) {
+        const int e = kTokenIds ? u * kUnit + row : u;
+        const int tok = kTokenIds ? sel_s[e] : sel_s[e] * kBlock + row;
+        const int r_e = row_s[e];
+        const int r_own = row_s[kMaxSplitEntries];
+        const bool bad = u >= n_units || tok < 0 || tok > p;
+        return static_cast<int64_t>(bad ? r_own : r_e + (kTokenIds ? 0 : row)) * kGroups + g;
+    };
     auto qload = [&](int u, int set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kQSlots; ++j) {
+        for (int j = 0; j < kQChunks; ++j) {
             const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
-            const int row = c >> 4;
-            const int seg = (c & 15) ^ rowperm(row);
-            const int e = kTokenIds ? u * kUnit + row : u;
-            const int tok = kTokenIds ? sel_s[e] : sel_s[e] * kBlock + row;
-            const int r_e = row_s[e];
-            const int r_own = row_s[kMaxSplitEntries];
-            const bool bad = u >= n_units || tok < 0 || tok > p;
-            const int64_t rq = static_cast<int64_t>(bad ? r_own : r_e + (kTokenIds ? 0 : row)) * kGroups + g;
-            const int64_t boff = kQ == 1 ? rq * kHeadDim + 8 * seg
-                                         : rq * (kHeadDim / 2) + 16 * (seg >> 2) + 8 * ((seg & 3) & 1);
-            kc[set][j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.k) + boff);
-            vc[set][j] = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(a.v) + boff);
-            kscl[set][j] = a.k_scale[rq * (kHeadDim / 32) + (seg >> 2)];
-            vscl[set][j] = a.v_scale[rq * (kHeadDim / 32) + (seg >> 2)];
+            const int64_t boff = qrow(u, c / kQPerRow) * (kQ == 1 ? kHeadDim : kHeadDim / 2) + 16 * (c % kQPerRow);
+            kc[set][j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.k) + boff);
+            vc[set][j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.v) + boff);
+        }
+        if (threadIdx.x < kUnit) {                 // waves 0, 1: one row's scales each
+            const int64_t rq = qrow(u, static_cast<int>(threadIdx.x));
+            kscl[set] = *reinterpret_cast<const f32x4*>(a.k_scale + rq * (kHeadDim / 32));
+            vscl[set] = *reinterpret_cast<const f32x4*>(a.v_scale + rq * (kHeadDim / 32));
         }
     };
-    auto dequant8 = [&](u32x2_t w, float sc, bool high) __attribute__((always_inline)) {
+    // 8 codes -> 8 bf16 values (exact): int8 bytes, or the low / high
+    // nibbles (stored + 8) of 8 bytes
+    auto codes8 = [&](uint32_t w0, uint32_t w1, int mode) __attribute__((always_inline)) {
         float f[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const uint32_t word = w[b >> 2];
+            const uint32_t word = b < 4 ? w0 : w1;
             const int byte = static_cast<int>((word >> (8 * (b & 3))) & 0xffu);
-            const int code = kQ == 1 ? static_cast<int>(static_cast<int8_t>(byte))
-                                     : (high ? (byte >> 4) : (byte & 15)) - 8;
-            f[b] = static_cast<float>(code) * sc;
+            const int code = mode == 0 ? static_cast<int>(static_cast<int8_t>(byte))
+                                       : (mode == 1 ? (byte & 15) : (byte >> 4)) - 8;
+            f[b] = static_cast<float>(code);
         }
-        u32x4 o;
-        o[0] = pack_bf16x2(f[0], f[1]);
-        o[1] = pack_bf16x2(f[2], f[3]);
-        o[2] = pack_bf16x2(f[4], f[5]);
-        o[3] = pack_bf16x2(f[6], f[7]);
-        return o;
+        return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])};
+    };
+    // 16 bytes of codes -> their 8-value segments of the staged row (the
+    // ring's permuted layout)
+    auto put_codes = [&](char* d, const u32x4& w, int c) __attribute__((always_inline)) {
+        const int row = c / kQPerRow, part = c % kQPerRow;
+        if constexpr (kQ == 1) {                   // values 16 part .. + 15: segments 2 part, 2 part + 1
+            *reinterpret_cast<u32x4*>(d + swz(row, 2 * part)) = codes8(w[0], w[1], 0);
+            *reinterpret_cast<u32x4*>(d + swz(row, 2 * part + 1)) = codes8(w[2], w[3], 0);
+        } else {                                   // block `part`: values 0..15 low nibbles, 16..31 high
+            *reinterpret_cast<u32x4*>(d + swz(row, 4 * part)) = codes8(w[0], w[1], 1);
+            *reinterpret_cast<u32x4*>(d + swz(row, 4 * part + 1)) = codes8(w[2], w[3], 1);
+            *reinterpret_cast<u32x4*>(d + swz(row, 4 * part + 2)) = codes8(w[0], w[1], 2);
+            *reinterpret_cast<u32x4*>(d + swz(row, 4 * part + 3)) = codes8(w[2], w[3], 2);
+        }
     };
     auto qcommit = [&](int set, char* kd, char* vd, float* ksd, float* vsd) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < kQSlots; ++j) {
+        for (int j = 0; j < kQChunks; ++j) {
             const int c = kAttThreads * j + static_cast<int>(threadIdx.x);
-            const int row = c >> 4;
-            const int seg = (c & 15) ^ rowperm(row);
-            const bool high = (seg & 3) >= 2;          // 4-bit: values 16 .. 31 of the block
-            *reinterpret_cast<u32x4*>(kd + 16 * c) = dequant8(kc[set][j], 1.f, high);   // codes, exact
-            *reinterpret_cast<u32x4*>(vd + 16 * c) = dequant8(vc[set][j], 1.f, high);   // codes, exact
-            if ((seg & 3) == 0) {
-                ksd[(seg >> 2) * kUnit + row] = kscl[set][j];
-                vsd[(seg >> 2) * kUnit + row] = vscl[set][j];
+            put_codes(kd, kc[set][j], c);           // codes, exact
+            put_codes(vd, vc[set][j], c);
+        }
+        if (threadIdx.x < kUnit) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                ksd[b * kUnit + threadIdx.x] = kscl[set][b];
+                vsd[b * kUnit + threadIdx.x] = vscl[set][b];
             }
         }
     };
