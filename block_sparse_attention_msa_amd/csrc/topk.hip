@@ -10,7 +10,9 @@
 // f32 block score, bits 30..0 = ~block id.  The maximum key is therefore the
 // local block first, then the highest score, then the LOWER id on equal
 // scores -- a total order, so the selection is unique and deterministic.
-// Up to 1024 candidates live in registers (a lane's 16 at most): each of the
+// Up to 1024 candidates live in registers (a lane's 16 at most; the kernel is
+// instantiated for 4, 8 and 16 per lane, so that short contexts do not pay
+// the register count of long ones): each of the
 // k rounds is a wave maximum after which every lane clears the winner if it
 // holds it.  Longer contexts (up to 4096 blocks) keep the keys in LDS; each
 // lane keeps the best key of its own slice, the wave takes the maximum over
@@ -80,22 +82,27 @@ __device__ __forceinline__ void write_ascending(const int32_t* chosen, int k, in
 // Candidates held in registers: lane l owns blocks l, l + 64, ..., kPer of
 // them (nvis <= 64 * kPer).  Each round takes the wave maximum and every lane
 // clears the key equal to it (only its owner has it), so no round waits on
-// memory.
-template <int kPer>
+// memory.  kOneSub: one score per block (no partial maxima to fold), which
+// keeps the widest instantiation's key loop free of an inner loop (that would
+// stop its unrolling and turn the keys into an indexed array).
+template <int kPer, bool kOneSub>
 __device__ __forceinline__ void topk_in_registers(const float* row, int n_sub, int nvis, int loc, int k, int lane,
                                                   int32_t* chosen) {
     uint64_t key[kPer];
+    // (loads of blocks past nvis read block 0 and are masked: every load is
+    // unconditional, so that they are all in flight together)
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int b = lane + 64 * j;
-        key[j] = 0;
-        if (b < nvis) {
-            float sc = row[b * n_sub];
-            for (int e = 1; e < n_sub; ++e) sc = fmaxf(sc, row[b * n_sub + e]);
-            key[j] = (static_cast<uint64_t>(ordered_key(sc)) << 31) | static_cast<uint64_t>(0x7fffffff - b) |
-                     (b == loc ? 1ull << 63 : 0ull);
-        }
+        const int bl = b < nvis ? b : 0;
+        float sc = row[kOneSub ? bl : bl * n_sub];
+        if constexpr (!kOneSub)
+            for (int e = 1; e < n_sub; ++e) sc = fmaxf(sc, row[bl * n_sub + e]);
+        const uint64_t kb = (static_cast<uint64_t>(ordered_key(sc)) << 31) | static_cast<uint64_t>(0x7fffffff - b) |
+                            (b == loc ? 1ull << 63 : 0ull);
+        key[j] = b < nvis ? kb : 0ull;
     }
+#pragma unroll 1
     for (int r = 0; r < k; ++r) {
         uint64_t best = key[0];
 #pragma unroll
@@ -107,6 +114,11 @@ __device__ __forceinline__ void topk_in_registers(const float* row, int n_sub, i
     }
 }
 
+// kPer: the widest register path this instantiation holds (candidates
+// 64 * kPer); it sets the kernel's register count, and with it how many
+// problems share a SIMD, so a launch takes the narrowest that covers its
+// contexts (0: none, longer contexts go through LDS).
+template <int kPer>
 __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict__ bs,
                                                          int64_t nblk_stride,
                                                          const int32_t* __restrict__ q_pos,
@@ -122,11 +134,12 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
     const int nvis = loc + 1;
     const float* row = bs + qg * nblk_stride;
 
-    if (nvis > 64 && nvis <= 64 * 16) {
+    // (the widest register path only for one score per block; partial
+    // maxima of a fine scan come with short contexts only)
+    if (kPer > 0 && nvis > 64 && nvis <= 64 * kPer && (kPer <= 8 || n_sub == 1)) {
         const int k = min(top_k, nvis);
-        if (nvis <= 64 * 4) topk_in_registers<4>(row, n_sub, nvis, loc, k, lane, chosen);
-        else if (nvis <= 64 * 8) topk_in_registers<8>(row, n_sub, nvis, loc, k, lane, chosen);
-        else topk_in_registers<16>(row, n_sub, nvis, loc, k, lane, chosen);
+        if constexpr (kPer > 8) topk_in_registers<kPer, true>(row, n_sub, nvis, loc, k, lane, chosen);
+        else if constexpr (kPer > 0) topk_in_registers<kPer, false>(row, n_sub, nvis, loc, k, lane, chosen);
         __syncthreads();
         write_ascending(chosen, k, top_k, lane, sel + qg * top_k);
         if (lane == 0) n_sel[qg] = k;
@@ -175,22 +188,34 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
     if (lane == 0) n_sel[qg] = k;
 }
 
+void launch_topk_kernel(int nblk, dim3 grid, size_t lds, hipStream_t s, const float* bs, int64_t nblk_stride,
+                        const int32_t* pos, int32_t pos0, int top_k, int32_t* sel, int32_t* n_sel, int n_sub) {
+    if (nblk <= 64 * 4)
+        hipLaunchKernelGGL(topk_blocks_kernel<4>, grid, dim3(64), lds, s, bs, nblk_stride, pos, pos0, top_k, sel, n_sel, n_sub);
+    else if (nblk <= 64 * 8)
+        hipLaunchKernelGGL(topk_blocks_kernel<8>, grid, dim3(64), lds, s, bs, nblk_stride, pos, pos0, top_k, sel, n_sel, n_sub);
+    else if (nblk <= 64 * 16)
+        hipLaunchKernelGGL(topk_blocks_kernel<16>, grid, dim3(64), lds, s, bs, nblk_stride, pos, pos0, top_k, sel, n_sel, n_sub);
+    else
+        hipLaunchKernelGGL(topk_blocks_kernel<0>, grid, dim3(64), lds, s, bs, nblk_stride, pos, pos0, top_k, sel, n_sel, n_sub);
+}
+
 }  // namespace
 
 hipError_t launch_topk_blocks(const float* bs, int64_t nblk_stride, const int32_t* pos,
                               int64_t n_q, int nblk, int top_k, int32_t* sel, int32_t* n_sel,
                               hipStream_t s, int n_sub) {
     const size_t lds = static_cast<size_t>(nblk) * sizeof(uint64_t);
-    hipLaunchKernelGGL(topk_blocks_kernel, dim3(static_cast<unsigned>(n_q * kGroups)), dim3(64), lds, s,
-                       bs, nblk_stride, pos, 0, top_k, sel, n_sel, n_sub);
+    launch_topk_kernel(nblk, dim3(static_cast<unsigned>(n_q * kGroups)), lds, s, bs, nblk_stride, pos, 0, top_k, sel,
+                       n_sel, n_sub);
     return hipGetLastError();
 }
 
 hipError_t launch_topk_blocks_range(const float* bs, int64_t nblk_stride, int32_t pos0, int64_t n_q,
                                     int nblk, int top_k, int32_t* sel, int32_t* n_sel, hipStream_t s) {
     const size_t lds = static_cast<size_t>(nblk) * sizeof(uint64_t);
-    hipLaunchKernelGGL(topk_blocks_kernel, dim3(static_cast<unsigned>(n_q * kGroups)), dim3(64), lds, s,
-                       bs, nblk_stride, nullptr, pos0, top_k, sel, n_sel, 1);
+    launch_topk_kernel(nblk, dim3(static_cast<unsigned>(n_q * kGroups)), lds, s, bs, nblk_stride, nullptr, pos0, top_k,
+                       sel, n_sel, 1);
     return hipGetLastError();
 }
 
