@@ -454,14 +454,16 @@ __global__ __launch_bounds__(kSelThreads) void dsa_topk_kernel(const float* __re
 // 16-byte loads (the scores come from other compute units' writes, so each
 // pass over memory would cost a full memory latency).  The three digits are
 // histogrammed from the registers: the first over eight copies (by lane),
-// because the exponent-heavy keys pile into few bins, the next two only for
-// the keys that match the prefix found so far.  The compaction counts each
-// wave's keys above T and equal to T (one scan over the waves gives each
-// wave its output offset), then walks the rounds in id order: a scan of the
-// lanes' counts places every kept key, into an LDS copy of the output that is
-// written out coalesced at the end.  No step branches per
-// key: a key that is not counted or kept goes to a spare bin or slot of its
-// lane instead.
+// because the exponent-heavy keys pile into few bins, the next two over a
+// list of the keys in the first digit's boundary bin (a block scan of the
+// threads' match counts places them; typically a few hundred keys).  The
+// compaction counts each wave's keys above T and equal to T (one scan over
+// the waves gives each wave its output offset), then walks the rounds in id
+// order: ballots of the lanes' keys above and equal to T rank every kept key
+// (the kept keys of lower lanes, then the lane's own earlier ones), into an
+// LDS copy of the output that is written out coalesced at the end.  No step
+// branches per key: a key that is not counted or kept goes to a spare bin or
+// slot of its lane instead.
 // ---------------------------------------------------------------------------
 constexpr int kRegThreads = 1024;
 constexpr int kRegWaves = kRegThreads / 64;
@@ -470,6 +472,7 @@ constexpr int kRegPer = 4 * kRegRounds;                   // keys per lane
 constexpr int kRegKeys = kRegThreads * kRegPer;           // 65536
 constexpr int kHistCopies = 8;
 constexpr int kTopKMax = 4096;
+constexpr int kCandRegCap = (kHistCopies - 1) * (kBins + 64);   // boundary-bin keys the freed copies hold
 
 __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float* __restrict__ scores,
                                                                     int64_t stride,
@@ -483,6 +486,7 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float*
     __shared__ uint32_t s_digit;
     __shared__ int s_remaining;
     __shared__ uint32_t s_T;
+    __shared__ int s_ncand;
     const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -536,7 +540,25 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float*
     pick_digit_t<kRegThreads>(hist[0], 12, top_k, wave_sums, &s_digit, &s_remaining);
     uint32_t prefix = s_digit << 20, mask = 0xfff00000u;
     int remaining = s_remaining;
-    // ---- digits 2 and 3 (12 and 8 bits) over the keys with the prefix
+    // ---- digits 2 and 3 (12 and 8 bits) over the keys with the prefix: the
+    // boundary bin (typically a few hundred keys) is first copied into a
+    // list in the free histogram copies, so each digit histograms the list
+    // only; a bin too large for the list takes every key per digit
+    uint32_t* cand = reinterpret_cast<uint32_t*>(&hist[1][0]);
+    int n_match = 0;
+#pragma unroll
+    for (int e = 0; e < kRegPer; ++e) n_match += (rk[e] & mask) == prefix;
+    const int m_incl = block_scan<kRegThreads>(n_match, wave_sums);
+    if (tid == kRegThreads - 1) s_ncand = m_incl;
+    __syncthreads();
+    const int n_cand = s_ncand;
+    if (n_cand <= kCandRegCap) {
+        int slot = m_incl - n_match;
+#pragma unroll
+        for (int e = 0; e < kRegPer; ++e) {
+            if ((rk[e] & mask) == prefix) cand[slot++] = rk[e];
+        }
+    }
 #pragma unroll
     for (int pass = 1; pass < 3; ++pass) {
         const int bits = kDigitBits[pass];
@@ -544,10 +566,17 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float*
         const uint32_t dmask = (1u << bits) - 1;
         for (int b = tid; b < kBins; b += kRegThreads) hist[0][b] = 0;
         __syncthreads();
+        if (n_cand <= kCandRegCap) {               // workgroup-uniform
+            for (int c = tid; c < n_cand; c += kRegThreads) {
+                const uint32_t key = cand[c];
+                if ((key & mask) == prefix) atomicAdd(&hist[0][(key >> shift) & dmask], 1);
+            }
+        } else {
 #pragma unroll
-        for (int e = 0; e < kRegPer; ++e) {
-            const uint32_t key = rk[e];
-            atomicAdd(&hist[0][(key & mask) == prefix ? static_cast<int>((key >> shift) & dmask) : kBins + lane], 1);
+            for (int e = 0; e < kRegPer; ++e) {
+                const uint32_t key = rk[e];
+                atomicAdd(&hist[0][(key & mask) == prefix ? static_cast<int>((key >> shift) & dmask) : kBins + lane], 1);
+            }
         }
         __syncthreads();
         pick_digit_t<kRegThreads>(hist[0], bits, remaining, wave_sums, &s_digit, &s_remaining);
@@ -573,29 +602,33 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float*
         if (w < wave) before += wave_tot[w];
     int G = static_cast<int>(before & 0xffffu), Q = static_cast<int>(before >> 16);   // keys before this round
     // T read back from LDS, so that the compares are redone here rather than
-    // kept from the count above (the lane masks would not fit in SGPRs); the
+    // kept from the count above (64 keys' masks would not fit in SGPRs); the
     // ids likewise are computed afresh from an opaque copy of `base` (kept
     // from the loads, their 16 registers would push keys out to scratch)
     const uint32_t T2 = s_T;
     int base2 = base;
     asm volatile("" : "+v"(base2));
+    // keys of this lane's lower-numbered lanes
+    const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
     for (int r = 0; r < kRegRounds; ++r) {
-        // this lane's counts in the round, packed; their exclusive prefix
-        // over the lanes places its keys after the round's earlier ones
-        uint32_t lc = 0;
+        // ranks inside the round from ballots of the lanes' keys above and
+        // equal to T: a kept key's place is the round's kept keys in lower
+        // lanes, then this lane's earlier keys
+        uint64_t mg[4], mq[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) lc += (rk[4 * r + c] > T2 ? 1u : 0u) + (rk[4 * r + c] == T2 ? 0x10000u : 0u);
-        uint32_t sc = lc;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(sc, o, 64);
-            if (lane >= o) sc += y;
+        for (int c = 0; c < 4; ++c) {
+            mg[c] = __builtin_amdgcn_ballot_w64(rk[4 * r + c] > T2);
+            mq[c] = __builtin_amdgcn_ballot_w64(rk[4 * r + c] == T2);
         }
-        const uint32_t round_tot = __shfl(sc, 63, 64);
-        int gb = G + static_cast<int>((sc - lc) & 0xffffu), qb = Q + static_cast<int>((sc - lc) >> 16);
-        G += static_cast<int>(round_tot & 0xffffu);
-        Q += static_cast<int>(round_tot >> 16);
+        int gb = G, qb = Q;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            gb += __builtin_popcountll(mg[c] & below);
+            qb += __builtin_popcountll(mq[c] & below);
+            G += __builtin_popcountll(mg[c]);
+            Q += __builtin_popcountll(mq[c]);
+        }
         const int j = base2 + 256 * r;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {

@@ -198,16 +198,22 @@ struct KvArgs {
     uint16_t* kv;
 };
 
+// Workgroup (g, b, m) handles keys 32m .. 32m + 31 of block b: the K slots of
+// waves w = 2m, 2m + 1 and the V slots of chunk c = m, 8 KiB each way.
 __global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
-    const int g = blockIdx.x % kGroups;
-    const int b = blockIdx.x / kGroups;
+    const int m = blockIdx.x & 3;
+    const int g = (blockIdx.x >> 2) % kGroups;
+    const int b = (blockIdx.x >> 2) / kGroups;
     if (a.used[g * a.nblk + b] == 0u) return;           // workgroup-uniform
     constexpr int kPitch = kHeadDim + 8;                 // 272-byte rows: the gathers below hit distinct banks
-    __shared__ __attribute__((aligned(16))) uint16_t tk[kBlock][kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t tv[kBlock][kPitch];
-    const int64_t row0 = a.pg.block_row(a.stream, b);
-    const int key0 = b * kBlock;
-    for (int s = threadIdx.x; s < kBlock * 16; s += kVtThreads) {
+    __shared__ __attribute__((aligned(16))) uint16_t tv[32][kPitch];
+    const int64_t row0 = a.pg.block_row(a.stream, b) + 32 * m;
+    const int key0 = b * kBlock + 32 * m;
+    uint16_t* dst = a.kv + (static_cast<int64_t>(g) * a.nblk + b) * 2 * kVtElems;
+    // 32 rows x 16 segments of K and of V: thread t takes segments t and t + 256
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int s = threadIdx.x + kVtThreads * h;
         const int r = s >> 4, seg = s & 15;
         u32x4 xk = u32x4{0u, 0u, 0u, 0u}, xv = xk;
         if (key0 + r <= a.last_row) {
@@ -215,17 +221,20 @@ __global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
             xk = *reinterpret_cast<const u32x4*>(a.k + off);
             xv = *reinterpret_cast<const u32x4*>(a.v + off);
         }
-        *reinterpret_cast<u32x4*>(&tk[r][8 * seg]) = xk;
+        // K: key 32m + r = 16w + l16 with w = 2m + r / 16, dims 8 seg = 32c + 8 l4
+        const int w = 2 * m + (r >> 4), l16 = r & 15, c = seg >> 2, l4 = seg & 3;
+        *reinterpret_cast<u32x4*>(dst + 8 * ((4 * w + c) * 64 + 16 * l4 + l16)) = xk;
         *reinterpret_cast<u32x4*>(&tv[r][8 * seg]) = xv;
     }
     __syncthreads();
-    uint16_t* dst = a.kv + (static_cast<int64_t>(g) * a.nblk + b) * 2 * kVtElems;
-    for (int o = threadIdx.x; o < kVtElems / 8; o += kVtThreads) {
-        const int lane = o & 63, c = (o >> 6) & 3, w = o >> 8;
+    // V^T slots of chunk m: (4w + m) * 64 + lane for the eight waves w
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int o = threadIdx.x + kVtThreads * h;     // 0 .. 511
+        const int lane = o & 63, w = o >> 6;
         const int l16 = lane & 15, l4 = lane >> 4;
-        *reinterpret_cast<u32x4*>(dst + 8 * o) = *reinterpret_cast<const u32x4*>(&tk[16 * w + l16][32 * c + 8 * l4]);
         const int dim = 16 * w + l16;
-        const int k0 = 32 * c + 4 * l4;
+        const int k0 = 4 * l4;
         uint32_t x[4];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
             x[2 + j] = static_cast<uint32_t>(tv[k0 + 16 + 2 * j][dim]) |
                        (static_cast<uint32_t>(tv[k0 + 16 + 2 * j + 1][dim]) << 16);
         }
-        *reinterpret_cast<u32x4*>(dst + kVtElems + 8 * o) = u32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<u32x4*>(dst + kVtElems + 8 * ((4 * w + m) * 64 + lane)) = u32x4{x[0], x[1], x[2], x[3]};
     }
 }
 
@@ -701,7 +710,7 @@ hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pag
     ka.last_row = last_row;
     ka.used = used;
     ka.kv = kv;
-    hipLaunchKernelGGL(prefill_kv_kernel, dim3(static_cast<unsigned>(n_used)), dim3(kVtThreads), 0, s, ka);
+    hipLaunchKernelGGL(prefill_kv_kernel, dim3(static_cast<unsigned>(4 * n_used)), dim3(kVtThreads), 0, s, ka);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
