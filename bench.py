@@ -463,28 +463,30 @@ def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10, profile=False):
     log(f"[bench] prefill attention, selections shared by each 16 consecutive queries: {t_sh * 1e3:.1f} us "
         f"({att_flop / (t_sh * 1e-3) / 1e12:.0f} TFLOP/s)")
 
-    # The same chunk's attention (the indexer's selection above) over an int8
-    # K/V cache holding the same rows: the decode kernel in launches of 256
-    # consecutive queries.
-    qk = torch.zeros((1, cap, 4, 128), dtype=torch.uint8, device=dev)
-    qv = torch.zeros_like(qk)
-    qks = torch.zeros((1, cap, 4, 4), dtype=torch.float32, device=dev)
-    qvs = torch.zeros_like(qks)
-    qcache = M.make_cache(k=qk, v=qv, idx_k=torch.zeros_like(idx_k), kv_format=M.KV_INT8, k_scale=qks, v_scale=qvs)
+    # The same chunk's attention (the indexer's selection above) over int8 and
+    # 4-bit K/V caches holding the same rows: the same tile sweep, the used
+    # blocks dequantized into its bf16 operand copy.
+    t_quant = {}
     all_ps = torch.arange(cap, dtype=torch.int32, device=dev)
-    M.msa_index_append(dims, qcache, torch.zeros(cap, dtype=torch.int32, device=dev), all_ps, cap - 1,
-                       idx_k.view(cap, 4, 128), k.view(cap, 4, 128), v.view(cap, 4, 128))
-    M.msa_attend_prefill(dims, qcache, q, 0, pos0, sel, out, ws_att)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(iters):
+    for fmt, fname, width in ((M.KV_INT8, "int8", 128), (M.KV_Q4, "q4", 64)):
+        qk = torch.zeros((1, cap, 4, width), dtype=torch.uint8, device=dev)
+        qv = torch.zeros_like(qk)
+        qks = torch.zeros((1, cap, 4, 4), dtype=torch.float32, device=dev)
+        qvs = torch.zeros_like(qks)
+        qcache = M.make_cache(k=qk, v=qv, idx_k=torch.zeros_like(idx_k), kv_format=fmt, k_scale=qks, v_scale=qvs)
+        M.msa_index_append(dims, qcache, torch.zeros(cap, dtype=torch.int32, device=dev), all_ps, cap - 1,
+                           idx_k.view(cap, 4, 128), k.view(cap, 4, 128), v.view(cap, 4, 128))
         M.msa_attend_prefill(dims, qcache, q, 0, pos0, sel, out, ws_att)
-    e1.record()
-    torch.cuda.synchronize()
-    t_q8 = e0.elapsed_time(e1) / iters
-    log(f"[bench] prefill attention over an int8 K/V cache: {t_q8 * 1e3:.1f} us "
-        f"({att_flop / (t_q8 * 1e-3) / 1e12:.0f} TFLOP/s)")
-    del qk, qv, qks, qvs, qcache
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            M.msa_attend_prefill(dims, qcache, q, 0, pos0, sel, out, ws_att)
+        e1.record()
+        torch.cuda.synchronize()
+        t_quant[fname] = e0.elapsed_time(e1) / iters
+        log(f"[bench] prefill attention over a {fname} K/V cache: {t_quant[fname] * 1e3:.1f} us "
+            f"({att_flop / (t_quant[fname] * 1e-3) / 1e12:.0f} TFLOP/s)")
+        del qk, qv, qks, qvs, qcache
     return {
         "prefill_tok_s": round(n_q / (total * 1e-3), 1),
         "prefill_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
@@ -497,7 +499,8 @@ def bench_prefill(M, W, torch, dev, bits, tens, wsbuf, iters=10, profile=False):
         "prefill_attend_frac_bf16_mfma": round(att_flop / (seg[2] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "prefill_attend_shared16_us": round(t_sh * 1e3, 2),
         "prefill_attend_shared16_frac_bf16_mfma": round(att_flop / (t_sh * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-        "prefill_attend_int8_kv_us": round(t_q8 * 1e3, 2),
+        "prefill_attend_int8_kv_us": round(t_quant["int8"] * 1e3, 2),
+        "prefill_attend_q4_kv_us": round(t_quant["q4"] * 1e3, 2),
     }
 
 

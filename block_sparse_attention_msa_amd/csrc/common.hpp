@@ -223,12 +223,15 @@ hipError_t launch_index_project(const float* x, int d_model, const float* w_q, c
                                 float* idx_k, uint16_t* idx_k16, const Pager& pg, void* ws, hipStream_t s);
 // Prefill attention for the consecutive positions pos0 .. pos0 + n_q - 1 of
 // one stream (MSA blocks); ws (prefill_attend_ws_bytes(n_q, top_k,
-// pos0 + n_q - 1) bytes) holds the per-tile step lists and V of the used
-// blocks transposed.
+// pos0 + n_q - 1) bytes) holds the per-tile step lists and K and V of the
+// used blocks rearranged into matrix-core operand order (bf16; a quantized
+// cache, kv_format 1 int8 or 2 4-bit with its f32 scales, is dequantized
+// into it).
 size_t prefill_attend_ws_bytes(int64_t n_q, int top_k, int32_t max_pos);
-hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pager& pg, const uint16_t* q,
-                                 int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
-                                 float scale, float* out, void* ws, hipStream_t s);
+hipError_t launch_prefill_attend(const void* k, const void* v, int kv_format, const float* k_scale,
+                                 const float* v_scale, const Pager& pg, const uint16_t* q, int32_t stream,
+                                 int32_t pos0, int64_t n_q, const int32_t* sel, int top_k, float scale, float* out,
+                                 void* ws, hipStream_t s);
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos);
 hipError_t launch_dsa_select(const uint16_t* dsa_k, const Pager& pg, const uint16_t* q_idx,

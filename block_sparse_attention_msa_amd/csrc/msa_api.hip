@@ -31,19 +31,6 @@ msa_status check_dims(const msa_dims* d, Mode mode) {
     return MSA_OK;
 }
 
-// Queries per launch when a prefill chunk attends over a quantized cache.
-constexpr int64_t kPrefillQuantBatch = 256;
-
-// Split partials of the quantized-cache prefill: the larger of a full batch's
-// and the ragged last batch's (a short batch may split its units further).
-size_t prefill_quant_ws(int64_t n_q, int top_k) {
-    const int64_t full = n_q < kPrefillQuantBatch ? n_q : kPrefillQuantBatch;
-    const size_t a = msa::attend_ws_bytes(full, top_k, kBlock);
-    const int64_t tail = n_q % kPrefillQuantBatch;
-    const size_t b = n_q > kPrefillQuantBatch && tail ? msa::attend_ws_bytes(tail, top_k, kBlock) : 0;
-    return a > b ? a : b;
-}
-
 msa_status check_cache(const msa_cache* c) {
     if (!c) return MSA_ERR_NULL_ARG;
     if (c->cap < 1 || c->n_stream < 1) return MSA_ERR_BAD_SHAPE;
@@ -245,12 +232,8 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
             return align256(msa::prefill_scores_ws_bytes(max_pos));
         case MSA_OP_ATTEND_DECODE:
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, dims->block));
-        case MSA_OP_ATTEND_PREFILL: {
-            // the larger of the bf16 path's and the quantized-cache path's needs
-            const size_t a = align256(msa::prefill_attend_ws_bytes(n_q, dims->top_k, max_pos));
-            const size_t b = align256(prefill_quant_ws(n_q, dims->top_k));
-            return a > b ? a : b;
-        }
+        case MSA_OP_ATTEND_PREFILL:
+            return align256(msa::prefill_attend_ws_bytes(n_q, dims->top_k, max_pos));
         case DSA_OP_SELECT:
             return align256(msa::dsa_select_ws_bytes(n_q, max_pos));
         case DSA_OP_ATTEND_DECODE:
@@ -425,25 +408,11 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     if (nblk_of(static_cast<int32_t>(pos0 + n_q - 1)) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({cache->k, cache->v, d_q, d_sel, d_out, d_ws}));
-    // one documented amount for both paths (the query cannot see the cache format)
     if (ws_bytes < msa_workspace_bytes(dims, MSA_OP_ATTEND_PREFILL, n_q, static_cast<int32_t>(pos0 + n_q - 1)))
         return MSA_ERR_WORKSPACE_TOO_SMALL;
-    if (cache->kv_format != 0) {
-        // quantized caches: the chunk's queries run through the decode
-        // attention kernel (its quantized path), in batches that bound the
-        // split partials in the workspace
-        for (int64_t b0 = 0; b0 < n_q; b0 += kPrefillQuantBatch) {
-            const int64_t m = n_q - b0 < kPrefillQuantBatch ? n_q - b0 : kPrefillQuantBatch;
-            constexpr int64_t kQRow = int64_t(kGroups) * msa::kHeadsPerGroup * msa::kHeadDim;
-            msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q + b0 * kQRow, nullptr, nullptr, m,
-                              d_sel + b0 * kGroups * dims->top_k, dims->top_k, dims->top_k, kBlock, dims->scale,
-                              d_out + b0 * kQRow, d_ws, cache->kv_format, cache->k_scale, cache->v_scale,
-                              stream, static_cast<int32_t>(pos0 + b0)};
-            MSA_TRY(hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream))));
-        }
-        return MSA_OK;
-    }
-    return hip_status(msa::launch_prefill_attend(cache->k, cache->v, view(cache).pg, d_q, stream, pos0, n_q, d_sel,
+    // (a quantized cache is dequantized into the sweep's bf16 operand copy)
+    return hip_status(msa::launch_prefill_attend(cache->k, cache->v, cache->kv_format, cache->k_scale,
+                                                 cache->v_scale, view(cache).pg, d_q, stream, pos0, n_q, d_sel,
                                                  dims->top_k, dims->scale, d_out, d_ws,
                                                  static_cast<hipStream_t>(hip_stream)));
 }

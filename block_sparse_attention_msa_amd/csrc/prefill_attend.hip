@@ -185,11 +185,15 @@ __global__ __launch_bounds__(kStepsThreads) void prefill_steps_kernel(StepArgs a
 //           chunk c of the probabilities, in the key order the score
 //           products write them.
 // Keys past the chunk's last key are zero (they are masked, and their
-// probabilities are zero).
+// probabilities are zero).  A quantized cache is dequantized here: each code
+// times its 32-value block's f32 scale, formed in f32 and rounded once to
+// bf16, so the sweep is the same for every cache format.
 // ---------------------------------------------------------------------------
 struct KvArgs {
-    const uint16_t* k;
-    const uint16_t* v;
+    const void* k;          // bf16 rows, or codes (kv_format 1: int8, 2: 4-bit)
+    const void* v;
+    const float* k_scale;   // quantized caches: one f32 per 32 values of a group's row
+    const float* v_scale;
     Pager pg;
     int32_t stream;
     int nblk;
@@ -198,8 +202,44 @@ struct KvArgs {
     uint16_t* kv;
 };
 
+// The eight codes of dims 8 seg .. 8 seg + 7 of cache row `rg` (row x group)
+// as exact floats: int8 bytes (kQ 1), or (kQ 2) the low nibbles (values
+// 0 .. 15 of a 32-value block) or high nibbles (values 16 .. 31), stored + 8,
+// of eight bytes.
+template <int kQ>
+__device__ __forceinline__ void row_codes8(const void* base, int64_t rg, int seg, float* f) {
+    const uint8_t* b = static_cast<const uint8_t*>(base);
+    if constexpr (kQ == 1) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(b + rg * kHeadDim + 8 * seg);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = static_cast<float>(static_cast<int8_t>((w[j >> 2] >> (8 * (j & 3))) & 255u));
+    } else {
+        const int j0 = 8 * (seg & 3);                   // first value inside the 32-value block
+        const u32x2 w = *reinterpret_cast<const u32x2*>(b + rg * (kHeadDim / 2) + 16 * (seg >> 2) + (j0 & 15));
+        const int sh = (j0 & 16) ? 4 : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            f[j] = static_cast<float>(static_cast<int>((w[j >> 2] >> (8 * (j & 3) + sh)) & 15u) - 8);
+    }
+}
+
+// Dims 8 seg .. 8 seg + 7 of cache row `rg` as eight bf16 values.
+template <int kQ>
+__device__ __forceinline__ u32x4 row_segment(const void* base, const float* scale, int64_t rg, int seg) {
+    if constexpr (kQ == 0) {
+        return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + rg * kHeadDim + 8 * seg);
+    } else {
+        float f[8];
+        row_codes8<kQ>(base, rg, seg, f);
+        const float sc = scale[rg * (kHeadDim / 32) + (seg >> 2)];
+        return u32x4{pack2_bf16(f[0] * sc, f[1] * sc), pack2_bf16(f[2] * sc, f[3] * sc),
+                     pack2_bf16(f[4] * sc, f[5] * sc), pack2_bf16(f[6] * sc, f[7] * sc)};
+    }
+}
+
 // Workgroup (g, b, m) handles keys 32m .. 32m + 31 of block b: the K slots of
 // waves w = 2m, 2m + 1 and the V slots of chunk c = m, 8 KiB each way.
+template <int kQ>
 __global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
     const int m = blockIdx.x & 3;
     const int g = (blockIdx.x >> 2) % kGroups;
@@ -217,9 +257,9 @@ __global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
         const int r = s >> 4, seg = s & 15;
         u32x4 xk = u32x4{0u, 0u, 0u, 0u}, xv = xk;
         if (key0 + r <= a.last_row) {
-            const int64_t off = ((row0 + r) * kGroups + g) * kHeadDim + 8 * seg;
-            xk = *reinterpret_cast<const u32x4*>(a.k + off);
-            xv = *reinterpret_cast<const u32x4*>(a.v + off);
+            const int64_t rg = (row0 + r) * kGroups + g;
+            xk = row_segment<kQ>(a.k, a.k_scale, rg, seg);
+            xv = row_segment<kQ>(a.v, a.v_scale, rg, seg);
         }
         // K: key 32m + r = 16w + l16 with w = 2m + r / 16, dims 8 seg = 32c + 8 l4
         const int w = 2 * m + (r >> 4), l16 = r & 15, c = seg >> 2, l4 = seg & 3;
@@ -250,7 +290,9 @@ __global__ __launch_bounds__(kVtThreads) void prefill_kv_kernel(KvArgs a) {
 // Attention sweep.
 // ---------------------------------------------------------------------------
 struct PaArgs {
-    const uint16_t* k;
+    const void* k;          // the cache's K rows (bf16, or codes), for the softmax references
+    const float* k_scale;   // quantized caches: one f32 per 32 values
+    int kv_format;          // 0 bf16, 1 int8, 2 4-bit
     const uint16_t* kv;
     Pager pg;
     const uint16_t* q;
@@ -318,16 +360,35 @@ __global__ __launch_bounds__(kPaThreads, 1) void prefill_attend_kernel(PaArgs a)
         float r = 0.f;
         if (t < n_tq) {
             const uint16_t* qr = a.q + q_base + t * kQStride + h * kHeadDim;
-            const uint16_t* kr = a.k + (a.pg.row(a.stream, a.pos0 + static_cast<int>(q_first) + t) * kGroups + g) * kHeadDim;
+            const int64_t rg = a.pg.row(a.stream, a.pos0 + static_cast<int>(q_first) + t) * kGroups + g;
             float s0 = 0.f, s1 = 0.f;
+            if (a.kv_format == 0) {
+                const uint16_t* kr = static_cast<const uint16_t*>(a.k) + rg * kHeadDim;
 #pragma unroll 4
-            for (int d = 0; d < kHeadDim; d += 8) {
-                const u32x4 qa = *reinterpret_cast<const u32x4*>(qr + d);
-                const u32x4 ka = *reinterpret_cast<const u32x4*>(kr + d);
+                for (int d = 0; d < kHeadDim; d += 8) {
+                    const u32x4 qa = *reinterpret_cast<const u32x4*>(qr + d);
+                    const u32x4 ka = *reinterpret_cast<const u32x4*>(kr + d);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    s0 = __builtin_fmaf(__uint_as_float(qa[j] << 16), __uint_as_float(ka[j] << 16), s0);
-                    s1 = __builtin_fmaf(__uint_as_float(qa[j] & 0xffff0000u), __uint_as_float(ka[j] & 0xffff0000u), s1);
+                    for (int j = 0; j < 4; ++j) {
+                        s0 = __builtin_fmaf(__uint_as_float(qa[j] << 16), __uint_as_float(ka[j] << 16), s0);
+                        s1 = __builtin_fmaf(__uint_as_float(qa[j] & 0xffff0000u), __uint_as_float(ka[j] & 0xffff0000u), s1);
+                    }
+                }
+            } else {
+                // codes times their block's scale (any finite reference will do)
+#pragma unroll 1
+                for (int seg = 0; seg < kHeadDim / 8; ++seg) {
+                    float f[8];
+                    if (a.kv_format == 1) row_codes8<1>(a.k, rg, seg, f);
+                    else row_codes8<2>(a.k, rg, seg, f);
+                    const u32x4 qa = *reinterpret_cast<const u32x4*>(qr + 8 * seg);
+                    float p = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        p = __builtin_fmaf(__uint_as_float(qa[j] << 16), f[2 * j], p);
+                        p = __builtin_fmaf(__uint_as_float(qa[j] & 0xffff0000u), f[2 * j + 1], p);
+                    }
+                    s0 = __builtin_fmaf(p, a.k_scale[rg * (kHeadDim / 32) + (seg >> 2)], s0);
                 }
             }
             r = (s0 + s1) * qk_scale;
@@ -665,9 +726,10 @@ size_t prefill_attend_ws_bytes(int64_t n_q, int top_k, int32_t max_pos) {
     return ws_layout(n_q, top_k, max_pos / kBlock + 1).total;
 }
 
-hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pager& pg, const uint16_t* q,
-                                 int32_t stream, int32_t pos0, int64_t n_q, const int32_t* sel, int top_k,
-                                 float scale, float* out, void* ws, hipStream_t s) {
+hipError_t launch_prefill_attend(const void* k, const void* v, int kv_format, const float* k_scale,
+                                 const float* v_scale, const Pager& pg, const uint16_t* q, int32_t stream,
+                                 int32_t pos0, int64_t n_q, const int32_t* sel, int top_k, float scale, float* out,
+                                 void* ws, hipStream_t s) {
     const int64_t n_wg = n_tiles_of(n_q) * kGroups;
     const int last_row = static_cast<int>(pos0 + n_q - 1);
     const int nblk = last_row / kBlock + 1;
@@ -704,18 +766,28 @@ hipError_t launch_prefill_attend(const uint16_t* k, const uint16_t* v, const Pag
     KvArgs ka;
     ka.k = k;
     ka.v = v;
+    ka.k_scale = k_scale;
+    ka.v_scale = v_scale;
     ka.pg = pg;
     ka.stream = stream;
     ka.nblk = nblk;
     ka.last_row = last_row;
     ka.used = used;
     ka.kv = kv;
-    hipLaunchKernelGGL(prefill_kv_kernel, dim3(static_cast<unsigned>(4 * n_used)), dim3(kVtThreads), 0, s, ka);
+    const dim3 kv_grid(static_cast<unsigned>(4 * n_used));
+    switch (kv_format) {
+        case 0: hipLaunchKernelGGL(prefill_kv_kernel<0>, kv_grid, dim3(kVtThreads), 0, s, ka); break;
+        case 1: hipLaunchKernelGGL(prefill_kv_kernel<1>, kv_grid, dim3(kVtThreads), 0, s, ka); break;
+        case 2: hipLaunchKernelGGL(prefill_kv_kernel<2>, kv_grid, dim3(kVtThreads), 0, s, ka); break;
+        default: return hipErrorInvalidValue;
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
     PaArgs a;
     a.k = k;
+    a.k_scale = k_scale;
+    a.kv_format = kv_format;
     a.kv = kv;
     a.pg = pg;
     a.q = q;

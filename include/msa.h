@@ -336,15 +336,14 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
  * pos0 + n_q - 1 must be written (the chunk's own keys included).
  * Workspace: msa_workspace_bytes(dims, MSA_OP_ATTEND_PREFILL, n_q, max_pos)
  * bytes at d_ws (16-byte aligned; MSA_ERR_WORKSPACE_TOO_SMALL otherwise),
- * the larger of two needs, whatever the cache format: bf16 caches keep, per
- * tile of 32 consecutive queries and group, the ascending list of the blocks
- * their selections hold, built on the device before the sweep, and a copy of
- * K and V of every block some selection holds, rearranged into the order the
- * matrix-core operands take (64 KiB per block of 0 .. max_pos and group, so
- * the amount grows with max_pos as well as with n_q); quantized
- * caches (kv_format 1, 2) run the queries through decode attention in
- * launches of at most 256 consecutive queries, whose split partials the
- * workspace holds (launches on one stream, so they reuse it in turn).
+ * the same for every cache format: per tile of 32 consecutive queries and
+ * group, the ascending list of the blocks their selections hold, built on
+ * the device before the sweep, and a bf16 copy of K and V of every block
+ * some selection holds, rearranged into the order the matrix-core operands
+ * take (64 KiB per block of 0 .. max_pos and group, so the amount grows with
+ * max_pos as well as with n_q).  A quantized cache (kv_format 1, 2) is
+ * dequantized into that copy: each code times its scale, formed in f32 and
+ * rounded once to bf16 (decode attention keeps the codes exact instead).
  */
 MSA_API msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,
                               int32_t stream, int32_t pos0, int64_t n_q, const int32_t* d_sel,

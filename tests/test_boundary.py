@@ -255,31 +255,21 @@ def test_workspace_sizes(L):
     # attention partials: per (query, group, split) 16 heads x (128 + 2) floats
     n = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, 32, 32767)
     assert n % (16 * 130 * 4 * 4 * 32) == 0 and n > 0
-    # prefill attention, the larger of: bf16 caches, per (32-query tile,
-    # group) a step count (256-byte aligned array), a used flag per (group,
-    # block) (256-byte aligned), up to 32 * top_k 16-byte step entries
-    # (256-byte aligned) and K and V of every block rearranged (64 KiB per
-    # group and block); quantized caches, the decode split partials (16 heads x 130
-    # floats per query, group and split) of a launch of at most 256 queries,
-    # or of the ragged last launch.
-    def splits(n, units=16):        # about 256 workgroups, at most 8 units per split
-        return max(min(-(-256 // (4 * n)), units), -(-units // 8))
-
-    def partials(n):
-        return n * 4 * splits(n) * 16 * 130 * 4
-
+    # prefill attention (every cache format): per (32-query tile, group) a
+    # step count (256-byte aligned array), a used flag per (group, block)
+    # (256-byte aligned), up to 32 * top_k 16-byte step entries (256-byte
+    # aligned) and K and V of every block rearranged as bf16 (64 KiB per
+    # group and block)
     def up(x):
         return -(-x // 256) * 256
 
     def prefill(n, max_pos=32767):
         nblk = max_pos // 128 + 1
         n_wg = -(-n // 32) * 4
-        steps = up(n_wg * 4) + up(4 * nblk * 4) + up(n_wg * 32 * 16 * 16) + 4 * nblk * 2 * 128 * 128 * 2
-        tail = partials(n % 256) if n > 256 and n % 256 else 0
-        return max(up(steps), up(max(partials(min(n, 256)), tail)))
+        return up(up(n_wg * 4) + up(4 * nblk * 4) + up(n_wg * 32 * 16 * 16) + 4 * nblk * 2 * 128 * 128 * 2)
 
     assert prefill(4096) == 2048 + 4096 + 512 * 32 * 16 * 16 + 4 * 256 * 65536   # K and V of 256 blocks
-    assert prefill(1, 127) == 16 * 4 * 8320            # one query over one block: 16 one-block splits
+    assert prefill(1, 127) == 256 + 256 + 4 * 8192 + 4 * 65536        # one query over one block
     for n in (1, 33, 100, 256, 257, 300, 4096, 4100):
         assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, 32767) == prefill(n), n
         assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, n - 1) == prefill(n, n - 1), n
