@@ -645,12 +645,356 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float*
     if (tid == 0) n_sel[i] = top_k;
 }
 
+// ---------------------------------------------------------------------------
+// Few queries over more than one chunk of keys: the same selection spread
+// over one workgroup per 8192-key chunk, so that a 16-query call over 64K
+// keys keeps 128 compute units busy instead of 16.
+//  1. dsa_chunk_hist_kernel: each chunk's histogram of the top 12 key bits
+//     (u16 counts) into the workspace.
+//  2. dsa_chunk_split_kernel: each chunk's workgroup adds up its query's
+//     chunk histograms, picks the boundary digit d1 as the one-workgroup
+//     kernels do, and writes the ids of its keys above the boundary bin (all
+//     of them kept) and the keys and ids of those inside it, each list at the
+//     offset the earlier chunks' counts give, so both are in id order.
+//  3. dsa_finish_kernel: one workgroup per query resolves the last 12 + 8
+//     bits over the boundary list (copied into LDS when it fits), keeps the
+//     boundary keys > T and the lowest-id keys == T, and merges the two
+//     ascending id lists into the output.
+// ---------------------------------------------------------------------------
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kChunk = 8192;
+constexpr int kMwThreads = 1024;
+constexpr int kMwPer = kChunk / kMwThreads;             // 8 consecutive keys per thread
+constexpr int kMwMaxQueries = 32;
+constexpr int kMwMaxChunks = kRegKeys / kChunk;         // 8
+constexpr int kMwHistCopies = 4;
+constexpr int kFinCap = 8192;                           // boundary entries the finishing kernel holds in LDS
+
+bool use_chunks(int64_t n_q, int32_t max_pos) {
+    const int64_t n = static_cast<int64_t>(max_pos) + 1;
+    return n_q <= kMwMaxQueries && n > kChunk && n <= kRegKeys;
+}
+int n_chunks_of(int32_t max_pos) { return (max_pos + kChunk) / kChunk; }
+
+// Workspace after the scores: chunk histograms [n_q][n_chunks][4096] u16 |
+// {d1, keys still needed from bin d1, above count, boundary count} [n_q] |
+// above-bin ids [n_q][4096] | boundary keys [n_q][stride] | boundary ids
+// [n_q][stride], each region 256-byte aligned.
+struct ChunkLayout {
+    size_t hist, meta, above, bkey, bid, total;
+};
+
+__global__ __launch_bounds__(kMwThreads) void dsa_chunk_hist_kernel(const float* __restrict__ scores, int64_t stride,
+                                                                    const int32_t* __restrict__ q_pos, int top_k,
+                                                                    int n_chunks, uint16_t* __restrict__ hist_g) {
+    __shared__ int hist[kMwHistCopies][kBins];
+    const int w = blockIdx.x;
+    const int64_t i = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int n = min(q_pos[i] + 1, static_cast<int>(stride));   // (positions lie in the rows)
+    const int c0 = w * kChunk;
+    if (n <= top_k || c0 >= n) return;                  // workgroup-uniform
+    const float* t = scores + i * stride;
+    // keys j0 .. j0 + 7 (a thread whose keys all lie past the row's end
+    // reads the row's last eight scores instead, and counts none)
+    const int j0 = c0 + kMwPer * tid;
+    const int jl = min(j0, static_cast<int>(stride) - kMwPer);
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(t + jl);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(t + jl + 4);
+    for (int b = tid; b < kMwHistCopies * kBins; b += kMwThreads) (&hist[0][0])[b] = 0;
+    __syncthreads();
+    const float xs[kMwPer] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    int* hc = hist[tid % kMwHistCopies];
+#pragma unroll
+    for (int e = 0; e < kMwPer; ++e)
+        if (j0 + e < n) atomicAdd(&hc[ordered_key(xs[e]) >> 20], 1);
+    __syncthreads();
+    // thread t: bins 4t .. 4t + 3 (at most 8192 keys each: u16)
+    uint32_t c[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kMwHistCopies; ++k) sum += hist[k][4 * tid + b];
+        c[b] = static_cast<uint32_t>(sum);
+    }
+    *reinterpret_cast<u32x2*>(hist_g + ((i * n_chunks + w) * kBins + 4 * tid)) = u32x2{c[0] | (c[1] << 16), c[2] | (c[3] << 16)};
+}
+
+struct SplitArgs {
+    const float* scores;
+    int64_t stride;
+    const int32_t* q_pos;
+    int top_k;
+    int n_chunks;
+    const uint16_t* hist;
+    int32_t* meta;
+    int32_t* above;
+    uint32_t* bkey;
+    int32_t* bid;
+};
+
+__global__ __launch_bounds__(kMwThreads) void dsa_chunk_split_kernel(SplitArgs a) {
+    __shared__ int hist[kBins];
+    __shared__ int wave_sums[kMwThreads / 64];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_remaining;
+    __shared__ int s_above[kMwMaxChunks];
+    __shared__ int s_inbin[kMwMaxChunks];
+    const int w = blockIdx.x;
+    const int64_t i = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int n = min(a.q_pos[i] + 1, static_cast<int>(a.stride));
+    const int nch = (n + kChunk - 1) / kChunk;
+    if (n <= a.top_k || w >= nch) return;               // workgroup-uniform
+    if (tid < kMwMaxChunks) {
+        s_above[tid] = 0;
+        s_inbin[tid] = 0;
+    }
+    // bins 4t .. 4t + 3 of every chunk histogram of the query (chunks past
+    // the query's last key re-read its last chunk and count as empty), then
+    // the thread's own eight keys, all loads in flight together
+    u32x2 hc[kMwMaxChunks];
+#pragma unroll
+    for (int k = 0; k < kMwMaxChunks; ++k) {
+        const int kk = min(k, nch - 1);
+        hc[k] = *reinterpret_cast<const u32x2*>(a.hist + ((i * a.n_chunks + kk) * kBins + 4 * tid));
+    }
+    const float* t = a.scores + i * a.stride;
+    const int j0 = w * kChunk + kMwPer * tid;
+    const int jl = min(j0, static_cast<int>(a.stride) - kMwPer);
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(t + jl);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(t + jl + 4);
+    auto count = [&](int k, int b) __attribute__((always_inline)) {
+        const uint32_t word = (b & 2) ? hc[k].y : hc[k].x;
+        return k < nch ? static_cast<int>((word >> (16 * (b & 1))) & 0xffffu) : 0;
+    };
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        int sum = 0;
+#pragma unroll
+        for (int k = 0; k < kMwMaxChunks; ++k) sum += count(k, b);
+        hist[4 * tid + b] = sum;
+    }
+    __syncthreads();
+    pick_digit_t<kMwThreads>(hist, 12, a.top_k, wave_sums, &s_digit, &s_remaining);
+    const int d1 = static_cast<int>(s_digit);
+    const int r1 = s_remaining;
+    // per chunk: keys above bin d1 (a sum over the workgroup) and in it (one
+    // thread holds that bin)
+#pragma unroll
+    for (int k = 0; k < kMwMaxChunks; ++k) {
+        int av = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) av += 4 * tid + b > d1 ? count(k, b) : 0;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) av += __shfl_xor(av, o, 64);
+        if (lane == 0 && av) atomicAdd(&s_above[k], av);
+        if ((d1 >> 2) == tid) s_inbin[k] = count(k, d1 & 3);
+    }
+    __syncthreads();
+    int A = 0, B = 0, NA = 0, NB = 0;
+#pragma unroll
+    for (int k = 0; k < kMwMaxChunks; ++k) {
+        if (k < w) {
+            A += s_above[k];
+            B += s_inbin[k];
+        }
+        NA += s_above[k];
+        NB += s_inbin[k];
+    }
+    const float xs[kMwPer] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t key[kMwPer];
+    int na_t = 0, nb_t = 0;
+#pragma unroll
+    for (int e = 0; e < kMwPer; ++e) {
+        key[e] = ordered_key(xs[e]);
+        const bool valid = j0 + e < n;
+        const int dig = static_cast<int>(key[e] >> 20);
+        na_t += valid && dig > d1;
+        nb_t += valid && dig == d1;
+    }
+    // (at most 8192 keys per chunk: the two counts share one int)
+    const int packed = na_t + (nb_t << 16);
+    const int excl = block_scan<kMwThreads>(packed, wave_sums) - packed;
+    int oa = A + (excl & 0xffff), ob = B + (excl >> 16);
+    int32_t* above = a.above + i * kTopKMax;
+    uint32_t* bkey = a.bkey + i * a.stride;
+    int32_t* bid = a.bid + i * a.stride;
+#pragma unroll
+    for (int e = 0; e < kMwPer; ++e) {
+        if (j0 + e < n) {
+            const int dig = static_cast<int>(key[e] >> 20);
+            if (dig > d1) {
+                above[oa++] = j0 + e;
+            } else if (dig == d1) {
+                bkey[ob] = key[e];
+                bid[ob] = j0 + e;
+                ++ob;
+            }
+        }
+    }
+    if (w == 0 && tid == 0) *reinterpret_cast<int4*>(a.meta + 4 * i) = make_int4(d1, r1, NA, NB);
+}
+
+// Number of entries of the ascending list v[0 .. len) below x.
+__device__ __forceinline__ int count_below(const int32_t* v, int len, int32_t x) {
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (v[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+struct FinishArgs {
+    const int32_t* q_pos;
+    int top_k;
+    int64_t stride;
+    const int32_t* meta;
+    const int32_t* above;
+    const uint32_t* bkey;
+    const int32_t* bid;
+    int32_t* sel;
+    int32_t* n_sel;
+};
+
+__global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
+    __shared__ int hist[kBins];
+    __shared__ uint32_t lkey[kFinCap];
+    __shared__ int32_t lid[kFinCap];
+    __shared__ int32_t ab[kTopKMax];
+    __shared__ int32_t kb[kTopKMax];
+    __shared__ uint64_t wave_sums64[kMwThreads / 64];
+    __shared__ int wave_sums[kMwThreads / 64];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_remaining;
+    const int64_t i = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n = min(a.q_pos[i] + 1, static_cast<int>(a.stride));
+    const int top_k = a.top_k;
+    int32_t* out = a.sel + i * top_k;
+    if (n <= top_k) {                                   // every visible key is kept
+        for (int j = tid; j < top_k; j += kMwThreads) out[j] = j < n ? j : -1;
+        if (tid == 0) a.n_sel[i] = n;
+        return;
+    }
+    const int4 m = *reinterpret_cast<const int4*>(a.meta + 4 * i);
+    const int d1 = m.x, na = m.z, nb = m.w;
+    const uint32_t* gkey = a.bkey + i * a.stride;
+    const int32_t* gid = a.bid + i * a.stride;
+    const bool in_lds = nb <= kFinCap;                   // workgroup-uniform
+    if (in_lds) {
+        for (int e = tid; e < nb; e += kMwThreads) {
+            lkey[e] = gkey[e];
+            lid[e] = gid[e];
+        }
+    }
+    for (int e = tid; e < na; e += kMwThreads) ab[e] = a.above[i * kTopKMax + e];
+    const uint32_t* keys = in_lds ? lkey : gkey;
+    const int32_t* ids = in_lds ? lid : gid;
+    uint32_t prefix = static_cast<uint32_t>(d1) << 20, mask = 0xfff00000u;
+    int remaining = m.y;
+#pragma unroll
+    for (int pass = 1; pass < 3; ++pass) {
+        const int bits = kDigitBits[pass];
+        const int shift = pass == 1 ? 8 : 0;
+        const uint32_t dmask = (1u << bits) - 1;
+        for (int b = tid; b < kBins; b += kMwThreads) hist[b] = 0;
+        __syncthreads();
+        for (int e = tid; e < nb; e += kMwThreads) {
+            const uint32_t key = keys[e];
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+        }
+        __syncthreads();
+        pick_digit_t<kMwThreads>(hist, bits, remaining, wave_sums, &s_digit, &s_remaining);
+        prefix |= s_digit << shift;
+        mask |= dmask << shift;
+        remaining = s_remaining;
+    }
+    const uint32_t T = prefix;          // the top_k-th largest key; `remaining` boundary keys equal to it are kept
+    // kept boundary entries, in list (= id) order: thread t takes entries
+    // [t * per, (t + 1) * per)
+    const int per = (nb + kMwThreads - 1) / kMwThreads;
+    const int e0 = min(tid * per, nb), e1 = min(e0 + per, nb);
+    uint32_t n_gt = 0, n_eq = 0;
+    for (int e = e0; e < e1; ++e) {
+        const uint32_t key = keys[e];
+        n_gt += key > T;
+        n_eq += key == T;
+    }
+    const uint64_t packed = static_cast<uint64_t>(n_gt) | (static_cast<uint64_t>(n_eq) << 32);
+    const uint64_t excl = block_scan<kMwThreads>(packed, wave_sums64) - packed;
+    const int gt_before = static_cast<int>(excl & 0xffffffffu);
+    int eq_rank = static_cast<int>(excl >> 32);
+    int slot = gt_before + min(eq_rank, remaining);
+    for (int e = e0; e < e1; ++e) {
+        const uint32_t key = keys[e];
+        if (key > T) {
+            kb[slot++] = ids[e];
+        } else if (key == T) {
+            if (eq_rank < remaining) kb[slot++] = ids[e];
+            ++eq_rank;
+        }
+    }
+    __syncthreads();
+    // merge the two ascending lists: an id's place is its rank in its own
+    // list plus the number of ids below it in the other
+    const int nk = top_k - na;
+    for (int j = tid; j < na; j += kMwThreads) {
+        const int32_t id = ab[j];
+        out[j + count_below(kb, nk, id)] = id;
+    }
+    for (int j = tid; j < nk; j += kMwThreads) {
+        const int32_t id = kb[j];
+        out[j + count_below(ab, na, id)] = id;
+    }
+    if (tid == 0) a.n_sel[i] = top_k;
+}
+
 int64_t score_stride(int32_t max_pos) {
     return ((static_cast<int64_t>(max_pos) + 1 + 63) / 64) * 64;
 }
 
-hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int64_t n_q, int32_t max_pos,
+ChunkLayout chunk_layout(int64_t n_q, int32_t max_pos) {
+    const size_t stride = static_cast<size_t>(score_stride(max_pos));
+    auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+    ChunkLayout l;
+    l.hist = up(static_cast<size_t>(n_q) * stride * sizeof(float));
+    l.meta = l.hist + up(static_cast<size_t>(n_q) * n_chunks_of(max_pos) * kBins * sizeof(uint16_t));
+    l.above = l.meta + up(static_cast<size_t>(n_q) * 4 * sizeof(int32_t));
+    l.bkey = l.above + up(static_cast<size_t>(n_q) * kTopKMax * sizeof(int32_t));
+    l.bid = l.bkey + up(static_cast<size_t>(n_q) * stride * sizeof(uint32_t));
+    l.total = l.bid + static_cast<size_t>(n_q) * stride * sizeof(int32_t);
+    return l;
+}
+
+hipError_t launch_topk(void* ws, int64_t stride, const int32_t* pos, int64_t n_q, int32_t max_pos,
                        int top_k, int32_t* sel, int32_t* n_sel, hipStream_t s) {
+    const float* scores = static_cast<const float*>(ws);
+    if (use_chunks(n_q, max_pos)) {
+        const ChunkLayout l = chunk_layout(n_q, max_pos);
+        char* base = static_cast<char*>(ws);
+        const int nc = n_chunks_of(max_pos);
+        uint16_t* hist = reinterpret_cast<uint16_t*>(base + l.hist);
+        int32_t* meta = reinterpret_cast<int32_t*>(base + l.meta);
+        int32_t* above = reinterpret_cast<int32_t*>(base + l.above);
+        uint32_t* bkey = reinterpret_cast<uint32_t*>(base + l.bkey);
+        int32_t* bid = reinterpret_cast<int32_t*>(base + l.bid);
+        const dim3 grid(static_cast<unsigned>(nc), static_cast<unsigned>(n_q));
+        hipLaunchKernelGGL(dsa_chunk_hist_kernel, grid, dim3(kMwThreads), 0, s, scores, stride, pos, top_k, nc, hist);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dsa_chunk_split_kernel, grid, dim3(kMwThreads), 0, s,
+                           SplitArgs{scores, stride, pos, top_k, nc, hist, meta, above, bkey, bid});
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(dsa_finish_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kMwThreads), 0, s,
+                           FinishArgs{pos, top_k, stride, meta, above, bkey, bid, sel, n_sel});
+        return hipGetLastError();
+    }
     if (static_cast<int64_t>(max_pos) + 1 <= kRegKeys)
         hipLaunchKernelGGL(dsa_topk_regs_kernel, dim3(static_cast<unsigned>(n_q)), dim3(kRegThreads), 0, s, scores,
                            stride, pos, top_k, sel, n_sel);
@@ -663,6 +1007,7 @@ hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, 
 }  // namespace
 
 size_t dsa_select_ws_bytes(int64_t n_q, int32_t max_pos) {
+    if (use_chunks(n_q, max_pos)) return chunk_layout(n_q, max_pos).total;
     return static_cast<size_t>(n_q) * score_stride(max_pos) * sizeof(float);
 }
 
@@ -677,7 +1022,7 @@ hipError_t launch_dsa_select(const uint16_t* dsa_k, const Pager& pg, const uint1
                        pg, q_idx, stream, pos, scores, stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_topk(scores, stride, pos, n_q, max_pos, top_k, sel, n_sel, s);
+    return launch_topk(ws, stride, pos, n_q, max_pos, top_k, sel, n_sel, s);
 }
 
 hipError_t launch_dsa_select_heads(const uint16_t* dsa_k, const Pager& pg, const uint16_t* q_idx_h,
@@ -701,7 +1046,7 @@ hipError_t launch_dsa_select_heads(const uint16_t* dsa_k, const Pager& pg, const
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_topk(scores, stride, pos, n_q, max_pos, top_k, sel, n_sel, s);
+    return launch_topk(ws, stride, pos, n_q, max_pos, top_k, sel, n_sel, s);
 }
 
 }  // namespace msa

@@ -370,7 +370,11 @@ MSA_API msa_status dsa_index_append(const msa_dims* dims, const msa_cache* cache
  * for j <= pos; keeps k = min(top_k, pos + 1) keys with the largest t, ties
  * to the lower token id, no local forcing.  Writes d_sel [n_q][top_k]
  * ascending token ids padded with -1 and d_n_sel [n_q] = k.
- *   d_q_idx [n_q][idx_dim] fp16.  Workspace: DSA_OP_SELECT.
+ *   d_q_idx [n_q][idx_dim] fp16.  Workspace: DSA_OP_SELECT, the f32 scores
+ *   (one row of max_pos + 1 rounded up to 64 per query) and, for calls of at
+ *   most 32 queries over 8193 .. 65536 keys, whose top-k runs over one
+ *   workgroup per 8192-key chunk: the chunks' first-digit histograms, the
+ *   kept ids above the boundary bin and the boundary bin's keys and ids.
  */
 MSA_API msa_status dsa_select(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q_idx,
                       const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,

@@ -274,7 +274,17 @@ def test_workspace_sizes(L):
         assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, 32767) == prefill(n), n
         assert M.workspace_bytes(d, M.MSA_OP_ATTEND_PREFILL, n, n - 1) == prefill(n, n - 1), n
     dd = M.dsa_dims()
-    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == 16 * 65536 * 4
+    # DSA select: the f32 score rows (max_pos + 1 rounded up to 64); calls of
+    # at most 32 queries over 8193 .. 65536 keys add, 256-byte aligned, the
+    # chunk histograms (4096 u16 per 8192-key chunk), four ints, 4096 above-bin
+    # ids and a boundary list of (key, id) per query
+    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 33, 65535) == 33 * 65536 * 4
+    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 70000) == 16 * 70016 * 4
+    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 8191) == 16 * 8192 * 4
+    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 16, 65535) == (
+        16 * 65536 * 4 + 16 * 8 * 4096 * 2 + 256 + 16 * 4096 * 4 + 16 * 65536 * 4 + 16 * 65536 * 4)
+    assert M.workspace_bytes(dd, M.DSA_OP_SELECT, 1, 8192) == (
+        up(8256 * 4) + up(2 * 4096 * 2) + 256 + up(4096 * 4) + up(8256 * 4) + 8256 * 4)
     with pytest.raises(M.MsaError):
         M.workspace_bytes(d, M.DSA_OP_SELECT, 16, 65535)   # DSA op needs DSA dims
 

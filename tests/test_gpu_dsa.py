@@ -131,3 +131,49 @@ def test_dsa_topk_with_ties_exact(top_k):
     o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
     assert np.array_equal(n_sel.cpu().numpy(), o_nsel)
     assert np.array_equal(sel.cpu().numpy(), o_sel), "selection differs from the oracle"
+
+
+@pytest.mark.parametrize("ints", [True, False])
+def test_dsa_topk_chunked_equals_one_workgroup(ints):
+    """Calls of at most 32 queries over more than 8192 keys rank each query's
+    scores over one workgroup per 8192-key chunk; larger calls use one
+    workgroup per query.  Both are exact, so 40 queries in one call and their
+    first 8 and last 32 in calls of their own select the same ids bit for
+    bit (integer scores: ties everywhere, also equal to the oracle's; Gaussian
+    keys: distinct scores), at context lengths across chunk edges."""
+    S, cap, top_k = 2, 30000, 2048
+    rng = np.random.default_rng(29 if ints else 31)
+    if ints:
+        k_rot = rng.integers(-2, 3, size=(S, cap, 128)).astype(np.float16)
+        q = rng.integers(-1, 2, size=(40, 128)).astype(np.float16)
+    else:
+        k_rot = rng.standard_normal((S, cap, 128)).astype(np.float16)
+        q = rng.standard_normal((40, 128)).astype(np.float16)
+    pos = rng.integers(2048, cap, size=40).astype(np.int32)
+    pos[:6] = [8191, 8192, 16383, 16384, 29999, 2047]
+    stream = rng.integers(0, S, size=40).astype(np.int32)
+    log(f"[dsa] chunked vs one-workgroup top-k, integer scores {ints}")
+    dims = M.dsa_dims(top_k, W.SCALE)
+    kv = torch.zeros((S, cap, 4, 128), dtype=torch.bfloat16, device=DEV)
+    cache = M.make_cache(k=kv, v=kv, dsa_k=torch.from_numpy(k_rot).to(DEV))
+    qd = torch.from_numpy(q).to(DEV)
+
+    def select(lo, hi):
+        n = hi - lo
+        sel = torch.empty((n, top_k), dtype=torch.int32, device=DEV)
+        n_sel = torch.empty(n, dtype=torch.int32, device=DEV)
+        mp = int(pos[lo:hi].max())
+        ws = torch.empty(M.workspace_bytes(dims, M.DSA_OP_SELECT, n, mp), dtype=torch.uint8, device=DEV)
+        M.dsa_select(dims, cache, qd[lo:hi].contiguous(), dev(stream[lo:hi]), dev(pos[lo:hi]), mp, sel, n_sel, ws)
+        torch.cuda.synchronize()
+        return sel.cpu().numpy(), n_sel.cpu().numpy()
+
+    s_all, n_all = select(0, 40)
+    s_a, n_a = select(0, 8)
+    s_b, n_b = select(8, 40)
+    assert np.array_equal(np.concatenate([s_a, s_b]), s_all)
+    assert np.array_equal(np.concatenate([n_a, n_b]), n_all)
+    if ints:
+        o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
+        assert np.array_equal(n_all, o_nsel)
+        assert np.array_equal(s_all, o_sel), "selection differs from the oracle"
