@@ -192,32 +192,47 @@ __global__ __launch_bounds__(64 * kMhWaves) void dsa_score_heads_kernel(
     }
 }
 
-// Inclusive prefix sum over the kThreads threads of the workgroup (T: int,
-// or a u64 holding two counts that never carry into each other).
-template <int kThreads, typename T>
+// Inclusive prefix sum over the 64 lanes of a wave: row_shr DPP steps inside
+// each 16-lane row, then the totals of the lower rows (read from lanes 15,
+// 31, 47) are added.
+__device__ __forceinline__ int wave_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);    // row_shr:1 (lanes past the row's start read 0)
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);    // row_shr:8
+    const int r = (threadIdx.x & 63) >> 4;
+    const int t0 = __builtin_amdgcn_readlane(x, 15);
+    const int t1 = __builtin_amdgcn_readlane(x, 31);
+    const int t2 = __builtin_amdgcn_readlane(x, 47);
+    return x + (r >= 1 ? t0 : 0) + (r >= 2 ? t1 : 0) + (r >= 3 ? t2 : 0);
+}
+// Sum over the 64 lanes of a wave (every lane gets it): DPP inside each
+// 16-lane row, then the four row totals.
+__device__ __forceinline__ int wave_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);     // quad_perm [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);     // quad_perm [2,3,0,1]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);    // row_half_mirror
+    x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false);    // row_mirror
+    return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+           __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+// Inclusive prefix sum over the kThreads threads of the workgroup: wave
+// scans, one barrier, each wave adds the totals of the waves below it.
+// With kDone, a final barrier frees wave_sums for the next use (a caller
+// that ends in a barrier of its own before reusing it passes false).
+template <int kThreads, typename T, bool kDone = true>
 __device__ T block_scan(T v, T* wave_sums) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const T y = __shfl_up(v, o, 64);
-        if (lane >= o) v += y;
-    }
+    v = wave_scan(v);
     if (lane == 63) wave_sums[wave] = v;
     __syncthreads();
-    if (wave == 0) {
-        T sum = lane < kThreads / 64 ? wave_sums[lane] : T(0);
+    T below = T(0);
 #pragma unroll
-        for (int o = 1; o < kThreads / 64; o <<= 1) {
-            const T y = __shfl_up(sum, o, 64);
-            if (lane >= o) sum += y;
-        }
-        if (lane < kThreads / 64) wave_sums[lane] = sum;
-    }
-    __syncthreads();
-    if (wave > 0) v += wave_sums[wave - 1];
-    __syncthreads();
-    return v;
+    for (int w = 0; w < kThreads / 64; ++w) below += w < wave ? wave_sums[w] : T(0);
+    if (kDone) __syncthreads();
+    return v + below;
 }
 __device__ int block_inclusive_scan(int v, int* wave_sums) { return block_scan<kSelThreads>(v, wave_sums); }
 
@@ -284,7 +299,7 @@ __device__ __forceinline__ void pick_digit_t(const int* hist, int bits, int rema
         c[e] = dd < nb ? hist[nb - 1 - dd] : 0;
         csum += c[e];
     }
-    const int incl = block_scan<kThreads>(csum, wave_sums);
+    const int incl = block_scan<kThreads, int, false>(csum, wave_sums);   // the barrier below frees wave_sums
     if (incl >= remaining && incl - csum < remaining) {
         int before = incl - csum;
 #pragma unroll
@@ -657,9 +672,10 @@ __global__ __launch_bounds__(kRegThreads) void dsa_topk_regs_kernel(const float*
 //     of them kept) and the keys and ids of those inside it, each list at the
 //     offset the earlier chunks' counts give, so both are in id order.
 //  3. dsa_finish_kernel: one workgroup per query resolves the last 12 + 8
-//     bits over the boundary list (copied into LDS when it fits), keeps the
-//     boundary keys > T and the lowest-id keys == T, and merges the two
-//     ascending id lists into the output.
+//     bits over the boundary list (copied into LDS when it fits), marks the
+//     above-bin ids, the boundary keys > T and the lowest-id keys == T in a
+//     bit map of the ids, and writes the marked ids in order (each thread's
+//     place from a scan of its map words' popcounts).
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kChunk = 8192;
@@ -781,17 +797,23 @@ __global__ __launch_bounds__(kMwThreads) void dsa_chunk_split_kernel(SplitArgs a
     pick_digit_t<kMwThreads>(hist, 12, a.top_k, wave_sums, &s_digit, &s_remaining);
     const int d1 = static_cast<int>(s_digit);
     const int r1 = s_remaining;
-    // per chunk: keys above bin d1 (a sum over the workgroup) and in it (one
-    // thread holds that bin)
+    // per chunk: keys above bin d1 (a sum over the workgroup; two chunks'
+    // counts share an int, at most 8192 each) and in it (one thread holds
+    // that bin)
 #pragma unroll
-    for (int k = 0; k < kMwMaxChunks; ++k) {
+    for (int k = 0; k < kMwMaxChunks; k += 2) {
         int av = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) av += 4 * tid + b > d1 ? count(k, b) : 0;
+        for (int b = 0; b < 4; ++b) av += 4 * tid + b > d1 ? count(k, b) + (count(k + 1, b) << 16) : 0;
+        av = wave_sum(av);
+        if (lane == 0 && av) {
+            atomicAdd(&s_above[k], av & 0xffff);
+            atomicAdd(&s_above[k + 1], av >> 16);
+        }
+    }
+    if ((d1 >> 2) == tid) {
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) av += __shfl_xor(av, o, 64);
-        if (lane == 0 && av) atomicAdd(&s_above[k], av);
-        if ((d1 >> 2) == tid) s_inbin[k] = count(k, d1 & 3);
+        for (int k = 0; k < kMwMaxChunks; ++k) s_inbin[k] = count(k, d1 & 3);
     }
     __syncthreads();
     int A = 0, B = 0, NA = 0, NB = 0;
@@ -826,27 +848,20 @@ __global__ __launch_bounds__(kMwThreads) void dsa_chunk_split_kernel(SplitArgs a
     for (int e = 0; e < kMwPer; ++e) {
         if (j0 + e < n) {
             const int dig = static_cast<int>(key[e] >> 20);
+            // (the bounds hold by the counts; kept as guards)
             if (dig > d1) {
-                above[oa++] = j0 + e;
+                if (oa < kTopKMax) above[oa] = j0 + e;
+                ++oa;
             } else if (dig == d1) {
-                bkey[ob] = key[e];
-                bid[ob] = j0 + e;
+                if (ob < n) {
+                    bkey[ob] = key[e];
+                    bid[ob] = j0 + e;
+                }
                 ++ob;
             }
         }
     }
     if (w == 0 && tid == 0) *reinterpret_cast<int4*>(a.meta + 4 * i) = make_int4(d1, r1, NA, NB);
-}
-
-// Number of entries of the ascending list v[0 .. len) below x.
-__device__ __forceinline__ int count_below(const int32_t* v, int len, int32_t x) {
-    int lo = 0, hi = len;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (v[mid] < x) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
 }
 
 struct FinishArgs {
@@ -865,9 +880,7 @@ __global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
     __shared__ int hist[kBins];
     __shared__ uint32_t lkey[kFinCap];
     __shared__ int32_t lid[kFinCap];
-    __shared__ int32_t ab[kTopKMax];
-    __shared__ int32_t kb[kTopKMax];
-    __shared__ uint64_t wave_sums64[kMwThreads / 64];
+    __shared__ uint32_t idmap[kRegKeys / 32];           // kept ids, one bit each
     __shared__ int wave_sums[kMwThreads / 64];
     __shared__ uint32_t s_digit;
     __shared__ int s_remaining;
@@ -881,18 +894,30 @@ __global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
         if (tid == 0) a.n_sel[i] = n;
         return;
     }
+    // the counts, the first kFinCap list entries and the above-bin ids are
+    // loaded together, before the counts are known (the lists hold at least
+    // kFinCap and kTopKMax entries: a row of more than 8192 scores each)
     const int4 m = *reinterpret_cast<const int4*>(a.meta + 4 * i);
-    const int d1 = m.x, na = m.z, nb = m.w;
     const uint32_t* gkey = a.bkey + i * a.stride;
     const int32_t* gid = a.bid + i * a.stride;
-    const bool in_lds = nb <= kFinCap;                   // workgroup-uniform
-    if (in_lds) {
-        for (int e = tid; e < nb; e += kMwThreads) {
-            lkey[e] = gkey[e];
-            lid[e] = gid[e];
-        }
+    constexpr int kLd = kFinCap / kMwThreads, kLa = kTopKMax / kMwThreads;
+    uint32_t kk[kLd];
+    int32_t ii[kLd], aa[kLa];
+#pragma unroll
+    for (int r = 0; r < kLd; ++r) {
+        kk[r] = gkey[tid + kMwThreads * r];
+        ii[r] = gid[tid + kMwThreads * r];
     }
-    for (int e = tid; e < na; e += kMwThreads) ab[e] = a.above[i * kTopKMax + e];
+#pragma unroll
+    for (int r = 0; r < kLa; ++r) aa[r] = a.above[i * kTopKMax + tid + kMwThreads * r];
+    for (int wd = tid; wd < kRegKeys / 32; wd += kMwThreads) idmap[wd] = 0u;
+    const int d1 = m.x, na = m.z, nb = m.w;
+    const bool in_lds = nb <= kFinCap;                   // workgroup-uniform
+#pragma unroll
+    for (int r = 0; r < kLd; ++r) {
+        lkey[tid + kMwThreads * r] = kk[r];
+        lid[tid + kMwThreads * r] = ii[r];
+    }
     const uint32_t* keys = in_lds ? lkey : gkey;
     const int32_t* ids = in_lds ? lid : gid;
     uint32_t prefix = static_cast<uint32_t>(d1) << 20, mask = 0xfff00000u;
@@ -915,41 +940,41 @@ __global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
         remaining = s_remaining;
     }
     const uint32_t T = prefix;          // the top_k-th largest key; `remaining` boundary keys equal to it are kept
-    // kept boundary entries, in list (= id) order: thread t takes entries
-    // [t * per, (t + 1) * per)
+    // kept ids into the bit map: every above-bin id, the boundary keys > T
+    // and the first `remaining` boundary keys == T in list (= id) order
+    // (thread t takes entries [t * per, (t + 1) * per))
+    auto keep = [&](int32_t id) __attribute__((always_inline)) {
+        atomicOr(&idmap[(id >> 5) & (kRegKeys / 32 - 1)], 1u << (id & 31));
+    };
+#pragma unroll
+    for (int r = 0; r < kLa; ++r)
+        if (tid + kMwThreads * r < na) keep(aa[r]);
     const int per = (nb + kMwThreads - 1) / kMwThreads;
     const int e0 = min(tid * per, nb), e1 = min(e0 + per, nb);
-    uint32_t n_gt = 0, n_eq = 0;
-    for (int e = e0; e < e1; ++e) {
-        const uint32_t key = keys[e];
-        n_gt += key > T;
-        n_eq += key == T;
-    }
-    const uint64_t packed = static_cast<uint64_t>(n_gt) | (static_cast<uint64_t>(n_eq) << 32);
-    const uint64_t excl = block_scan<kMwThreads>(packed, wave_sums64) - packed;
-    const int gt_before = static_cast<int>(excl & 0xffffffffu);
-    int eq_rank = static_cast<int>(excl >> 32);
-    int slot = gt_before + min(eq_rank, remaining);
+    int n_eq = 0;
+    for (int e = e0; e < e1; ++e) n_eq += keys[e] == T;
+    int eq_rank = block_scan<kMwThreads>(n_eq, wave_sums) - n_eq;
     for (int e = e0; e < e1; ++e) {
         const uint32_t key = keys[e];
         if (key > T) {
-            kb[slot++] = ids[e];
+            keep(ids[e]);
         } else if (key == T) {
-            if (eq_rank < remaining) kb[slot++] = ids[e];
+            if (eq_rank < remaining) keep(ids[e]);
             ++eq_rank;
         }
     }
     __syncthreads();
-    // merge the two ascending lists: an id's place is its rank in its own
-    // list plus the number of ids below it in the other
-    const int nk = top_k - na;
-    for (int j = tid; j < na; j += kMwThreads) {
-        const int32_t id = ab[j];
-        out[j + count_below(kb, nk, id)] = id;
-    }
-    for (int j = tid; j < nk; j += kMwThreads) {
-        const int32_t id = kb[j];
-        out[j + count_below(ab, na, id)] = id;
+    // the output in id order: thread t writes the kept ids of its two words
+    // (ids 64t .. 64t + 63) after the kept ids of the lower words
+    const uint32_t w0 = idmap[2 * tid], w1 = idmap[2 * tid + 1];
+    const int c = __builtin_popcount(w0) + __builtin_popcount(w1);
+    int o = block_scan<kMwThreads>(c, wave_sums) - c;
+    uint64_t bm = static_cast<uint64_t>(w0) | (static_cast<uint64_t>(w1) << 32);
+    while (bm) {
+        const int b = __builtin_ctzll(bm);
+        if (o < top_k) out[o] = 64 * tid + b;           // exactly top_k bits are set; the bound is defensive
+        ++o;
+        bm &= bm - 1;
     }
     if (tid == 0) a.n_sel[i] = top_k;
 }
