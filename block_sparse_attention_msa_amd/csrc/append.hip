@@ -45,7 +45,10 @@ __device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
     return static_cast<double>(__builtin_bit_cast(_Float16, h));   // exact
 }
 
-// One workgroup of 128 threads per new row.
+// One workgroup of 128 threads per new row.  Every source row is loaded
+// before the destination slot is known (the slot needs the row's stream and
+// position, and a paged cache its block table), so the loads and the slot
+// lookup overlap instead of following one another.
 __global__ __launch_bounds__(128) void append_kernel(
     float* __restrict__ idx_k, uint16_t* __restrict__ idx_k16, uint16_t* __restrict__ dsa_k, uint16_t* __restrict__ k,
     uint16_t* __restrict__ v, Pager pg, const int32_t* __restrict__ stream,
@@ -54,35 +57,40 @@ __global__ __launch_bounds__(128) void append_kernel(
     const uint16_t* __restrict__ v_new, double inv_sqrt_n) {
     const int64_t i = blockIdx.x;
     const int tid = threadIdx.x;
-    const int64_t slot = pg.row(stream[i], pos[i]);
+    const int32_t st = stream[i], ps = pos[i];
+    // 4 x 128 f32 index values = 128 x 16 B; 4 x 128 bf16 of K and of V = 64 x 16 B each
+    u32x4 xi = u32x4{0u, 0u, 0u, 0u}, xk = xi, xv = xi;
+    if (idx_k_new) xi = reinterpret_cast<const u32x4*>(idx_k_new + i * kGroups * kIdxDim)[tid];
+    if (tid < 64) {
+        if (k_new) xk = reinterpret_cast<const u32x4*>(k_new + i * kGroups * kHeadDim)[tid];
+        if (v_new) xv = reinterpret_cast<const u32x4*>(v_new + i * kGroups * kHeadDim)[tid];
+    }
+    uint16_t h0 = 0, h1 = 0;                        // DSA key elements tid and tid + 64
+    if (dsa_key_new && tid < 64) {
+        h0 = dsa_key_new[i * kIdxDim + tid];
+        h1 = dsa_key_new[i * kIdxDim + tid + 64];
+    }
+    const int64_t slot = pg.row(st, ps);
 
-    if (idx_k_new) {   // 4 x 128 f32 = 128 x 16 B
-        const u32x4* src = reinterpret_cast<const u32x4*>(idx_k_new + i * kGroups * kIdxDim);
+    if (idx_k_new) {
         if (idx_k16) {     // fp16 cache: 4 keys -> 8 B per thread
-            const f32x4 x = __builtin_bit_cast(f32x4, src[tid]);
+            const f32x4 x = __builtin_bit_cast(f32x4, xi);
             typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
             const f16x4 h = __builtin_convertvector(x, f16x4);    // round to nearest even
             typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
             reinterpret_cast<u32x2_t*>(idx_k16 + slot * kGroups * kIdxDim)[tid] = __builtin_bit_cast(u32x2_t, h);
         } else {
-            reinterpret_cast<u32x4*>(idx_k + slot * kGroups * kIdxDim)[tid] = src[tid];
+            reinterpret_cast<u32x4*>(idx_k + slot * kGroups * kIdxDim)[tid] = xi;
         }
     }
-    if (tid < 64) {    // 4 x 128 bf16 = 64 x 16 B each
-        if (k_new) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(k_new + i * kGroups * kHeadDim);
-            reinterpret_cast<u32x4*>(k + slot * kGroups * kHeadDim)[tid] = src[tid];
-        }
-        if (v_new) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(v_new + i * kGroups * kHeadDim);
-            reinterpret_cast<u32x4*>(v + slot * kGroups * kHeadDim)[tid] = src[tid];
-        }
+    if (tid < 64) {
+        if (k_new) reinterpret_cast<u32x4*>(k + slot * kGroups * kHeadDim)[tid] = xk;
+        if (v_new) reinterpret_cast<u32x4*>(v + slot * kGroups * kHeadDim)[tid] = xv;
     }
     if (dsa_key_new && tid < 64) {
         // lane l holds elements l and l + 64 of the 128-point transform
-        const uint16_t* x = dsa_key_new + i * kIdxDim;
-        double e0 = f16_bits_to_f64(x[tid]);
-        double e1 = f16_bits_to_f64(x[tid + 64]);
+        double e0 = f16_bits_to_f64(h0);
+        double e1 = f16_bits_to_f64(h1);
         double t = e0 + e1;                           // butterfly of span 64 (in lane)
         e1 = e0 - e1;
         e0 = t;

@@ -894,13 +894,15 @@ __global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
         if (tid == 0) a.n_sel[i] = n;
         return;
     }
-    // the counts, the first kFinCap list entries and the above-bin ids are
-    // loaded together, before the counts are known (the lists hold at least
-    // kFinCap and kTopKMax entries: a row of more than 8192 scores each)
+    // the counts, the first kSpec list entries and the above-bin ids (fewer
+    // than top_k) are loaded together, before the counts are known (the
+    // lists hold at least 8192 and kTopKMax entries: a row of more than 8192
+    // scores each); a longer list that fits in LDS takes a second round
     const int4 m = *reinterpret_cast<const int4*>(a.meta + 4 * i);
     const uint32_t* gkey = a.bkey + i * a.stride;
     const int32_t* gid = a.bid + i * a.stride;
-    constexpr int kLd = kFinCap / kMwThreads, kLa = kTopKMax / kMwThreads;
+    constexpr int kSpec = 2048;
+    constexpr int kLd = kSpec / kMwThreads, kLa = kTopKMax / kMwThreads;
     uint32_t kk[kLd];
     int32_t ii[kLd], aa[kLa];
 #pragma unroll
@@ -909,7 +911,10 @@ __global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
         ii[r] = gid[tid + kMwThreads * r];
     }
 #pragma unroll
-    for (int r = 0; r < kLa; ++r) aa[r] = a.above[i * kTopKMax + tid + kMwThreads * r];
+    for (int r = 0; r < kLa; ++r) {
+        const int e = tid + kMwThreads * r;
+        aa[r] = e < top_k ? a.above[i * kTopKMax + e] : 0;
+    }
     for (int wd = tid; wd < kRegKeys / 32; wd += kMwThreads) idmap[wd] = 0u;
     const int d1 = m.x, na = m.z, nb = m.w;
     const bool in_lds = nb <= kFinCap;                   // workgroup-uniform
@@ -917,6 +922,12 @@ __global__ __launch_bounds__(kMwThreads) void dsa_finish_kernel(FinishArgs a) {
     for (int r = 0; r < kLd; ++r) {
         lkey[tid + kMwThreads * r] = kk[r];
         lid[tid + kMwThreads * r] = ii[r];
+    }
+    if (in_lds) {
+        for (int e = kSpec + tid; e < nb; e += kMwThreads) {
+            lkey[e] = gkey[e];
+            lid[e] = gid[e];
+        }
     }
     const uint32_t* keys = in_lds ? lkey : gkey;
     const int32_t* ids = in_lds ? lid : gid;

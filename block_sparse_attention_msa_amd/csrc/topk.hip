@@ -85,9 +85,11 @@ __device__ __forceinline__ void write_ascending(const int32_t* chosen, int k, in
 // memory.  kOneSub: one score per block (no partial maxima to fold), which
 // keeps the widest instantiation's key loop free of an inner loop (that would
 // stop its unrolling and turn the keys into an indexed array).
+// pre: the first score of each candidate, loaded by the caller (with one
+// score per block, before the query's position is known).
 template <int kPer, bool kOneSub>
-__device__ __forceinline__ void topk_in_registers(const float* row, int n_sub, int nvis, int loc, int k, int lane,
-                                                  int32_t* chosen) {
+__device__ __forceinline__ void topk_in_registers(const float* row, const float* pre, int n_sub, int nvis, int loc,
+                                                  int k, int lane, int32_t* chosen) {
     uint64_t key[kPer];
     // (loads of blocks past nvis read block 0 and are masked: every load is
     // unconditional, so that they are all in flight together)
@@ -95,9 +97,13 @@ __device__ __forceinline__ void topk_in_registers(const float* row, int n_sub, i
     for (int j = 0; j < kPer; ++j) {
         const int b = lane + 64 * j;
         const int bl = b < nvis ? b : 0;
-        float sc = row[kOneSub ? bl : bl * n_sub];
-        if constexpr (!kOneSub)
-            for (int e = 1; e < n_sub; ++e) sc = fmaxf(sc, row[bl * n_sub + e]);
+        float sc = pre[j];
+        if constexpr (!kOneSub) {
+            if (n_sub > 1) {
+                sc = row[bl * n_sub];
+                for (int e = 1; e < n_sub; ++e) sc = fmaxf(sc, row[bl * n_sub + e]);
+            }
+        }
         const uint64_t kb = (static_cast<uint64_t>(ordered_key(sc)) << 31) | static_cast<uint64_t>(0x7fffffff - b) |
                             (b == loc ? 1ull << 63 : 0ull);
         key[j] = b < nvis ? kb : 0ull;
@@ -130,16 +136,29 @@ __global__ __launch_bounds__(64) void topk_blocks_kernel(const float* __restrict
     const int64_t qg = blockIdx.x;                 // query * kGroups + group
     const int64_t i = qg / kGroups;
     const int lane = threadIdx.x;
+    const float* row = bs + qg * nblk_stride;
+    // with one score per block, the register path's candidate scores load
+    // together with the query's position (candidates past the row read
+    // block 0; those past the visible blocks are masked later)
+    constexpr int kPre = kPer > 0 ? kPer : 1;
+    float pre[kPre];
+    if (kPer > 0 && n_sub == 1) {
+        const int nb_row = static_cast<int>(nblk_stride);
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+            const int b = lane + 64 * j;
+            pre[j] = row[b < nb_row ? b : 0];
+        }
+    }
     const int loc = (q_pos ? q_pos[i] : pos0 + static_cast<int>(i)) / kBlock;
     const int nvis = loc + 1;
-    const float* row = bs + qg * nblk_stride;
 
     // (the widest register path only for one score per block; partial
     // maxima of a fine scan come with short contexts only)
     if (kPer > 0 && nvis > 64 && nvis <= 64 * kPer && (kPer <= 8 || n_sub == 1)) {
         const int k = min(top_k, nvis);
-        if constexpr (kPer > 8) topk_in_registers<kPer, true>(row, n_sub, nvis, loc, k, lane, chosen);
-        else if constexpr (kPer > 0) topk_in_registers<kPer, false>(row, n_sub, nvis, loc, k, lane, chosen);
+        if constexpr (kPer > 8) topk_in_registers<kPer, true>(row, pre, n_sub, nvis, loc, k, lane, chosen);
+        else if constexpr (kPer > 0) topk_in_registers<kPer, false>(row, pre, n_sub, nvis, loc, k, lane, chosen);
         __syncthreads();
         write_ascending(chosen, k, top_k, lane, sel + qg * top_k);
         if (lane == 0) n_sel[qg] = k;
