@@ -177,3 +177,31 @@ def test_dsa_topk_chunked_equals_one_workgroup(ints):
         o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
         assert np.array_equal(n_all, o_nsel)
         assert np.array_equal(s_all, o_sel), "selection differs from the oracle"
+
+
+def test_dsa_topk_boundary_tie_list_over_2048():
+    """5000 keys share the boundary score (a planted mid-level key), 1500 rank
+    above it: the chunked top-k's boundary list holds about 5000 entries,
+    more than it loads ahead of its counts but fewer than its LDS copy
+    holds, and the kept ties are the lowest ids.  Exact against the oracle."""
+    S, cap, top_k = 1, 30000, 2048
+    rng = np.random.default_rng(37)
+    k_rot = rng.integers(-1, 2, size=(S, cap, 128)).astype(np.float16)
+    ids = rng.permutation(cap)
+    k_rot[0, ids[:1500]] = 1.0                                   # score 128
+    k_rot[0, ids[1500:6500]] = np.where(np.arange(128) < 64, 1.0, 0.0).astype(np.float16)   # score 64
+    q = np.ones((2, 128), np.float16)
+    pos = np.array([29999, 21000], np.int32)
+    stream = np.zeros(2, np.int32)
+    log("[dsa] boundary tie list over 2048 entries")
+    dims = M.dsa_dims(top_k, W.SCALE)
+    kv = torch.zeros((S, cap, 4, 128), dtype=torch.bfloat16, device=DEV)
+    cache = M.make_cache(k=kv, v=kv, dsa_k=torch.from_numpy(k_rot).to(DEV))
+    sel = torch.empty((2, top_k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty(2, dtype=torch.int32, device=DEV)
+    ws = torch.empty(M.workspace_bytes(dims, M.DSA_OP_SELECT, 2, int(pos.max())), dtype=torch.uint8, device=DEV)
+    M.dsa_select(dims, cache, torch.from_numpy(q).to(DEV), dev(stream), dev(pos), int(pos.max()), sel, n_sel, ws)
+    torch.cuda.synchronize()
+    o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
+    assert np.array_equal(n_sel.cpu().numpy(), o_nsel)
+    assert np.array_equal(sel.cpu().numpy(), o_sel), "selection differs from the oracle"
