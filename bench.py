@@ -576,8 +576,54 @@ def bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name, iters=30):
         f"{t_sel * 1e3:.1f} attend {seg[:, 2].mean() * 1e3:.1f} us; indexer {scan_bytes / (t_sel * 1e-3) / 1e9:.0f} GB/s; "
         f"graph replay {np.median(g_ms) * 1e3:.1f} us (p10 {np.percentile(g_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(g_ms, 90) * 1e3:.1f}; output {'identical' if graph_ok else 'DIFFERS'})")
+    # The same step as one msa_decode_step call (three kernels for a few
+    # queries over at most 64 blocks: the scan appends the rows, the
+    # attention ranks the blocks), eager and from a graph replay.
+    ws_step = wsbuf(dims, M.MSA_OP_DECODE_STEP, S, p)
+    out_sep = out.clone()
+
+    def run_step():
+        M.msa_decode_step(dims, cache, stream, pos, p, new_idx, new_k, new_v, idx_q, q, sel, n_sel, out, ws_step)
+
+    for _ in range(5):
+        run_step()
+    torch.cuda.synchronize()
+    s_ms = []
+    for _ in range(iters):
+        g0.record()
+        run_step()
+        g1.record()
+        torch.cuda.synchronize()
+        s_ms.append(g0.elapsed_time(g1))
+    s_ms = np.array(s_ms)
+    step_ok = bool(torch.equal(out, out_sep))
+    graph_s = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_s):
+        run_step()
+    for _ in range(5):
+        graph_s.replay()
+    torch.cuda.synchronize()
+    gs_ms = []
+    for _ in range(iters):
+        g0.record()
+        graph_s.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gs_ms.append(g0.elapsed_time(g1))
+    gs_ms = np.array(gs_ms)
+    step_ok = step_ok and bool(torch.equal(out, out_sep))
+    log(f"[bench] {name}: msa_decode_step {np.median(s_ms) * 1e3:.1f} us (p10 {np.percentile(s_ms, 10) * 1e3:.1f}), "
+        f"graph replay {np.median(gs_ms) * 1e3:.1f} us (p10 {np.percentile(gs_ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(gs_ms, 90) * 1e3:.1f}); output {'identical to the separate calls' if step_ok else 'DIFFERS'}")
     key = name.replace("decode_", "")
     return {
+        f"decode_{key}_step_call_us": {"eager_median": round(np.median(s_ms) * 1e3, 2),
+                                       "eager_p10": round(np.percentile(s_ms, 10) * 1e3, 2),
+                                       "graph_median": round(np.median(gs_ms) * 1e3, 2),
+                                       "graph_p10": round(np.percentile(gs_ms, 10) * 1e3, 2),
+                                       "graph_p90": round(np.percentile(gs_ms, 90) * 1e3, 2),
+                                       "output_identical": step_ok},
+        f"decode_{key}_step_call_graph_queries_s": round(S / (np.median(gs_ms) * 1e-3), 1) if step_ok else None,
         f"decode_{key}_queries_s": round(S / (step.mean() * 1e-3), 1),
         f"decode_{key}_graph_queries_s": round(S / (np.median(g_ms) * 1e-3), 1) if graph_ok else None,
         f"decode_{key}_us": {"step": round(step.mean() * 1e3, 2), "step_p10": round(np.percentile(step, 10) * 1e3, 2),

@@ -47,12 +47,14 @@ DSA_OP_SELECT = 5
 DSA_OP_ATTEND_DECODE = 6
 MSA_OP_BLOCK_SCORES_PREFILL = 7
 MSA_OP_INDEX_PROJECT = 8
+MSA_OP_DECODE_STEP = 9
 
 EXPORTS = (
     "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",
     "msa_topk_blocks", "msa_select", "msa_block_scores_prefill", "msa_select_prefill",
     "msa_attend_decode", "msa_attend_prefill", "dsa_index_append", "dsa_select",
     "dsa_select_heads", "dsa_attend_decode", "msa_index_project", "msa_select_static",
+    "msa_decode_step",
 )
 
 
@@ -129,6 +131,7 @@ def lib() -> ctypes.CDLL:
             "dsa_select_heads": [D, C, P, P, I32, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
             "msa_index_project": [D, C, ctypes.POINTER(Proj), P, P, P, I64, I32, P, P, ctypes.c_size_t, P],
             "dsa_attend_decode": [D, C, P, P, P, I64, I32, P, P, P, ctypes.c_size_t, P],
+            "msa_decode_step": [D, C, P, P, I64, I32, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -329,6 +332,19 @@ def msa_attend_decode(dims, cache, q, stream, pos, max_pos, sel, out, ws=None, h
                                    _p(stream, torch.int32), _p(pos, torch.int32), pos.numel(), max_pos,
                                    _p(sel, torch.int32), _p(out, torch.float32, "out"), wp, wn,
                                    _stream(hip_stream)), "msa_attend_decode")
+
+
+def msa_decode_step(dims, cache, stream, pos, max_pos, idx_k_new, k_new, v_new, idx_q, q, sel, n_sel, out, ws,
+                    hip_stream=None):
+    """msa_index_append + msa_select + msa_attend_decode of one decode step
+    (three kernels for few queries over short contexts)."""
+    wp, wn = _ws(ws)
+    _check(lib().msa_decode_step(ctypes.byref(dims), ctypes.byref(cache), _p(stream, torch.int32),
+                                 _p(pos, torch.int32), pos.numel(), max_pos,
+                                 _p(idx_k_new, torch.float32, "idx_k_new"), _p(k_new, torch.bfloat16, "k_new"),
+                                 _p(v_new, torch.bfloat16, "v_new"), _p(idx_q, torch.float32, "idx_q"),
+                                 _p(q, torch.bfloat16, "q"), _p(sel, torch.int32), _p(n_sel, torch.int32),
+                                 _p(out, torch.float32, "out"), wp, wn, _stream(hip_stream)), "msa_decode_step")
 
 
 def msa_attend_prefill(dims, cache, q, stream_id, pos0, sel, out, ws=None, hip_stream=None):

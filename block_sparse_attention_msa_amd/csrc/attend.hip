@@ -145,10 +145,48 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         n_valid_s = 0;
         row_s[kMaxSplitEntries] = own_row;
     }
+    // decode step: this (query, group)'s blocks ranked here from the scan's
+    // partial maxima (one wave; a block's rank is the number of larger keys,
+    // the keys of the block top-k: local block first, then the score, then
+    // the lower id), the winners in ascending id order
+    __shared__ uint64_t rkey_s[kRankedBlocks];
+    __shared__ int32_t ranked_s[kRankedBlocks];
+    const bool ranked = !kTokenIds && a.bs_part != nullptr;     // launch-uniform
+    if (ranked) {
+        const int loc = p / kBlock;
+        const int nvis = loc + 1;                   // <= nblk_part <= kRankedBlocks
+        const int k = min(a.sel_len, nvis);
+        uint64_t key = 0;
+        if (wave == 0) {
+            if (lane < nvis) {
+                const float* bp = a.bs_part + ((i * kGroups + g) * a.nblk_part + lane) * a.n_sub;
+                float sc = bp[0];
+                for (int e = 1; e < a.n_sub; ++e) sc = fmaxf(sc, bp[e]);
+                key = (static_cast<uint64_t>(ordered_key(sc)) << 31) | static_cast<uint64_t>(0x7fffffff - lane) |
+                      (lane == loc ? 1ull << 63 : 0ull);
+            }
+            rkey_s[lane] = key;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int rank = 0;
+            for (int c = 0; c < nvis; ++c) rank += rkey_s[c] > key;
+            const bool win = lane < nvis && rank < k;
+            const uint64_t wins = __builtin_amdgcn_ballot_w64(win);
+            if (win) ranked_s[__builtin_popcountll(wins & ((1ull << lane) - 1ull))] = lane;
+            for (int t = k + lane; t < a.sel_len; t += 64) ranked_s[t] = -1;
+        }
+        __syncthreads();
+        if (sp == 0) {
+            for (int t = threadIdx.x; t < a.sel_len; t += kAttThreads)
+                a.sel_out[(i * kGroups + g) * a.sel_len + t] = ranked_s[t];
+            if (threadIdx.x == 0) a.n_sel_out[i * kGroups + g] = k;
+        }
+    }
     __syncthreads();
     for (int e = e_begin + static_cast<int>(threadIdx.x); e < e_begin + (u_end - u_begin) * (kTokenIds ? kUnit : 1);
          e += kAttThreads) {
-        int id = e < e_end ? sel[e] : -1;
+        int id = e < e_end ? (ranked ? ranked_s[e] : sel[e]) : -1;
         if (kTokenIds ? (id > p) : (id > p / kBlock)) id = -1;
         sel_s[e - e_begin] = id;
         row_s[e - e_begin] = id < 0 ? own_row

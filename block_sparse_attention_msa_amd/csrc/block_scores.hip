@@ -230,6 +230,114 @@ __global__ __launch_bounds__(64 * kFineWaves) void block_scores_decode_fine_kern
     }
 }
 
+// Decode step, small problems: the fine scan of the step's queries, which
+// also appends the step's rows.  The new index keys are scored from the
+// inputs (a row this launch writes cannot be read back by it): the query's
+// own token, and any token of its stream that another query of the launch
+// appends (found by a ballot over the launch's (stream, position) pairs,
+// 64 per round; rows loaded from the cache for such a token are replaced).
+// The workgroup holding a query's own token writes its index, K and V rows,
+// which later kernels read.  The dot products, and with them the partial
+// maxima, are those of the fine scan, bit for bit.
+struct StepScanArgs {
+    float* idx_k;
+    uint16_t* k;
+    uint16_t* v;
+    Pager pg;
+    const float* idx_q;
+    const int32_t* stream;
+    const int32_t* pos;
+    int64_t n_q;
+    const float* idx_k_new;     // [n_q][kGroups][kIdxDim]
+    const uint16_t* k_new;      // [n_q][kGroups][kHeadDim] bf16, or NULL
+    const uint16_t* v_new;
+    float* bs_part;
+    int nblk;
+};
+
+__global__ __launch_bounds__(64 * kFineWaves) void decode_step_fine_kernel(StepScanArgs a) {
+    const int64_t i = blockIdx.x;
+    const int b = blockIdx.y;
+    const int sub = blockIdx.z;
+    const int p = a.pos[i];
+    const int s = a.stream[i];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    constexpr int kTokPerWg = kFineWaves * kFineTokPerWave;                // 16
+    const f32x4* new_row = reinterpret_cast<const f32x4*>(a.idx_k_new + i * kGroups * kIdxDim);
+    if (b == p / kBlock && sub == (p % kBlock) / kTokPerWg) {
+        const int64_t slot = a.pg.row(s, p);
+        if (tid < kGroups * kIdxDim / 4)   // 128 x 16 B
+            reinterpret_cast<u32x4*>(a.idx_k + slot * kGroups * kIdxDim)[tid] =
+                reinterpret_cast<const u32x4*>(new_row)[tid];
+        if (tid < kGroups * kHeadDim / 8) {   // 64 x 16 B each
+            if (a.k_new)
+                reinterpret_cast<u32x4*>(a.k + slot * kGroups * kHeadDim)[tid] =
+                    reinterpret_cast<const u32x4*>(a.k_new + i * kGroups * kHeadDim)[tid];
+            if (a.v_new)
+                reinterpret_cast<u32x4*>(a.v + slot * kGroups * kHeadDim)[tid] =
+                    reinterpret_cast<const u32x4*>(a.v_new + i * kGroups * kHeadDim)[tid];
+        }
+    }
+    float m = -INFINITY;
+    const int t_begin = (sub * kFineWaves + wave) * kFineTokPerWave;
+    const int t_end = min(t_begin + kFineTokPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+    if (t_begin < t_end) {
+        const f32x4* qrow = reinterpret_cast<const f32x4*>(a.idx_q + i * kGroups * kIdxDim);
+        const f32x4 q0 = qrow[g * 32 + c];
+        const f32x4 q1 = qrow[g * 32 + 16 + c];
+        const f32x4* rows = reinterpret_cast<const f32x4*>(
+            a.idx_k + a.pg.block_row_uniform(s, b) * (kGroups * kIdxDim)) + g * 32 + c;
+        f32x4 ka[kFineTokPerWave], kb[kFineTokPerWave];
+        int tok[kFineTokPerWave];
+#pragma unroll
+        for (int u = 0; u < kFineTokPerWave; ++u) {
+            tok[u] = b * kBlock + min(t_begin + u, t_end - 1);            // past the query: its last visible token again
+            const f32x4* src = tok[u] == p ? new_row + g * 32 + c : rows + (tok[u] - b * kBlock) * kRowF4;
+            ka[u] = __builtin_nontemporal_load(src);
+            kb[u] = __builtin_nontemporal_load(src + 16);
+        }
+        // tokens of this wave that other queries of the launch append
+        const int tok_lo = b * kBlock + t_begin, tok_hi = b * kBlock + t_end;   // [lo, hi)
+        for (int64_t j0 = 0; j0 < a.n_q; j0 += 64) {
+            const int64_t j = j0 + lane;
+            bool hit = false;
+            if (j < a.n_q && j != i && a.stream[j] == s) {
+                const int pj = a.pos[j];
+                hit = pj >= tok_lo && pj < tok_hi;
+            }
+            uint64_t mask = __builtin_amdgcn_ballot_w64(hit);
+            while (mask) {                                               // wave-uniform
+                const int64_t jj = j0 + __builtin_ctzll(mask);
+                mask &= mask - 1;
+                const int pj = a.pos[jj];
+                const f32x4* src = reinterpret_cast<const f32x4*>(a.idx_k_new + jj * kGroups * kIdxDim) + g * 32 + c;
+#pragma unroll
+                for (int u = 0; u < kFineTokPerWave; ++u) {
+                    if (tok[u] == pj) {
+                        ka[u] = src[0];
+                        kb[u] = src[16];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kFineTokPerWave; ++u) m = fmaxf(m, row16_sum(dot8(q0, q1, ka[u], kb[u])));
+    }
+    __shared__ float red[kFineWaves][kGroups];
+    if (c == 0) red[wave][g] = m;
+    __syncthreads();
+    if (tid < kGroups) {
+        float r = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < kFineWaves; ++w) r = fmaxf(r, red[w][tid]);
+        a.bs_part[((i * kGroups + tid) * a.nblk + b) * kFineSub + sub] = r;
+    }
+}
+
 }  // namespace
 
 bool scan_is_fine(int64_t n_q, int nblk) {
@@ -241,6 +349,16 @@ hipError_t launch_block_scores_decode_fine(const CacheView& c, const float* idx_
                                            hipStream_t s) {
     hipLaunchKernelGGL(block_scores_decode_fine_kernel, dim3(static_cast<unsigned>(n_q), nblk, kFineSub),
                        dim3(64 * kFineWaves), 0, s, c.idx_k, c.pg, idx_q, stream, pos, bs_part, nblk);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step_fine(float* idx_k, uint16_t* k, uint16_t* v, const Pager& pg, const float* idx_q,
+                                   const int32_t* stream, const int32_t* pos, int64_t n_q, int nblk,
+                                   const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
+                                   float* bs_part, hipStream_t s) {
+    StepScanArgs a{idx_k, k, v, pg, idx_q, stream, pos, n_q, idx_k_new, k_new, v_new, bs_part, nblk};
+    hipLaunchKernelGGL(decode_step_fine_kernel, dim3(static_cast<unsigned>(n_q), nblk, kFineSub),
+                       dim3(64 * kFineWaves), 0, s, a);
     return hipGetLastError();
 }
 

@@ -170,6 +170,13 @@ bool scan_is_fine(int64_t n_q, int nblk);
 hipError_t launch_block_scores_decode_fine(const CacheView& c, const float* idx_q, const int32_t* stream,
                                            const int32_t* pos, int64_t n_q, int nblk, float* bs_part,
                                            hipStream_t s);
+// Decode step, small problems (scan_is_fine): the fine scan, which also
+// writes each query's new index, K and V rows at (stream, pos) and scores
+// the step's new keys from idx_k_new (k_new, v_new may be NULL).
+hipError_t launch_decode_step_fine(float* idx_k, uint16_t* k, uint16_t* v, const Pager& pg, const float* idx_q,
+                                   const int32_t* stream, const int32_t* pos, int64_t n_q, int nblk,
+                                   const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
+                                   float* bs_part, hipStream_t s);
 
 // ws: prefill_scores_ws_bytes(pos0 + n_q - 1) bytes (the split keys).
 size_t prefill_scores_ws_bytes(int32_t max_pos);
@@ -209,7 +216,18 @@ struct AttendArgs {
     const float* v_scale;
     int32_t stream0;         // stream == NULL: query i is at (stream0, pos0 + i) (a prefill chunk)
     int32_t pos0;
+    // Decode step (MSA blocks, at most kRankedBlocks of them): the selection
+    // is ranked by the kernel from the scan's partial maxima
+    // bs_part[query][group][nblk_part][n_sub], as launch_topk_blocks ranks
+    // them, instead of read from `sel`; the workgroups of split 0 write it
+    // to sel_out [query][group][sel_len] and its size to n_sel_out.
+    const float* bs_part = nullptr;
+    int nblk_part = 0;
+    int n_sub = 1;
+    int32_t* sel_out = nullptr;
+    int32_t* n_sel_out = nullptr;
 };
+constexpr int kRankedBlocks = 64;
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);

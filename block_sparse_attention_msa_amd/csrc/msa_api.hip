@@ -83,6 +83,19 @@ size_t select_ws(int64_t n_q, int32_t max_pos) {
     return align256(static_cast<size_t>(n_q) * kGroups * nblk * per * sizeof(float));
 }
 
+// msa_decode_step: the block scores, then the attention partials.
+size_t decode_step_ws(const msa_dims* dims, int64_t n_q, int32_t max_pos) {
+    return select_ws(n_q, max_pos) + align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
+}
+
+// msa_decode_step in three kernels: few queries over at most 64 blocks (the
+// attention kernel ranks them), the f32 index cache and bf16 K/V.
+bool decode_step_fused(const msa_cache* c, int64_t n_q, int32_t max_pos) {
+    const int nblk = nblk_of(max_pos);
+    return c->idx_k && !c->idx_k_f16 && c->kv_format == 0 && nblk <= msa::kRankedBlocks &&
+           msa::scan_is_fine(n_q, nblk);
+}
+
 // msa_select_prefill: block scores, then the split keys of the scorer.
 size_t select_prefill_ws(int64_t n_q, int32_t max_pos) {
     return select_ws(n_q, max_pos) + align256(msa::prefill_scores_ws_bytes(max_pos));
@@ -219,7 +232,7 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
     const bool dsa = op == DSA_OP_SELECT || op == DSA_OP_ATTEND_DECODE ||
                      (op == MSA_OP_ATTEND_DECODE && dims && dims->block == 1);
     if (check_dims(dims, dsa ? Mode::Dsa : Mode::Msa) != MSA_OK) return bad;
-    if (op < MSA_OP_SELECT || op > MSA_OP_INDEX_PROJECT) return bad;
+    if (op < MSA_OP_SELECT || op > MSA_OP_DECODE_STEP) return bad;
     if (n_q == 0) return 0;   // an empty call launches nothing and needs no workspace
     switch (op) {
         case MSA_OP_SELECT:
@@ -240,6 +253,9 @@ size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t
             return align256(msa::attend_ws_bytes(n_q, dims->top_k, 1));
         case MSA_OP_INDEX_PROJECT:
             return align256(msa::project_ws_bytes(n_q));
+        case MSA_OP_DECODE_STEP:
+            if (nblk_of(max_pos) > msa::kMaxBlocks) return bad;
+            return decode_step_ws(dims, n_q, max_pos);
     }
     return bad;
 }
@@ -395,6 +411,49 @@ msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cache, const
                       dims->top_k, dims->top_k, kBlock, dims->scale, d_out, d_ws,
                       cache->kv_format, cache->k_scale, cache->v_scale};
     return hip_status(msa::launch_attend(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
+                           const int32_t* d_pos, int64_t n_q, int32_t max_pos, const float* d_idx_k_new,
+                           const uint16_t* d_k_new, const uint16_t* d_v_new, const float* d_idx_q,
+                           const uint16_t* d_q, int32_t* d_sel, int32_t* d_n_sel, float* d_out, void* d_ws,
+                           size_t ws_bytes, void* hip_stream) {
+    MSA_TRY(check_dims(dims, Mode::Msa));
+    MSA_TRY(check_cache(cache));
+    MSA_TRY(check_count_pos(n_q, max_pos, cache));
+    if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
+    MSA_TRY(check_index_cache(cache));
+    MSA_TRY(check_ptrs({d_stream, d_pos, d_idx_k_new, d_idx_q, d_q, d_sel, d_n_sel, d_out, d_ws, cache->k, cache->v}));
+    if (d_k_new) MSA_TRY(check_ptrs({d_k_new}));
+    if (d_v_new) MSA_TRY(check_ptrs({d_v_new}));
+    if (nblk_of(max_pos) > msa::kMaxBlocks) return MSA_ERR_UNSUPPORTED;
+    const size_t sel_bytes = select_ws(n_q, max_pos);
+    const size_t att_bytes = align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
+    if (ws_bytes < decode_step_ws(dims, n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
+    char* att_ws = static_cast<char*>(d_ws) + sel_bytes;
+    if (!decode_step_fused(cache, n_q, max_pos)) {
+        MSA_TRY(msa_index_append(dims, cache, d_stream, d_pos, n_q, max_pos, d_idx_k_new, d_k_new, d_v_new,
+                                 hip_stream));
+        MSA_TRY(msa_select(dims, cache, d_idx_q, d_stream, d_pos, n_q, max_pos, d_sel, d_n_sel, d_ws, sel_bytes,
+                           hip_stream));
+        return msa_attend_decode(dims, cache, d_q, d_stream, d_pos, n_q, max_pos, d_sel, d_out, att_ws, att_bytes,
+                                 hip_stream);
+    }
+    const hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const int nblk = nblk_of(max_pos);
+    float* bs_part = static_cast<float*>(d_ws);
+    MSA_TRY(hip_status(msa::launch_decode_step_fine(cache->idx_k, cache->k, cache->v, view(cache).pg, d_idx_q,
+                                                    d_stream, d_pos, n_q, nblk, d_idx_k_new, d_k_new, d_v_new,
+                                                    bs_part, s)));
+    msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q, d_stream, d_pos, n_q, d_sel,
+                      dims->top_k, dims->top_k, kBlock, dims->scale, d_out, att_ws,
+                      0, nullptr, nullptr};
+    a.bs_part = bs_part;
+    a.nblk_part = nblk;
+    a.n_sub = msa::kFineSub;
+    a.sel_out = d_sel;
+    a.n_sel_out = d_n_sel;
+    return hip_status(msa::launch_attend(a, s));
 }
 
 msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, const uint16_t* d_q,

@@ -150,7 +150,8 @@ typedef enum msa_op {
     DSA_OP_SELECT = 5,          /* dsa_select */
     DSA_OP_ATTEND_DECODE = 6,   /* dsa_attend_decode */
     MSA_OP_BLOCK_SCORES_PREFILL = 7,  /* msa_block_scores_prefill */
-    MSA_OP_INDEX_PROJECT = 8          /* msa_index_project (n_q = tokens) */
+    MSA_OP_INDEX_PROJECT = 8,         /* msa_index_project (n_q = tokens) */
+    MSA_OP_DECODE_STEP = 9            /* msa_decode_step */
 } msa_op;
 
 /* Bytes of workspace `op` needs for n_q queries whose positions are all
@@ -327,6 +328,29 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
                              const int32_t* d_stream, const int32_t* d_pos, int64_t n_q,
                              int32_t max_pos, const int32_t* d_sel, float* d_out,
                              void* d_ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * One decode step ([MSA-PR] Implementation, decode path: the new token's
+ * index key is written before the same step's query scores the cache):
+ * msa_index_append of d_idx_k_new / d_k_new / d_v_new at (d_stream[i],
+ * d_pos[i]), then msa_select and msa_attend_decode of the queries at those
+ * same slots, with the same outputs bit for bit (cache rows, d_sel [n_q]
+ * [n_group][top_k], d_n_sel, d_out).  d_k_new and d_v_new may be NULL (that
+ * cache is not written); d_idx_k_new is required.  For few queries over
+ * short contexts (at most 64 blocks, an f32 index cache, bf16 K/V, and a
+ * scan of fewer than 256 workgroups) it runs three kernels instead of five:
+ * the scan writes the rows and scores the new keys from d_idx_k_new, the
+ * attention ranks each (query, group)'s blocks itself, then the split
+ * combine; any other shape runs the separate calls' kernels.
+ * Device preconditions: those of the three calls ((stream, pos) pairs
+ * distinct, d_pos[i] <= max_pos).  Workspace: MSA_OP_DECODE_STEP, the
+ * block scores followed by the attention partials (each 256-byte aligned).
+ */
+MSA_API msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
+                           const int32_t* d_pos, int64_t n_q, int32_t max_pos, const float* d_idx_k_new,
+                           const uint16_t* d_k_new, const uint16_t* d_v_new, const float* d_idx_q,
+                           const uint16_t* d_q, int32_t* d_sel, int32_t* d_n_sel, float* d_out, void* d_ws,
+                           size_t ws_bytes, void* hip_stream);
 
 /*
  * Prefill form of msa_attend_decode ([MSA-PR] Implementation, batch path:

@@ -295,7 +295,7 @@ def test_workspace_of_an_empty_call_is_zero(L):
     pairs on the host)."""
     d, dd = M.msa_dims(), M.dsa_dims()
     msa_ops = (M.MSA_OP_SELECT, M.MSA_OP_SELECT_PREFILL, M.MSA_OP_ATTEND_DECODE, M.MSA_OP_ATTEND_PREFILL,
-               M.MSA_OP_BLOCK_SCORES_PREFILL, M.MSA_OP_INDEX_PROJECT)
+               M.MSA_OP_BLOCK_SCORES_PREFILL, M.MSA_OP_INDEX_PROJECT, M.MSA_OP_DECODE_STEP)
     for op in msa_ops:
         for max_pos in (0, 127, 32767):
             assert M.workspace_bytes(d, op, 0, max_pos) == 0, (op, max_pos)
@@ -338,3 +338,31 @@ def test_select_static_limits(L):
     assert call(1, 4095, idx_q=MIS) == ALIGN
     assert call(0, 4095) == OK
     assert call(1, 1 << 20) == RANGE
+
+
+def test_decode_step_validation_and_workspace(L):
+    """msa_decode_step: the block scores of msa_select followed by the
+    attention partials of msa_attend_decode (each 256-byte aligned); the
+    index keys to append are required, K/V rows optional; the usual checks
+    run before any launch."""
+    d = M.msa_dims()
+    up = lambda x: -(-x // 256) * 256
+    for n_q, max_pos in ((1, 4095), (5, 2999), (32, 32767), (20, 8191), (100, 127)):
+        sel_ws = M.workspace_bytes(d, M.MSA_OP_SELECT, n_q, max_pos)
+        att_ws = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, n_q, max_pos)
+        assert M.workspace_bytes(d, M.MSA_OP_DECODE_STEP, n_q, max_pos) == sel_ws + up(att_ws)
+    c = _cache(dsa=None)
+    need = M.workspace_bytes(d, M.MSA_OP_DECODE_STEP, 1, 4095)
+
+    def step(idx_new=A, k_new=A, v_new=A, n=1, max_pos=4095, ws=A, nb=need, cache=c):
+        return L.msa_decode_step(ctypes.byref(d), ctypes.byref(cache), A, A, n, max_pos, idx_new, k_new, v_new,
+                                 A, A, A, A, A, ws, nb, None)
+    assert step(n=0) == OK
+    assert step(idx_new=None) == NULL
+    assert step(k_new=MIS) == ALIGN
+    assert step(ws=None) == NULL
+    assert step(nb=need - 1) == WS
+    assert step(max_pos=4096) == RANGE
+    assert step(n=-1) == SHAPE
+    assert step(cache=_cache(idx=None, dsa=None)) == NULL        # no index cache
+    assert step(k_new=None, v_new=None) not in (NULL, ALIGN, SHAPE, UNSUP, WS)   # accepted (no GPU here)

@@ -1,0 +1,132 @@
+"""GPU tests of msa_decode_step (append, selection and attention of one
+decode step in one call), through the C ABI.
+
+Its outputs -- the appended cache rows, the selection, its sizes and the
+attention output -- must equal those of msa_index_append + msa_select +
+msa_attend_decode bit for bit: on the three-kernel form (few queries over
+at most 64 blocks, f32 index cache, bf16 K/V: the scan appends the rows and
+scores the new keys from the inputs, the attention ranks the blocks itself,
+then the split combine) and on the separate-kernel form the other shapes
+take.  The integer workload
+is also held to the oracle (selection bit-exact, attention to the attention
+tolerances), and queries of one stream at neighbouring positions score each
+other's new keys.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_msa_amd as M
+import oracle
+import workloads as W
+from _gpu_common import DEV, check_attention, dev, dev_bits, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _both_forms(wl: W.Workload, paged: bool = False):
+    """Runs the step both ways on identical caches (the step's own rows
+    zeroed first, so both must write them); returns the step's outputs."""
+    host, qs = W.caches(wl), W.queries(wl)
+    dims = M.msa_dims(wl.top_k, W.SCALE)
+    st, ps = qs["stream"].astype(np.int64), qs["pos"].astype(np.int64)
+    assert len(set(zip(st.tolist(), ps.tolist()))) == wl.n_q, "the step's (stream, pos) pairs must be distinct"
+    new_idx = dev(host["idx_k"][st, ps])
+    new_k = dev_bits(host["k"][st, ps], torch.bfloat16)
+    new_v = dev_bits(host["v"][st, ps], torch.bfloat16)
+    q, idx_q = dev_bits(qs["q"], torch.bfloat16), dev(qs["idx_q"])
+    stream, pos = dev(qs["stream"]), dev(qs["pos"])
+    S, cap = wl.n_stream, wl.cap
+    nb = (cap + 127) // 128
+    table = np.random.default_rng(11).permutation(S * nb + 3)[: S * nb].astype(np.int32).reshape(S, nb)
+    results = []
+    for fused in (False, True):
+        idx_k = dev(host["idx_k"])
+        k = dev_bits(host["k"], torch.bfloat16)
+        v = dev_bits(host["v"], torch.bfloat16)
+        ti, tp = torch.from_numpy(st), torch.from_numpy(ps)
+        idx_k[ti, tp] = 0
+        k[ti, tp] = 0
+        v[ti, tp] = 0
+        if paged:
+            # the same rows placed in pages by a seeded table
+            n_pages = S * nb + 3
+            pk = torch.zeros((n_pages * 128, 4, 128), dtype=torch.bfloat16, device=DEV)
+            pv, pi = torch.zeros_like(pk), torch.zeros((n_pages * 128, 4, 128), dtype=torch.float32, device=DEV)
+            for s in range(S):
+                for b in range(nb):
+                    r0, r1 = b * 128, min(cap, b * 128 + 128)
+                    d0 = int(table[s, b]) * 128
+                    pk[d0:d0 + r1 - r0] = k[s, r0:r1]
+                    pv[d0:d0 + r1 - r0] = v[s, r0:r1]
+                    pi[d0:d0 + r1 - r0] = idx_k[s, r0:r1]
+            k, v, idx_k = pk, pv, pi
+            cache = M.make_cache(k=k, v=v, idx_k=idx_k, block_table=dev(table), cap=cap)
+        else:
+            cache = M.make_cache(k=k, v=v, idx_k=idx_k)
+        sel = torch.full((wl.n_q, 4, wl.top_k), -7, dtype=torch.int32, device=DEV)
+        n_sel = torch.full((wl.n_q, 4), -7, dtype=torch.int32, device=DEV)
+        out = torch.zeros((wl.n_q, 64, 128), dtype=torch.float32, device=DEV)
+        if fused:
+            ws = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_DECODE_STEP, wl.n_q, wl.max_pos), 256),
+                             dtype=torch.uint8, device=DEV)
+            M.msa_decode_step(dims, cache, stream, pos, wl.max_pos, new_idx, new_k, new_v, idx_q, q, sel, n_sel,
+                              out, ws)
+        else:
+            M.msa_index_append(dims, cache, stream, pos, wl.max_pos, idx_k_new=new_idx, k_new=new_k, v_new=new_v)
+            ws_s = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_SELECT, wl.n_q, wl.max_pos), 256),
+                               dtype=torch.uint8, device=DEV)
+            M.msa_select(dims, cache, idx_q, stream, pos, wl.max_pos, sel, n_sel, ws_s)
+            ws_a = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_ATTEND_DECODE, wl.n_q, wl.max_pos), 256),
+                               dtype=torch.uint8, device=DEV)
+            M.msa_attend_decode(dims, cache, q, stream, pos, wl.max_pos, sel, out, ws_a)
+        torch.cuda.synchronize()
+        results.append({"idx_k": idx_k.cpu(), "k": k.view(torch.int16).cpu(), "v": v.view(torch.int16).cpu(),
+                        "sel": sel.cpu(), "n_sel": n_sel.cpu(), "out": out.cpu()})
+    for name in results[0]:
+        assert torch.equal(results[0][name], results[1][name]), f"{name}: the step differs from the separate calls"
+    assert torch.isfinite(results[1]["out"]).all()
+    return results[1], host, qs
+
+
+# Shapes: the rule for the three-kernel form is nblk <= 64 and
+# n_q * ceil(nblk / 2) < 256 (and an f32 index cache with bf16 K/V).
+CASES = [
+    # (name, n_stream, cap, streams, positions, top_k)
+    ("one_query_4k", 1, 4096, (0,), (4095,), 16),
+    ("ragged_5", 5, 3000, (0, 1, 2, 3, 4), (2999, 0, 127, 128, 1500), 16),
+    ("one_stream_neighbours", 2, 3000, (0, 0, 0, 1, 0), (1000, 1001, 1130, 500, 1127), 16),
+    ("short_top64", 3, 8192, (0, 1, 2), (200, 8191, 4000), 64),
+    ("top1", 2, 2048, (0, 1), (2047, 300), 1),
+    ("separate_kernels_20x8k", 20, 8192, tuple(range(20)), tuple(8191 - 37 * j for j in range(20)), 16),
+    ("separate_kernels_long", 2, 20000, (0, 1), (19999, 9000), 16),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_decode_step_equals_separate_calls(case):
+    name, S, cap, streams, positions, top_k = case
+    wl = W.Workload(f"step_{name}", "msa_decode", S, cap, streams, positions, top_k=top_k)
+    log(f"[decode step] {name}: n_q={wl.n_q} max_pos={wl.max_pos} top_k={top_k}")
+    _both_forms(wl)
+
+
+def test_decode_step_paged():
+    wl = W.Workload("step_paged", "msa_decode", 3, 3000, (0, 1, 2, 1), (2999, 1500, 130, 1501), top_k=16)
+    log("[decode step] paged cache")
+    _both_forms(wl, paged=True)
+
+
+def test_decode_step_integer_workload_against_oracle():
+    """The 1 x 4K integer-indexer decode: the step's selection equals the
+    oracle's bit for bit, its attention is within the attention tolerances."""
+    wl = W.CONFIGS["decode_1x4k_int"]
+    log(f"[decode step] {wl.name} against the oracle")
+    res, host, qs = _both_forms(wl)
+    _, o_sel, o_nsel = oracle.msa_select(host["idx_k"], qs["stream"], qs["pos"], qs["idx_q"], top_k=wl.top_k)
+    assert np.array_equal(res["sel"].numpy(), o_sel)
+    assert np.array_equal(res["n_sel"].numpy(), o_nsel)
+    o_out = oracle.sparse_attend(host["k"], host["v"], qs["stream"], qs["pos"], qs["q"], o_sel, unit=128,
+                                 scale=W.SCALE)
+    wa, wr = check_attention(res["out"].numpy(), o_out)
+    log(f"  attention max-abs {wa:.3e}, rel-L2 {wr:.3e}")
