@@ -200,7 +200,43 @@ def main():
     graph_ok = bool(torch.equal(out, out_eager))
     log(f"[bench] decode step eager {ms_eager * 1e3:.1f} us, graph replay {ms_graph * 1e3:.1f} us "
         f"(replay output {'identical' if graph_ok else 'DIFFERS'})")
-    ms_per_step = min(ms_eager, ms_graph) if graph_ok else ms_eager
+    # The same step as one msa_decode_step call (the scan appends the rows,
+    # the attention ranks each (query, group)'s blocks: three kernels
+    # instead of five), eager and from a graph replay; its outputs must equal
+    # the separate calls'.
+    ws_step = wsbuf(dims, M.MSA_OP_DECODE_STEP, S, p)
+    out_sep, sel_sep = out.clone(), sel.clone()
+
+    def step_call():
+        M.msa_decode_step(dims, cache, stream, pos, p, new_idx, new_k, new_v, idx_q, q, sel, n_sel, out, ws_step)
+
+    for _ in range(args.warmup):
+        step_call()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step_call()
+    torch.cuda.synchronize()
+    ms_call = (time.perf_counter() - t_start) * 1e3 / args.steps
+    call_ok = bool(torch.equal(out, out_sep) and torch.equal(sel, sel_sep))
+    graph_c = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_c):
+        step_call()
+    for _ in range(args.warmup):
+        graph_c.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        graph_c.replay()
+    torch.cuda.synchronize()
+    ms_call_graph = (time.perf_counter() - t_start) * 1e3 / args.steps
+    call_ok = call_ok and bool(torch.equal(out, out_sep) and torch.equal(sel, sel_sep))
+    log(f"[bench] decode step as msa_decode_step: eager {ms_call * 1e3:.1f} us, graph replay "
+        f"{ms_call_graph * 1e3:.1f} us (output {'identical to the separate calls' if call_ok else 'DIFFERS'})")
+    forms = [(ms_eager, "separate calls"), (ms_graph if graph_ok else 1e9, "separate calls, graph replay")]
+    if call_ok:
+        forms += [(ms_call, "msa_decode_step"), (ms_call_graph, "msa_decode_step, graph replay")]
+    ms_per_step, step_form = min(forms)
     value = S / (ms_per_step / 1e3)
     scan_bytes = S * (p + 1) * 4 * 128 * 4 + S * 4 * 128 * 4 + S * 4 * nblk * 4
     att_bytes = S * 4 * 16 * 128 * 128 * 2 * 2 + S * 64 * 128 * 2 + S * 64 * 128 * 4 + S * 4 * 16 * 4
@@ -280,6 +316,9 @@ def main():
     log(f"[bench] device copy {copy_gbps:.0f} GB/s (read + write)")
     extra = {
         "decode_step_us": {"eager": round(ms_eager * 1e3, 2), "hip_graph": round(ms_graph * 1e3, 2),
+                           "msa_decode_step": round(ms_call * 1e3, 2),
+                           "msa_decode_step_graph": round(ms_call_graph * 1e3, 2),
+                           "msa_decode_step_identical": call_ok,
                            "graph_replay_matches_eager": graph_ok},
         "device_copy_GBps": round(copy_gbps, 1),
         "decode_us": {"append": round(t_append * 1e3, 2), "indexer_scan": round(t_scan * 1e3, 2),
@@ -355,7 +394,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "decode_32x32k", "streams": S, "ctx": cap, "query_pos": p,
+        "config": {"workload": "decode_32x32k", "step": step_form, "streams": S, "ctx": cap, "query_pos": p,
                    "groups": 4, "q_heads": 64, "kv_heads": 4, "head_dim": 128, "idx_dim": 128,
                    "block": 128, "top_k": 16, "kv_dtype": "bf16", "index_cache_dtype": "f32"},
         "roofline": {"bound": "hbm", "kernel": "block_scores_decode_kernel",

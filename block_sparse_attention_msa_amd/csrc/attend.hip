@@ -33,6 +33,7 @@
 //    operand per 32-dim block of the output, so the only rounding is that of
 //    the scaled probabilities, as in the bf16 path.
 #include "common.hpp"
+#include "topk_regs.hpp"
 
 namespace msa {
 namespace {
@@ -146,41 +147,67 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         row_s[kMaxSplitEntries] = own_row;
     }
     // decode step: this (query, group)'s blocks ranked here from the scan's
-    // partial maxima (one wave; a block's rank is the number of larger keys,
-    // the keys of the block top-k: local block first, then the score, then
-    // the lower id), the winners in ascending id order
-    __shared__ uint64_t rkey_s[kRankedBlocks];
-    __shared__ int32_t ranked_s[kRankedBlocks];
-    const bool ranked = !kTokenIds && a.bs_part != nullptr;     // launch-uniform
-    if (ranked) {
-        const int loc = p / kBlock;
-        const int nvis = loc + 1;                   // <= nblk_part <= kRankedBlocks
-        const int k = min(a.sel_len, nvis);
-        uint64_t key = 0;
-        if (wave == 0) {
-            if (lane < nvis) {
-                const float* bp = a.bs_part + ((i * kGroups + g) * a.nblk_part + lane) * a.n_sub;
-                float sc = bp[0];
-                for (int e = 1; e < a.n_sub; ++e) sc = fmaxf(sc, bp[e]);
-                key = (static_cast<uint64_t>(ordered_key(sc)) << 31) | static_cast<uint64_t>(0x7fffffff - lane) |
-                      (lane == loc ? 1ull << 63 : 0ull);
+    // block scores (or a fine scan's partial maxima) by one wave, with the
+    // keys of the block top-k (local block first, then the score, then the
+    // lower id): up to 64 candidates by rank (the number of larger keys),
+    // more by the top-k's register rounds; the winners in ascending id order
+    constexpr int kRankDirect = 64;
+    __shared__ uint64_t rkey_s[kRankDirect];
+    __shared__ int32_t ranked_s[kMaxTopkBlocks];
+    __shared__ int32_t chosen_s[kMaxTopkBlocks];
+    const bool ranked = !kTokenIds && kQ == 0 && a.bs_part != nullptr;     // launch-uniform
+    if constexpr (!kTokenIds && kQ == 0) {
+        if (ranked) {
+            const int loc = p / kBlock;
+            const int nvis = loc + 1;                   // <= nblk_part <= kRankedBlocks
+            const int k = min(a.sel_len, nvis);
+            const float* row = a.bs_part + (i * kGroups + g) * a.nblk_part * a.n_sub;
+            if (nvis <= kRankDirect) {
+                uint64_t key = 0;
+                if (wave == 0) {
+                    if (lane < nvis) {
+                        const float* bp = row + lane * a.n_sub;
+                        float sc = bp[0];
+                        for (int e = 1; e < a.n_sub; ++e) sc = fmaxf(sc, bp[e]);
+                        key = (static_cast<uint64_t>(ordered_key(sc)) << 31) |
+                              static_cast<uint64_t>(0x7fffffff - lane) | (lane == loc ? 1ull << 63 : 0ull);
+                    }
+                    rkey_s[lane] = key;
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    int rank = 0;
+                    for (int c = 0; c < nvis; ++c) rank += rkey_s[c] > key;
+                    const bool win = lane < nvis && rank < k;
+                    const uint64_t wins = __builtin_amdgcn_ballot_w64(win);
+                    if (win) ranked_s[__builtin_popcountll(wins & ((1ull << lane) - 1ull))] = lane;
+                    for (int t = k + lane; t < a.sel_len; t += 64) ranked_s[t] = -1;
+                }
+            } else {
+                if (wave == 0) {
+                    auto rank_regs = [&](auto per) __attribute__((always_inline)) {
+                        constexpr int kPer = decltype(per)::value;
+                        float pre[kPer];
+#pragma unroll
+                        for (int j = 0; j < kPer; ++j) {
+                            const int b = lane + 64 * j;
+                            pre[j] = row[(b < a.nblk_part ? b : 0) * a.n_sub];
+                        }
+                        topk_in_registers<kPer, (kPer > 8)>(row, pre, a.n_sub, nvis, loc, k, lane, chosen_s);
+                    };
+                    if (nvis <= 256) rank_regs(std::integral_constant<int, 4>{});
+                    else if (nvis <= 512) rank_regs(std::integral_constant<int, 8>{});
+                    else rank_regs(std::integral_constant<int, 16>{});   // one score per block (coarse scan)
+                }
+                __syncthreads();
+                if (wave == 0) write_ascending(chosen_s, k, a.sel_len, lane, ranked_s);
             }
-            rkey_s[lane] = key;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            int rank = 0;
-            for (int c = 0; c < nvis; ++c) rank += rkey_s[c] > key;
-            const bool win = lane < nvis && rank < k;
-            const uint64_t wins = __builtin_amdgcn_ballot_w64(win);
-            if (win) ranked_s[__builtin_popcountll(wins & ((1ull << lane) - 1ull))] = lane;
-            for (int t = k + lane; t < a.sel_len; t += 64) ranked_s[t] = -1;
-        }
-        __syncthreads();
-        if (sp == 0) {
-            for (int t = threadIdx.x; t < a.sel_len; t += kAttThreads)
-                a.sel_out[(i * kGroups + g) * a.sel_len + t] = ranked_s[t];
-            if (threadIdx.x == 0) a.n_sel_out[i * kGroups + g] = k;
+            __syncthreads();
+            if (sp == 0) {
+                for (int t = threadIdx.x; t < a.sel_len; t += kAttThreads)
+                    a.sel_out[(i * kGroups + g) * a.sel_len + t] = ranked_s[t];
+                if (threadIdx.x == 0) a.n_sel_out[i * kGroups + g] = k;
+            }
         }
     }
     __syncthreads();

@@ -44,13 +44,30 @@ __device__ __forceinline__ float dot8(const f32x4& q0, const f32x4& q1, const f3
     return d;
 }
 
+// Decode step (kStep): the scan also appends the step's rows, as the fine
+// scan of small problems does (decode_step_fine_kernel): the workgroup
+// holding a query's own block writes its index, K and V rows, and the new
+// keys are scored from the inputs -- the query's own token after the loop,
+// and (rare: several queries of one stream) a wave whose tokens hold another
+// query's new row scores its tokens one by one from wherever each lives.
+struct StepRows {
+    float* idx_k;               // the cache the rows go to
+    uint16_t* k;
+    uint16_t* v;
+    int64_t n_q;
+    const float* idx_k_new;     // [n_q][kGroups][kIdxDim]
+    const uint16_t* k_new;      // [n_q][kGroups][kHeadDim] bf16, or NULL
+    const uint16_t* v_new;
+};
+
 // One workgroup per (query, pair of key blocks); four waves per block, 32
 // tokens each.  Index keys are read once with non-temporal 128-bit loads
 // (they are streamed, never re-read), 16 KiB per wave in flight.
+template <bool kStep>
 __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
     const float* __restrict__ idx_k, Pager pg, const float* __restrict__ idx_q,
     const int32_t* __restrict__ q_stream, const int32_t* __restrict__ q_pos,
-    float* __restrict__ bs, int64_t nblk_stride, int nblk) {
+    float* __restrict__ bs, int64_t nblk_stride, int nblk, StepRows st) {
     const int64_t i = blockIdx.x;
     const int b0 = blockIdx.y * kScanBlocksPerWg;
     const int p = q_pos[i];
@@ -60,6 +77,23 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
     const int g = lane >> 4;     // the DPP row of this lane = its group
     const int c = lane & 15;     // lane's 16-byte column within the group's first/second half
     const int b = b0 + wave / kScanWavesPerBlock;   // this wave's key block
+    if constexpr (kStep) {
+        if (loc >= b0 && loc < b0 + kScanBlocksPerWg) {      // this workgroup holds the query's own token
+            const int tid = threadIdx.x;
+            const int64_t slot = pg.row(q_stream[i], p);
+            if (tid < kGroups * kIdxDim / 4)
+                reinterpret_cast<u32x4*>(st.idx_k + slot * kGroups * kIdxDim)[tid] =
+                    reinterpret_cast<const u32x4*>(st.idx_k_new + i * kGroups * kIdxDim)[tid];
+            if (tid < kGroups * kHeadDim / 8) {
+                if (st.k_new)
+                    reinterpret_cast<u32x4*>(st.k + slot * kGroups * kHeadDim)[tid] =
+                        reinterpret_cast<const u32x4*>(st.k_new + i * kGroups * kHeadDim)[tid];
+                if (st.v_new)
+                    reinterpret_cast<u32x4*>(st.v + slot * kGroups * kHeadDim)[tid] =
+                        reinterpret_cast<const u32x4*>(st.v_new + i * kGroups * kHeadDim)[tid];
+            }
+        }
+    }
     float m = -INFINITY;
     if (b < nblk && b <= loc) {
         const f32x4* qrow = reinterpret_cast<const f32x4*>(idx_q + i * kGroups * kIdxDim);
@@ -68,7 +102,42 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
         const f32x4* rows = reinterpret_cast<const f32x4*>(
             idx_k + pg.block_row_uniform(q_stream[i], b) * (kGroups * kIdxDim)) + g * 32 + c;
         const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
-        const int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+        int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+        bool own = false;             // step: this wave holds the query's own token (its last)
+        bool other = false;           // step: ... or another query's new row
+        if constexpr (kStep) {
+            own = t_begin < t_end && b * kBlock + t_end - 1 == p;
+            const int s = q_stream[i];
+            for (int64_t j0 = 0; j0 < st.n_q; j0 += 64) {
+                const int64_t j = j0 + lane;
+                bool hit = false;
+                if (j < st.n_q && j != i && q_stream[j] == s) {
+                    const int pj = q_pos[j] - b * kBlock;
+                    hit = pj >= t_begin && pj < t_end;
+                }
+                other = other || __builtin_amdgcn_ballot_w64(hit) != 0;
+            }
+            if (other) {
+                // token by token: the row of the query that appends it, if any
+                for (int t = t_begin; t < t_end; ++t) {
+                    const int tok = b * kBlock + t;
+                    int64_t src_q = tok == p ? i : -1;
+                    for (int64_t j0 = 0; j0 < st.n_q && src_q < 0; j0 += 64) {
+                        const int64_t j = j0 + lane;
+                        const bool hit = j < st.n_q && q_stream[j] == s && q_pos[j] == tok;
+                        const uint64_t mk = __builtin_amdgcn_ballot_w64(hit);
+                        if (mk) src_q = j0 + __builtin_ctzll(mk);
+                    }
+                    const f32x4* src = src_q >= 0
+                                           ? reinterpret_cast<const f32x4*>(st.idx_k_new + src_q * kGroups * kIdxDim) + g * 32 + c
+                                           : rows + t * kRowF4;
+                    m = fmaxf(m, row16_sum(dot8(q0, q1, src[0], src[16])));
+                }
+                t_end = t_begin;      // done
+            } else if (own) {
+                --t_end;              // the own token is scored from the input below
+            }
+        }
         int t = t_begin;
         for (; t + kScanUnroll <= t_end; t += kScanUnroll) {
             f32x4 a[kScanUnroll], bb[kScanUnroll];
@@ -84,6 +153,10 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
             const f32x4 a = rows[t * kRowF4];
             const f32x4 bb = rows[t * kRowF4 + 16];
             m = fmaxf(m, row16_sum(dot8(q0, q1, a, bb)));
+        }
+        if (kStep && own && !other) {
+            const f32x4* src = reinterpret_cast<const f32x4*>(st.idx_k_new + i * kGroups * kIdxDim) + g * 32 + c;
+            m = fmaxf(m, row16_sum(dot8(q0, q1, src[0], src[16])));
         }
     }
     __shared__ float red[kScanWaves][kGroups];
@@ -362,6 +435,17 @@ hipError_t launch_decode_step_fine(float* idx_k, uint16_t* k, uint16_t* v, const
     return hipGetLastError();
 }
 
+hipError_t launch_decode_step_scan(float* idx_k, uint16_t* k, uint16_t* v, const Pager& pg, const float* idx_q,
+                                   const int32_t* stream, const int32_t* pos, int64_t n_q, int nblk,
+                                   const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
+                                   float* bs, hipStream_t s) {
+    const unsigned ny = static_cast<unsigned>((nblk + kScanBlocksPerWg - 1) / kScanBlocksPerWg);
+    hipLaunchKernelGGL(block_scores_decode_kernel<true>, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
+                       0, s, idx_k, pg, idx_q, stream, pos, bs, static_cast<int64_t>(nblk), nblk,
+                       StepRows{idx_k, k, v, n_q, idx_k_new, k_new, v_new});
+    return hipGetLastError();
+}
+
 hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, const int32_t* stream,
                                       const int32_t* pos, int64_t n_q, int nblk, float* bs,
                                       int64_t nblk_stride, hipStream_t s) {
@@ -371,8 +455,9 @@ hipError_t launch_block_scores_decode(const CacheView& c, const float* idx_q, co
         hipLaunchKernelGGL(block_scores_decode_f16_kernel, dim3(static_cast<unsigned>(n_q), ny16),
                            dim3(64 * kScanWaves), 0, s, c.idx_k16, c.pg, idx_q, stream, pos, bs, nblk_stride, nblk);
     else
-        hipLaunchKernelGGL(block_scores_decode_kernel, dim3(static_cast<unsigned>(n_q), ny), dim3(64 * kScanWaves),
-                           0, s, c.idx_k, c.pg, idx_q, stream, pos, bs, nblk_stride, nblk);
+        hipLaunchKernelGGL(block_scores_decode_kernel<false>, dim3(static_cast<unsigned>(n_q), ny),
+                           dim3(64 * kScanWaves), 0, s, c.idx_k, c.pg, idx_q, stream, pos, bs, nblk_stride, nblk,
+                           StepRows{});
     return hipGetLastError();
 }
 

@@ -178,6 +178,13 @@ hipError_t launch_decode_step_fine(float* idx_k, uint16_t* k, uint16_t* v, const
                                    const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
                                    float* bs_part, hipStream_t s);
 
+// Decode step, larger problems: the scan above (one score per block, nblk
+// per (query, group)), which also appends the rows as the fine form does.
+hipError_t launch_decode_step_scan(float* idx_k, uint16_t* k, uint16_t* v, const Pager& pg, const float* idx_q,
+                                   const int32_t* stream, const int32_t* pos, int64_t n_q, int nblk,
+                                   const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
+                                   float* bs, hipStream_t s);
+
 // ws: prefill_scores_ws_bytes(pos0 + n_q - 1) bytes (the split keys).
 size_t prefill_scores_ws_bytes(int32_t max_pos);
 hipError_t launch_block_scores_prefill(const CacheView& c, const float* idx_q, int32_t stream,
@@ -216,8 +223,9 @@ struct AttendArgs {
     const float* v_scale;
     int32_t stream0;         // stream == NULL: query i is at (stream0, pos0 + i) (a prefill chunk)
     int32_t pos0;
-    // Decode step (MSA blocks, at most kRankedBlocks of them): the selection
-    // is ranked by the kernel from the scan's partial maxima
+    // Decode step (MSA blocks, at most kRankedBlocks of them; a fine scan's
+    // n_sub > 1 partials only up to 512): the selection is ranked by the
+    // kernel from the scan's block scores or partial maxima
     // bs_part[query][group][nblk_part][n_sub], as launch_topk_blocks ranks
     // them, instead of read from `sel`; the workgroups of split 0 write it
     // to sel_out [query][group][sel_len] and its size to n_sel_out.
@@ -227,7 +235,7 @@ struct AttendArgs {
     int32_t* sel_out = nullptr;
     int32_t* n_sel_out = nullptr;
 };
-constexpr int kRankedBlocks = 64;
+constexpr int kRankedBlocks = 1024;
 int attend_num_splits(int64_t n_q, int sel_len, int unit);
 size_t attend_ws_bytes(int64_t n_q, int sel_len, int unit);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);

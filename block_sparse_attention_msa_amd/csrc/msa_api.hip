@@ -88,12 +88,11 @@ size_t decode_step_ws(const msa_dims* dims, int64_t n_q, int32_t max_pos) {
     return select_ws(n_q, max_pos) + align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
 }
 
-// msa_decode_step in three kernels: few queries over at most 64 blocks (the
-// attention kernel ranks them), the f32 index cache and bf16 K/V.
-bool decode_step_fused(const msa_cache* c, int64_t n_q, int32_t max_pos) {
-    const int nblk = nblk_of(max_pos);
-    return c->idx_k && !c->idx_k_f16 && c->kv_format == 0 && nblk <= msa::kRankedBlocks &&
-           msa::scan_is_fine(n_q, nblk);
+// msa_decode_step in three kernels (the scan appends the rows, the attention
+// kernel ranks the blocks): the f32 index cache, bf16 K/V and at most
+// kRankedBlocks blocks.
+bool decode_step_fused(const msa_cache* c, int32_t max_pos) {
+    return c->idx_k && !c->idx_k_f16 && c->kv_format == 0 && nblk_of(max_pos) <= msa::kRankedBlocks;
 }
 
 // msa_select_prefill: block scores, then the split keys of the scorer.
@@ -431,7 +430,7 @@ msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const i
     const size_t att_bytes = align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
     if (ws_bytes < decode_step_ws(dims, n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     char* att_ws = static_cast<char*>(d_ws) + sel_bytes;
-    if (!decode_step_fused(cache, n_q, max_pos)) {
+    if (!decode_step_fused(cache, max_pos)) {
         MSA_TRY(msa_index_append(dims, cache, d_stream, d_pos, n_q, max_pos, d_idx_k_new, d_k_new, d_v_new,
                                  hip_stream));
         MSA_TRY(msa_select(dims, cache, d_idx_q, d_stream, d_pos, n_q, max_pos, d_sel, d_n_sel, d_ws, sel_bytes,
@@ -442,15 +441,21 @@ msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const i
     const hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const int nblk = nblk_of(max_pos);
     float* bs_part = static_cast<float*>(d_ws);
-    MSA_TRY(hip_status(msa::launch_decode_step_fine(cache->idx_k, cache->k, cache->v, view(cache).pg, d_idx_q,
-                                                    d_stream, d_pos, n_q, nblk, d_idx_k_new, d_k_new, d_v_new,
-                                                    bs_part, s)));
+    const bool fine = msa::scan_is_fine(n_q, nblk);     // few queries over a short context: partial maxima
+    if (fine)
+        MSA_TRY(hip_status(msa::launch_decode_step_fine(cache->idx_k, cache->k, cache->v, view(cache).pg, d_idx_q,
+                                                        d_stream, d_pos, n_q, nblk, d_idx_k_new, d_k_new, d_v_new,
+                                                        bs_part, s)));
+    else
+        MSA_TRY(hip_status(msa::launch_decode_step_scan(cache->idx_k, cache->k, cache->v, view(cache).pg, d_idx_q,
+                                                        d_stream, d_pos, n_q, nblk, d_idx_k_new, d_k_new, d_v_new,
+                                                        bs_part, s)));
     msa::AttendArgs a{cache->k, cache->v, view(cache).pg, d_q, d_stream, d_pos, n_q, d_sel,
                       dims->top_k, dims->top_k, kBlock, dims->scale, d_out, att_ws,
                       0, nullptr, nullptr};
     a.bs_part = bs_part;
     a.nblk_part = nblk;
-    a.n_sub = msa::kFineSub;
+    a.n_sub = fine ? msa::kFineSub : 1;
     a.sel_out = d_sel;
     a.n_sel_out = d_n_sel;
     return hip_status(msa::launch_attend(a, s));

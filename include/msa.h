@@ -336,12 +336,12 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
  * d_pos[i]), then msa_select and msa_attend_decode of the queries at those
  * same slots, with the same outputs bit for bit (cache rows, d_sel [n_q]
  * [n_group][top_k], d_n_sel, d_out).  d_k_new and d_v_new may be NULL (that
- * cache is not written); d_idx_k_new is required.  For few queries over
- * short contexts (at most 64 blocks, an f32 index cache, bf16 K/V, and a
- * scan of fewer than 256 workgroups) it runs three kernels instead of five:
- * the scan writes the rows and scores the new keys from d_idx_k_new, the
- * attention ranks each (query, group)'s blocks itself, then the split
- * combine; any other shape runs the separate calls' kernels.
+ * cache is not written); d_idx_k_new is required.  With an f32 index
+ * cache, bf16 K/V and at most 1024 blocks (max_pos < 131072) it runs three
+ * kernels instead of five: the scan also writes the rows and scores the new
+ * keys from d_idx_k_new, the attention ranks each (query, group)'s blocks
+ * itself (and writes d_sel, d_n_sel), then the split combine; other caches
+ * and longer contexts run the separate calls' kernels.
  * Device preconditions: those of the three calls ((stream, pos) pairs
  * distinct, d_pos[i] <= max_pos).  Workspace: MSA_OP_DECODE_STEP, the
  * block scores followed by the attention partials (each 256-byte aligned).

@@ -89,8 +89,10 @@ def _both_forms(wl: W.Workload, paged: bool = False):
     return results[1], host, qs
 
 
-# Shapes: the rule for the three-kernel form is nblk <= 64 and
-# n_q * ceil(nblk / 2) < 256 (and an f32 index cache with bf16 K/V).
+# Shapes: the three-kernel form takes an f32 index cache, bf16 K/V and at
+# most 1024 blocks; its scan is the fine one (partial maxima) when
+# n_q * ceil(nblk / 2) < 256, and the attention ranks up to 64 blocks
+# directly, more by register rounds (4, 8 or 16 keys per lane).
 CASES = [
     # (name, n_stream, cap, streams, positions, top_k)
     ("one_query_4k", 1, 4096, (0,), (4095,), 16),
@@ -98,8 +100,11 @@ CASES = [
     ("one_stream_neighbours", 2, 3000, (0, 0, 0, 1, 0), (1000, 1001, 1130, 500, 1127), 16),
     ("short_top64", 3, 8192, (0, 1, 2), (200, 8191, 4000), 64),
     ("top1", 2, 2048, (0, 1), (2047, 300), 1),
-    ("separate_kernels_20x8k", 20, 8192, tuple(range(20)), tuple(8191 - 37 * j for j in range(20)), 16),
-    ("separate_kernels_long", 2, 20000, (0, 1), (19999, 9000), 16),
+    ("coarse_scan_20x8k", 20, 8192, tuple(range(20)), tuple(8191 - 37 * j for j in range(20)), 16),
+    ("fine_scan_register_rank", 2, 20000, (0, 1), (19999, 9000), 16),
+    ("coarse_scan_one_stream_neighbours", 3, 40000, (0, 0, 1, 0, 2), (39999, 39998, 20000, 30000, 128), 16),
+    ("coarse_scan_1024_blocks", 1, 131072, (0,), (131071,), 16),
+    ("separate_kernels_over_1024_blocks", 1, 140000, (0,), (139999,), 16),
 ]
 
 
