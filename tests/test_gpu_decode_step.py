@@ -135,3 +135,55 @@ def test_decode_step_integer_workload_against_oracle():
                                  scale=W.SCALE)
     wa, wr = check_attention(res["out"].numpy(), o_out)
     log(f"  attention max-abs {wa:.3e}, rel-L2 {wr:.3e}")
+
+
+@pytest.mark.parametrize("ctx,n_stream", [(4096, 1), (16384, 24)])
+def test_decode_step_graph_replay_matches_eager(ctx, n_stream):
+    """msa_decode_step captured into a HIP graph and replayed six times, with
+    eager work and synchronisations in between (outputs cleared, the
+    workspace cleared before one replay, an eager call before another),
+    reproduces the eager step bit for bit every time: the fine-scan form
+    (one query over 4096 slots) and the regular-scan form (24 queries over
+    16384)."""
+    wl = W.decode_workload(f"step_graph_{ctx}", n_stream, ctx)
+    host, qs = W.caches(wl), W.queries(wl)
+    dims = M.msa_dims(16, W.SCALE)
+    st, ps = qs["stream"].astype(np.int64), qs["pos"].astype(np.int64)
+    cache = M.make_cache(k=dev_bits(host["k"], torch.bfloat16), v=dev_bits(host["v"], torch.bfloat16),
+                         idx_k=dev(host["idx_k"]))
+    stream, pos = dev(qs["stream"]), dev(qs["pos"])
+    new_idx = dev(host["idx_k"][st, ps])
+    new_k = dev_bits(host["k"][st, ps], torch.bfloat16)
+    new_v = dev_bits(host["v"][st, ps], torch.bfloat16)
+    idx_q, q = dev(qs["idx_q"]), dev_bits(qs["q"], torch.bfloat16)
+    sel = torch.empty((wl.n_q, 4, 16), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty((wl.n_q, 4), dtype=torch.int32, device=DEV)
+    out = torch.empty((wl.n_q, 64, 128), dtype=torch.float32, device=DEV)
+    ws = torch.empty(M.workspace_bytes(dims, M.MSA_OP_DECODE_STEP, wl.n_q, wl.max_pos), dtype=torch.uint8,
+                     device=DEV)
+    log(f"[decode step] graph replay: {wl.n_q} queries over {ctx} slots")
+
+    def step():
+        M.msa_decode_step(dims, cache, stream, pos, wl.max_pos, new_idx, new_k, new_v, idx_q, q, sel, n_sel, out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel, ref_n = out.clone(), sel.clone(), n_sel.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(6):
+        out.zero_()
+        sel.fill_(-7)
+        n_sel.fill_(-7)
+        if r == 1:
+            ws.zero_()
+        elif r == 3:
+            step()
+            out.zero_()
+            sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {r}: output differs"
+        assert torch.equal(sel, ref_sel) and torch.equal(n_sel, ref_n), f"replay {r}: selection differs"
