@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         float* dst = a.out + (i * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + hh) * kHeadDim + d0;
         *reinterpret_cast<f32x4*>(dst) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-    } else {
+    } else if (a.arrive == nullptr) {
         float* part = static_cast<float*>(a.ws) + ((i * kGroups + g) * ka.n_split + sp) * kPartFloats;
         float* dst = part + hh * kHeadDim + d0;
         *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
@@ -553,6 +553,85 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         if ((threadIdx.x & 15) == 0) {
             part[kHeadsPerGroup * kHeadDim + 2 * hh] = M;
             part[kHeadsPerGroup * kHeadDim + 2 * hh + 1] = L;
+        }
+    } else {
+        // Decode step: the last split of this (query, group) to finish
+        // merges the partials as the combine kernels do (split order,
+        // against the largest m).  The partials of the pair are written and
+        // read with system-coherent (sc1) buffer accesses, which go to and
+        // come from memory past every XCD's L2, so they need no L2
+        // write-back or invalidation: each thread waits for its partial
+        // stores to complete before the barrier that precedes the arrival
+        // (an agent-scope atomic), and the merging workgroup reads only
+        // after the arrival returned.
+        const int64_t pair = i * kGroups + g;
+        const uint32_t pbytes = static_cast<uint32_t>(ka.n_split * kPartFloats * sizeof(float));
+        const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<float*>(a.ws) + pair * ka.n_split * kPartFloats, 0, pbytes, 0x00020000);
+        constexpr int kSc1 = 16;                  // cache policy: sc1
+        constexpr int kMl = kHeadsPerGroup * kHeadDim;   // (m, l) of head h at kMl + 2h
+        const int own = sp * kPartFloats;         // this split's partial, in floats
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{o[0], o[1], o[2], o[3]}), prs,
+                                               4 * (own + hh * kHeadDim + d0), 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{o[4], o[5], o[6], o[7]}), prs,
+                                               4 * (own + hh * kHeadDim + d0 + 4), 0, kSc1);
+        if ((threadIdx.x & 15) == 0) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), prs, 4 * (own + kMl + 2 * hh), 0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), prs, 4 * (own + kMl + 2 * hh + 1), 0, kSc1);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));     // this thread's partial stores have completed
+        __shared__ int last_s;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            last_s = __hip_atomic_fetch_add(a.arrive + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     ka.n_split - 1;
+        __syncthreads();
+        if (last_s) {
+            // the partials in batches of 16 splits, each batch's loads in
+            // flight together (masked past the last split, whose weight is 0)
+            constexpr int kB = 16;
+            float Mx = -INFINITY;
+            for (int s0 = 0; s0 < ka.n_split; s0 += kB) {
+                float ms[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int jj = s0 + j < ka.n_split ? s0 + j : s0;
+                    ms[j] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(prs, 4 * (jj * kPartFloats + kMl + 2 * hh), 0, kSc1));
+                }
+#pragma unroll
+                for (int j = 0; j < kB; ++j) Mx = fmaxf(Mx, s0 + j < ka.n_split ? ms[j] : -INFINITY);
+            }
+            float Lx = 0.f;
+            float ox[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < ka.n_split; s0 += kB) {
+                float ms[kB], ls[kB];
+                f32x4 a0[kB], a1[kB];
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {
+                    const int jj = s0 + j < ka.n_split ? s0 + j : s0;
+                    const int base = jj * kPartFloats;
+                    ms[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(prs, 4 * (base + kMl + 2 * hh), 0, kSc1));
+                    ls[j] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(prs, 4 * (base + kMl + 2 * hh + 1), 0, kSc1));
+                    a0[j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, 4 * (base + hh * kHeadDim + d0), 0, kSc1));
+                    a1[j] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, 4 * (base + hh * kHeadDim + d0 + 4), 0, kSc1));
+                }
+#pragma unroll
+                for (int j = 0; j < kB; ++j) {                   // in split order
+                    const float mj = s0 + j < ka.n_split ? ms[j] : -INFINITY;
+                    const float wt = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - Mx);
+                    Lx += wt * ls[j];
+                    ox[0] += wt * a0[j].x; ox[1] += wt * a0[j].y; ox[2] += wt * a0[j].z; ox[3] += wt * a0[j].w;
+                    ox[4] += wt * a1[j].x; ox[5] += wt * a1[j].y; ox[6] += wt * a1[j].z; ox[7] += wt * a1[j].w;
+                }
+            }
+            const float inv = 1.f / Lx;
+            float* od = a.out + (i * kGroups * kHeadsPerGroup + g * kHeadsPerGroup + hh) * kHeadDim + d0;
+            *reinterpret_cast<f32x4*>(od) = f32x4{ox[0] * inv, ox[1] * inv, ox[2] * inv, ox[3] * inv};
+            *reinterpret_cast<f32x4*>(od + 4) = f32x4{ox[4] * inv, ox[5] * inv, ox[6] * inv, ox[7] * inv};
         }
     }
 }
@@ -707,7 +786,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
         default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || ka.n_split == 1) return e;
+    if (e != hipSuccess || ka.n_split == 1 || a.arrive != nullptr) return e;   // (arrival: merged in the kernel)
     const dim3 cgrid(static_cast<unsigned>(a.n_q * kGroups));
     const float* part = static_cast<const float*>(a.ws);
     switch (ka.n_split) {

@@ -326,6 +326,7 @@ struct StepScanArgs {
     const uint16_t* v_new;
     float* bs_part;
     int nblk;
+    int32_t* arrive;            // [n_q][kGroups], zeroed here for the attention that follows
 };
 
 __global__ __launch_bounds__(64 * kFineWaves) void decode_step_fine_kernel(StepScanArgs a) {
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(64 * kFineWaves) void decode_step_fine_kernel(StepS
     const int c = lane & 15;
     constexpr int kTokPerWg = kFineWaves * kFineTokPerWave;                // 16
     const f32x4* new_row = reinterpret_cast<const f32x4*>(a.idx_k_new + i * kGroups * kIdxDim);
+    if (b == 0 && sub == 0 && tid < kGroups) a.arrive[i * kGroups + tid] = 0;
     if (b == p / kBlock && sub == (p % kBlock) / kTokPerWg) {
         const int64_t slot = a.pg.row(s, p);
         if (tid < kGroups * kIdxDim / 4)   // 128 x 16 B
@@ -428,8 +430,8 @@ hipError_t launch_block_scores_decode_fine(const CacheView& c, const float* idx_
 hipError_t launch_decode_step_fine(float* idx_k, uint16_t* k, uint16_t* v, const Pager& pg, const float* idx_q,
                                    const int32_t* stream, const int32_t* pos, int64_t n_q, int nblk,
                                    const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
-                                   float* bs_part, hipStream_t s) {
-    StepScanArgs a{idx_k, k, v, pg, idx_q, stream, pos, n_q, idx_k_new, k_new, v_new, bs_part, nblk};
+                                   float* bs_part, int32_t* arrive, hipStream_t s) {
+    StepScanArgs a{idx_k, k, v, pg, idx_q, stream, pos, n_q, idx_k_new, k_new, v_new, bs_part, nblk, arrive};
     hipLaunchKernelGGL(decode_step_fine_kernel, dim3(static_cast<unsigned>(n_q), nblk, kFineSub),
                        dim3(64 * kFineWaves), 0, s, a);
     return hipGetLastError();

@@ -171,12 +171,13 @@ hipError_t launch_block_scores_decode_fine(const CacheView& c, const float* idx_
                                            const int32_t* pos, int64_t n_q, int nblk, float* bs_part,
                                            hipStream_t s);
 // Decode step, small problems (scan_is_fine): the fine scan, which also
-// writes each query's new index, K and V rows at (stream, pos) and scores
-// the step's new keys from idx_k_new (k_new, v_new may be NULL).
+// writes each query's new index, K and V rows at (stream, pos), scores the
+// step's new keys from idx_k_new (k_new, v_new may be NULL) and zeroes the
+// attention's arrival counters arrive[n_q][kGroups].
 hipError_t launch_decode_step_fine(float* idx_k, uint16_t* k, uint16_t* v, const Pager& pg, const float* idx_q,
                                    const int32_t* stream, const int32_t* pos, int64_t n_q, int nblk,
                                    const float* idx_k_new, const uint16_t* k_new, const uint16_t* v_new,
-                                   float* bs_part, hipStream_t s);
+                                   float* bs_part, int32_t* arrive, hipStream_t s);
 
 // Decode step, larger problems: the scan above (one score per block, nblk
 // per (query, group)), which also appends the rows as the fine form does.
@@ -234,6 +235,10 @@ struct AttendArgs {
     int n_sub = 1;
     int32_t* sel_out = nullptr;
     int32_t* n_sel_out = nullptr;
+    // Decode step: an arrival counter per (query, group), zero at launch;
+    // the last split of a pair to finish merges the pair's partials (no
+    // combine launch).
+    int32_t* arrive = nullptr;
 };
 constexpr int kRankedBlocks = 1024;
 int attend_num_splits(int64_t n_q, int sel_len, int unit);

@@ -83,9 +83,11 @@ size_t select_ws(int64_t n_q, int32_t max_pos) {
     return align256(static_cast<size_t>(n_q) * kGroups * nblk * per * sizeof(float));
 }
 
-// msa_decode_step: the block scores, then the attention partials.
+// msa_decode_step: the block scores, the attention partials, then an
+// arrival counter per (query, group).
 size_t decode_step_ws(const msa_dims* dims, int64_t n_q, int32_t max_pos) {
-    return select_ws(n_q, max_pos) + align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
+    return select_ws(n_q, max_pos) + align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock)) +
+           align256(static_cast<size_t>(n_q) * kGroups * sizeof(int32_t));
 }
 
 // msa_decode_step in three kernels (the scan appends the rows, the attention
@@ -430,6 +432,7 @@ msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const i
     const size_t att_bytes = align256(msa::attend_ws_bytes(n_q, dims->top_k, kBlock));
     if (ws_bytes < decode_step_ws(dims, n_q, max_pos)) return MSA_ERR_WORKSPACE_TOO_SMALL;
     char* att_ws = static_cast<char*>(d_ws) + sel_bytes;
+    int32_t* arrive = reinterpret_cast<int32_t*>(att_ws + att_bytes);
     if (!decode_step_fused(cache, max_pos)) {
         MSA_TRY(msa_index_append(dims, cache, d_stream, d_pos, n_q, max_pos, d_idx_k_new, d_k_new, d_v_new,
                                  hip_stream));
@@ -445,7 +448,7 @@ msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const i
     if (fine)
         MSA_TRY(hip_status(msa::launch_decode_step_fine(cache->idx_k, cache->k, cache->v, view(cache).pg, d_idx_q,
                                                         d_stream, d_pos, n_q, nblk, d_idx_k_new, d_k_new, d_v_new,
-                                                        bs_part, s)));
+                                                        bs_part, arrive, s)));
     else
         MSA_TRY(hip_status(msa::launch_decode_step_scan(cache->idx_k, cache->k, cache->v, view(cache).pg, d_idx_q,
                                                         d_stream, d_pos, n_q, nblk, d_idx_k_new, d_k_new, d_v_new,
@@ -458,6 +461,7 @@ msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const i
     a.n_sub = fine ? msa::kFineSub : 1;
     a.sel_out = d_sel;
     a.n_sel_out = d_n_sel;
+    a.arrive = fine ? arrive : nullptr;       // few queries: the last split merges (no combine launch)
     return hip_status(msa::launch_attend(a, s));
 }
 

@@ -340,11 +340,15 @@ MSA_API msa_status msa_attend_decode(const msa_dims* dims, const msa_cache* cach
  * cache, bf16 K/V and at most 1024 blocks (max_pos < 131072) it runs three
  * kernels instead of five: the scan also writes the rows and scores the new
  * keys from d_idx_k_new, the attention ranks each (query, group)'s blocks
- * itself (and writes d_sel, d_n_sel), then the split combine; other caches
- * and longer contexts run the separate calls' kernels.
+ * itself (and writes d_sel, d_n_sel), then the split combine; when the
+ * fine scan runs (few queries over short contexts) the last attention split
+ * of each (query, group) merges the partials itself, so two kernels run.
+ * Other caches and longer contexts run the separate calls' kernels.
  * Device preconditions: those of the three calls ((stream, pos) pairs
  * distinct, d_pos[i] <= max_pos).  Workspace: MSA_OP_DECODE_STEP, the
- * block scores followed by the attention partials (each 256-byte aligned).
+ * block scores, the attention partials, then n_q * 4 arrival counters
+ * (int32), each part 256-byte aligned; calls that overlap on one workspace
+ * race.
  */
 MSA_API msa_status msa_decode_step(const msa_dims* dims, const msa_cache* cache, const int32_t* d_stream,
                            const int32_t* d_pos, int64_t n_q, int32_t max_pos, const float* d_idx_k_new,

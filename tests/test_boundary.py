@@ -350,7 +350,7 @@ def test_decode_step_validation_and_workspace(L):
     for n_q, max_pos in ((1, 4095), (5, 2999), (32, 32767), (20, 8191), (100, 127)):
         sel_ws = M.workspace_bytes(d, M.MSA_OP_SELECT, n_q, max_pos)
         att_ws = M.workspace_bytes(d, M.MSA_OP_ATTEND_DECODE, n_q, max_pos)
-        assert M.workspace_bytes(d, M.MSA_OP_DECODE_STEP, n_q, max_pos) == sel_ws + up(att_ws)
+        assert M.workspace_bytes(d, M.MSA_OP_DECODE_STEP, n_q, max_pos) == sel_ws + up(att_ws) + up(n_q * 4 * 4)
     c = _cache(dsa=None)
     need = M.workspace_bytes(d, M.MSA_OP_DECODE_STEP, 1, 4095)
 

@@ -6,8 +6,9 @@ attention output -- must equal those of msa_index_append + msa_select +
 msa_attend_decode bit for bit: on the three-kernel form (few queries over
 at most 64 blocks, f32 index cache, bf16 K/V: the scan appends the rows and
 scores the new keys from the inputs, the attention ranks the blocks itself,
-then the split combine) and on the separate-kernel form the other shapes
-take.  The integer workload
+then the split combine, or, after the fine scan, the last split of each
+(query, group) merging the partials itself) and on the separate-kernel form
+the other shapes take.  The integer workload
 is also held to the oracle (selection bit-exact, attention to the attention
 tolerances), and queries of one stream at neighbouring positions score each
 other's new keys.
