@@ -6,9 +6,11 @@ workload: append one token per stream (index key + K + V) at position 32767,
 score -> causal mask -> block max-pool (indexer scan), top-16 block selection,
 and sparse attention of all 64 heads over the 2048 selected keys.  `value` is
 decode queries/s (32 queries per step), inputs resident in HBM; the step is
-timed both launched eagerly and replayed from a HIP graph (the library only
-enqueues on the caller's stream, so a step can be captured), and the faster
-of the two is reported when the replay reproduces the eager output.
+timed launched eagerly, replayed from a HIP graph one step per replay, and
+with the K timed steps captured into one graph replayed once (the library
+only enqueues on the caller's stream, so steps can be captured), each as
+separate calls and as one msa_decode_step call; the fastest form is reported
+when it reproduces the eager output, and config.step names it.
 
 Also measured in the same run and reported under "extra": the indexer scan
 and decode attention GB/s, the 4096-query prefill chunk at positions
@@ -233,9 +235,39 @@ def main():
     call_ok = call_ok and bool(torch.equal(out, out_sep) and torch.equal(sel, sel_sep))
     log(f"[bench] decode step as msa_decode_step: eager {ms_call * 1e3:.1f} us, graph replay "
         f"{ms_call_graph * 1e3:.1f} us (output {'identical to the separate calls' if call_ok else 'DIFFERS'})")
+    # The K timed steps captured consecutively into one graph and replayed
+    # once between the two synchronisations: the same K steps, every kernel
+    # of each, with one host launch for all of them.
+    def k_step_graph(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                fn()
+        g.replay()                                 # warm-up replay (untimed)
+        torch.cuda.synchronize()
+        out.zero_()
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ok = bool(torch.equal(out, out_sep) and torch.equal(sel, sel_sep))
+        del g
+        return ms, ok
+
+    ms_kg, kg_ok = k_step_graph(step)
+    ms_call_kg, call_kg_ok = k_step_graph(step_call)
+    log(f"[bench] decode step, {args.steps} steps in one graph replay: separate calls {ms_kg * 1e3:.1f} us, "
+        f"msa_decode_step {ms_call_kg * 1e3:.1f} us per step (outputs "
+        f"{'identical' if kg_ok and call_kg_ok else 'DIFFER'})")
     forms = [(ms_eager, "separate calls"), (ms_graph if graph_ok else 1e9, "separate calls, graph replay")]
+    if kg_ok:
+        forms += [(ms_kg, f"separate calls, {args.steps} steps in one graph replay")]
     if call_ok:
         forms += [(ms_call, "msa_decode_step"), (ms_call_graph, "msa_decode_step, graph replay")]
+        if call_kg_ok:
+            forms += [(ms_call_kg, f"msa_decode_step, {args.steps} steps in one graph replay")]
     ms_per_step, step_form = min(forms)
     value = S / (ms_per_step / 1e3)
     scan_bytes = S * (p + 1) * 4 * 128 * 4 + S * 4 * 128 * 4 + S * 4 * nblk * 4
@@ -318,6 +350,8 @@ def main():
         "decode_step_us": {"eager": round(ms_eager * 1e3, 2), "hip_graph": round(ms_graph * 1e3, 2),
                            "msa_decode_step": round(ms_call * 1e3, 2),
                            "msa_decode_step_graph": round(ms_call_graph * 1e3, 2),
+                           "k_steps_one_graph": round(ms_kg * 1e3, 2),
+                           "msa_decode_step_k_steps_one_graph": round(ms_call_kg * 1e3, 2),
                            "msa_decode_step_identical": call_ok,
                            "graph_replay_matches_eager": graph_ok},
         "device_copy_GBps": round(copy_gbps, 1),
@@ -654,6 +688,36 @@ def bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name, iters=30):
     log(f"[bench] {name}: msa_decode_step {np.median(s_ms) * 1e3:.1f} us (p10 {np.percentile(s_ms, 10) * 1e3:.1f}), "
         f"graph replay {np.median(gs_ms) * 1e3:.1f} us (p10 {np.percentile(gs_ms, 10) * 1e3:.1f}, "
         f"p90 {np.percentile(gs_ms, 90) * 1e3:.1f}); output {'identical to the separate calls' if step_ok else 'DIFFERS'}")
+    # One replay above is bracketed by events with the host's graph launch
+    # inside the interval, which for a step of small kernels is longer than
+    # the step itself.  Here n_rep consecutive steps are captured into one
+    # graph: one host launch per n_rep steps, so the per-step time is the
+    # device's (every kernel of every step, and the gaps between dependent
+    # kernels).
+    n_rep = 20
+    per_step = {}
+    for form, fn in (("separate_calls", run), ("msa_decode_step", run_step)):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph_n = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_n):
+            for _ in range(n_rep):
+                fn()
+        graph_n.replay()
+        torch.cuda.synchronize()
+        ok = bool(torch.equal(out, out_sep))
+        t_n = []
+        for _ in range(5):
+            g0.record()
+            graph_n.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            t_n.append(g0.elapsed_time(g1) / n_rep)
+        per_step[form] = {"us": round(float(np.median(t_n)) * 1e3, 2), "output_identical": ok}
+        del graph_n
+    log(f"[bench] {name}: {n_rep} steps per graph replay: separate calls "
+        f"{per_step['separate_calls']['us']:.1f} us, msa_decode_step {per_step['msa_decode_step']['us']:.1f} us "
+        f"per step (outputs {'identical' if all(v['output_identical'] for v in per_step.values()) else 'DIFFER'})")
     key = name.replace("decode_", "")
     return {
         f"decode_{key}_step_call_us": {"eager_median": round(np.median(s_ms) * 1e3, 2),
@@ -663,6 +727,7 @@ def bench_decode_config(M, W, torch, dev, bits, tens, wsbuf, name, iters=30):
                                        "graph_p90": round(np.percentile(gs_ms, 90) * 1e3, 2),
                                        "output_identical": step_ok},
         f"decode_{key}_step_call_graph_queries_s": round(S / (np.median(gs_ms) * 1e-3), 1) if step_ok else None,
+        f"decode_{key}_{n_rep}_steps_per_graph_us": per_step,
         f"decode_{key}_queries_s": round(S / (step.mean() * 1e-3), 1),
         f"decode_{key}_graph_queries_s": round(S / (np.median(g_ms) * 1e-3), 1) if graph_ok else None,
         f"decode_{key}_us": {"step": round(step.mean() * 1e3, 2), "step_p10": round(np.percentile(step, 10) * 1e3, 2),
@@ -728,6 +793,29 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20, profile=False):
     att_bytes = S * 4 * 2048 * 128 * 2 * 2 + S * 2048 * 4
     total = seg.sum()
     log(f"[bench] dsa: append {seg[0] * 1e3:.1f} select {seg[1] * 1e3:.1f} attend {seg[2] * 1e3:.1f} us")
+    # The same step by the wall clock of back-to-back calls, and captured once
+    # into a HIP graph and replayed (every kernel still runs; only the host
+    # launch gaps go away); the replays must reproduce the eager outputs.
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        run()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / iters
+    out_eager, sel_eager = out.clone(), sel.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / iters
+    graph_ok = bool(torch.equal(out, out_eager) and torch.equal(sel, sel_eager))
+    log(f"[bench] dsa step: eager {eager_ms * 1e3:.1f} us, graph replay {graph_ms * 1e3:.1f} us "
+        f"(replay output {'identical' if graph_ok else 'DIFFERENT'})")
 
     # The multi-head indexer (32 heads, weights per query): a "full" layer
     # selects with it; an IndexShare "shared" layer reuses the last full
@@ -764,6 +852,9 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20, profile=False):
         f"attend {seg_h[2] * 1e3:.1f} us; shared layer (no select) {shared_ms * 1e3:.1f} us")
     return {
         "dsa_queries_s": round(S / (total * 1e-3), 1),
+        "dsa_step_us": {"events": round(total * 1e3, 2), "eager": round(eager_ms * 1e3, 2),
+                        "hip_graph": round(graph_ms * 1e3, 2), "graph_replay_matches_eager": graph_ok},
+        "dsa_graph_queries_s": round(S / (graph_ms * 1e-3), 1),
         "dsa_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
                    "attend": round(seg[2] * 1e3, 2)},
         "dsa_select_GBps": round(scan_bytes / (seg[1] * 1e-3) / 1e9, 1),

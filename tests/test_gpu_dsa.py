@@ -205,3 +205,57 @@ def test_dsa_topk_boundary_tie_list_over_2048():
     o_sel, o_nsel, _ = oracle.dsa_select(k_rot.view(np.uint16), stream, pos, q.view(np.uint16), top_k=top_k)
     assert np.array_equal(n_sel.cpu().numpy(), o_nsel)
     assert np.array_equal(sel.cpu().numpy(), o_sel), "selection differs from the oracle"
+
+
+@pytest.mark.parametrize("n_stream,ctx", [(4, 20000), (3, 3000)])
+def test_dsa_step_graph_replay_matches_eager(n_stream, ctx):
+    """The DSA decode step (append, select, attend) captured into a HIP graph
+    and replayed six times, with eager work and synchronisations in between
+    (outputs cleared, both workspaces cleared before one replay, an eager
+    step before another), reproduces the eager step bit for bit every time:
+    the chunked top-k (4 queries over 20000 keys) and the one-workgroup
+    register top-k (3 queries over 3000)."""
+    wl = W.Workload(f"dsa_graph_{ctx}", "dsa_decode", n_stream, ctx, tuple(range(n_stream)),
+                    tuple(ctx - 1 - 7 * j for j in range(n_stream)), top_k=2048)
+    log(f"[dsa] graph replay: {wl.n_q} queries over {ctx} slots")
+    gw = GpuWorkload(wl)
+    gw.append_own_rows()
+    dims = M.dsa_dims(wl.top_k, W.SCALE)
+    st, ps = gw.qs["stream"].astype(np.int64), gw.qs["pos"].astype(np.int64)
+    new_key = dev_bits(gw.host["dsa_k"][st, ps], torch.float16)
+    new_k = dev_bits(gw.host["k"][st, ps], torch.bfloat16)
+    new_v = dev_bits(gw.host["v"][st, ps], torch.bfloat16)
+    q_idx = dev_bits(gw.qs["q_idx"], torch.float16)
+    sel = torch.empty((wl.n_q, wl.top_k), dtype=torch.int32, device=DEV)
+    n_sel = torch.empty(wl.n_q, dtype=torch.int32, device=DEV)
+    out = torch.empty((wl.n_q, 64, 128), dtype=torch.float32, device=DEV)
+    ws_sel = gw.ws(dims, M.DSA_OP_SELECT)
+    ws_att = gw.ws(dims, M.DSA_OP_ATTEND_DECODE)
+
+    def step():
+        M.dsa_index_append(dims, gw.cache, gw.stream, gw.pos, wl.max_pos, new_key, new_k, new_v)
+        M.dsa_select(dims, gw.cache, q_idx, gw.stream, gw.pos, wl.max_pos, sel, n_sel, ws_sel)
+        M.dsa_attend_decode(dims, gw.cache, gw.q, gw.stream, gw.pos, wl.max_pos, sel, out, ws_att)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_sel, ref_n = out.clone(), sel.clone(), n_sel.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(6):
+        out.zero_()
+        sel.fill_(-7)
+        n_sel.fill_(-7)
+        if r == 1:
+            ws_sel.zero_()
+            ws_att.zero_()
+        elif r == 3:
+            step()
+            out.zero_()
+            sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {r}: output differs"
+        assert torch.equal(sel, ref_sel) and torch.equal(n_sel, ref_n), f"replay {r}: selection differs"
