@@ -814,8 +814,31 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20, profile=False):
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3 / iters
     graph_ok = bool(torch.equal(out, out_eager) and torch.equal(sel, sel_eager))
-    log(f"[bench] dsa step: eager {eager_ms * 1e3:.1f} us, graph replay {graph_ms * 1e3:.1f} us "
-        f"(replay output {'identical' if graph_ok else 'DIFFERENT'})")
+    del graph
+    # iters consecutive steps in one graph, replayed once
+    out.zero_()
+    sel.fill_(-7)
+    graph_n = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_n):
+        for _ in range(iters):
+            run()
+    graph_n.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph_n.replay()
+    torch.cuda.synchronize()
+    graph_n_ms = (time.perf_counter() - t0) * 1e3 / iters
+    graph_n_ok = bool(torch.equal(out, out_eager) and torch.equal(sel, sel_eager))
+    del graph_n
+    log(f"[bench] dsa step: eager {eager_ms * 1e3:.1f} us, graph replay {graph_ms * 1e3:.1f} us, "
+        f"{iters} steps in one graph replay {graph_n_ms * 1e3:.1f} us per step (replay outputs "
+        f"{'identical' if graph_ok and graph_n_ok else 'DIFFERENT'})")
+    dsa_forms = [(eager_ms, "eager")]
+    if graph_ok:
+        dsa_forms.append((graph_ms, "graph replay"))
+    if graph_n_ok:
+        dsa_forms.append((graph_n_ms, f"{iters} steps in one graph replay"))
+    best_ms, best_form = min(dsa_forms)
 
     # The multi-head indexer (32 heads, weights per query): a "full" layer
     # selects with it; an IndexShare "shared" layer reuses the last full
@@ -851,14 +874,15 @@ def bench_dsa(M, W, torch, dev, bits, tens, wsbuf, iters=20, profile=False):
     log(f"[bench] dsa {n_head}-head indexer: append {seg_h[0] * 1e3:.1f} select {seg_h[1] * 1e3:.1f} "
         f"attend {seg_h[2] * 1e3:.1f} us; shared layer (no select) {shared_ms * 1e3:.1f} us")
     return {
-        "dsa_queries_s": round(S / (total * 1e-3), 1),
+        "dsa_queries_s": round(S / (best_ms * 1e-3), 1),
+        "dsa_step_form": best_form,
         "dsa_step_us": {"events": round(total * 1e3, 2), "eager": round(eager_ms * 1e3, 2),
-                        "hip_graph": round(graph_ms * 1e3, 2), "graph_replay_matches_eager": graph_ok},
-        "dsa_graph_queries_s": round(S / (graph_ms * 1e-3), 1),
+                        "hip_graph": round(graph_ms * 1e3, 2), "k_steps_one_graph": round(graph_n_ms * 1e3, 2),
+                        "graph_replays_match_eager": graph_ok and graph_n_ok},
         "dsa_us": {"append": round(seg[0] * 1e3, 2), "select": round(seg[1] * 1e3, 2),
                    "attend": round(seg[2] * 1e3, 2)},
         "dsa_select_GBps": round(scan_bytes / (seg[1] * 1e-3) / 1e9, 1),
-        "dsa_path_GBps": round((scan_bytes + att_bytes) / (total * 1e-3) / 1e9, 1),
+        "dsa_path_GBps": round((scan_bytes + att_bytes) / (best_ms * 1e-3) / 1e9, 1),
         "dsa_heads": {"n_head": n_head, "full_layer_queries_s": round(S / (full_ms * 1e-3), 1),
                       "full_layer_us": round(full_ms * 1e3, 2), "select_us": round(seg_h[1] * 1e3, 2),
                       "select_GBps": round(scan_bytes / (seg_h[1] * 1e-3) / 1e9, 1),
