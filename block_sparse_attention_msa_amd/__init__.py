@@ -48,6 +48,9 @@ DSA_OP_ATTEND_DECODE = 6
 MSA_OP_BLOCK_SCORES_PREFILL = 7
 MSA_OP_INDEX_PROJECT = 8
 MSA_OP_DECODE_STEP = 9
+# call-size limits of include/msa.h
+MSA_MAX_QUERIES = 1 << 18
+MSA_MAX_ROWS = 1 << 24
 
 EXPORTS = (
     "msa_workspace_bytes", "msa_status_string", "msa_index_append", "msa_block_scores",

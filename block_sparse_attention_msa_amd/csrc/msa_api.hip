@@ -47,10 +47,12 @@ msa_status check_cache(const msa_cache* c) {
     return MSA_OK;
 }
 
-// n_q: 0 is an empty call, negative is a shape error; max_pos must lie in the cache.
-msa_status check_count_pos(int64_t n, int32_t max_pos, const msa_cache* c) {
+// n_q: 0 is an empty call, negative is a shape error, more than `limit` is
+// unsupported (the launch grids would overflow a dispatch dimension); max_pos
+// must lie in the cache.
+msa_status check_count_pos(int64_t n, int32_t max_pos, const msa_cache* c, int64_t limit = MSA_MAX_QUERIES) {
     if (n < 0) return MSA_ERR_BAD_SHAPE;
-    if (n > (int64_t(1) << 31) - 1) return MSA_ERR_UNSUPPORTED;
+    if (n > limit) return MSA_ERR_UNSUPPORTED;
     if (max_pos < 0 || static_cast<int64_t>(max_pos) >= c->cap) return MSA_ERR_OUT_OF_RANGE;
     return MSA_OK;
 }
@@ -119,7 +121,7 @@ msa_status append_impl(Mode mode, const msa_dims* dims, const msa_cache* cache, 
                        void* hip_stream) {
     MSA_TRY(check_dims(dims, mode));
     MSA_TRY(check_cache(cache));
-    MSA_TRY(check_count_pos(n_new, max_pos, cache));
+    MSA_TRY(check_count_pos(n_new, max_pos, cache, MSA_MAX_ROWS));
     if (n_new == 0) return MSA_OK;
     MSA_TRY(check_ptrs({d_stream, d_pos}));
     if (d_idx_k_new) {
@@ -230,6 +232,7 @@ const char* msa_status_string(msa_status s) {
 size_t msa_workspace_bytes(const msa_dims* dims, msa_op op, int64_t n_q, int32_t max_pos) {
     const size_t bad = static_cast<size_t>(-1);
     if (n_q < 0 || max_pos < 0) return bad;
+    if (n_q > (op == MSA_OP_INDEX_PROJECT ? MSA_MAX_ROWS : MSA_MAX_QUERIES)) return bad;
     const bool dsa = op == DSA_OP_SELECT || op == DSA_OP_ATTEND_DECODE ||
                      (op == MSA_OP_ATTEND_DECODE && dims && dims->block == 1);
     if (check_dims(dims, dsa ? Mode::Dsa : Mode::Msa) != MSA_OK) return bad;
@@ -270,9 +273,8 @@ msa_status msa_index_project(const msa_dims* dims, const msa_cache* cache, const
     if (proj->d_model < 32 || proj->d_model % 32 || proj->rot_dim < 0 || proj->rot_dim > 64 ||
         proj->rot_dim % 2 || !(proj->eps >= 0.f) || !(proj->rope_theta > 0.f))
         return MSA_ERR_UNSUPPORTED;
-    MSA_TRY(check_count_pos(n_tok, max_pos, cache));
+    MSA_TRY(check_count_pos(n_tok, max_pos, cache, MSA_MAX_ROWS));
     if (n_tok == 0) return MSA_OK;   // empty call: nothing to read or launch
-    if (n_tok > (int64_t(1) << 24)) return MSA_ERR_UNSUPPORTED;
     MSA_TRY(check_ptrs({proj->d_w_q, proj->d_w_k, proj->d_g_q, proj->d_g_k, d_x, d_stream, d_pos, d_idx_q}));
     MSA_TRY(check_index_cache(cache));
     MSA_TRY(check_ptrs({d_ws}));
@@ -319,6 +321,7 @@ msa_status msa_topk_blocks(const msa_dims* dims, const float* d_bs, int64_t nblk
                            int32_t* d_n_sel, void* hip_stream) {
     MSA_TRY(check_dims(dims, Mode::Msa));
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (n_q > MSA_MAX_QUERIES) return MSA_ERR_UNSUPPORTED;
     if (max_pos < 0) return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
     MSA_TRY(check_ptrs({d_bs, d_pos, d_sel, d_n_sel}));
@@ -349,6 +352,7 @@ msa_status msa_block_scores_prefill(const msa_dims* dims, const msa_cache* cache
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (n_q > MSA_MAX_QUERIES) return MSA_ERR_UNSUPPORTED;
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
@@ -369,6 +373,7 @@ msa_status msa_select_prefill(const msa_dims* dims, const msa_cache* cache, cons
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (n_q > MSA_MAX_QUERIES) return MSA_ERR_UNSUPPORTED;
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch
@@ -471,6 +476,7 @@ msa_status msa_attend_prefill(const msa_dims* dims, const msa_cache* cache, cons
     MSA_TRY(check_dims(dims, Mode::Msa));
     MSA_TRY(check_cache(cache));
     if (n_q < 0) return MSA_ERR_BAD_SHAPE;
+    if (n_q > MSA_MAX_QUERIES) return MSA_ERR_UNSUPPORTED;
     if (stream < 0 || stream >= cache->n_stream || pos0 < 0 || pos0 + n_q > cache->cap)
         return MSA_ERR_OUT_OF_RANGE;
     if (n_q == 0) return MSA_OK;   // empty call: nothing to read or launch

@@ -49,6 +49,13 @@
  *    appended.  No exception crosses this ABI.
  *  - Device pointers must be 16-byte aligned (128-bit vector access).
  *  - n_q == 0 (or n_new == 0) is a valid empty call: MSA_OK, nothing runs.
+ *  - Call sizes: at most MSA_MAX_QUERIES queries per select, block-score,
+ *    top-k, attention or decode-step call, and MSA_MAX_ROWS rows (tokens)
+ *    per append or projection call, so that every launch grid stays within
+ *    the 2^32 work-items of one dispatch dimension; dsa_select and
+ *    dsa_select_heads take at most 65535 queries (the query is the second
+ *    grid dimension of their scans).  A larger call returns
+ *    MSA_ERR_UNSUPPORTED (split it into several calls).
  *  - Supported geometry: n_group 4, heads_per_group 16, head_dim 128,
  *    idx_dim 128; MSA: block 128, 1 <= top_k <= 64; DSA: block 1,
  *    1 <= top_k <= 4096.  Anything else returns MSA_ERR_UNSUPPORTED.
@@ -70,6 +77,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Largest queries per select / attention / step call, rows per append or
+ * projection call (see the call-size note above). */
+#define MSA_MAX_QUERIES ((int64_t)1 << 18)
+#define MSA_MAX_ROWS ((int64_t)1 << 24)
 
 typedef enum msa_status {
     MSA_OK = 0,

@@ -366,3 +366,54 @@ def test_decode_step_validation_and_workspace(L):
     assert step(n=-1) == SHAPE
     assert step(cache=_cache(idx=None, dsa=None)) == NULL        # no index cache
     assert step(k_new=None, v_new=None) not in (NULL, ALIGN, SHAPE, UNSUP, WS)   # accepted (no GPU here)
+
+
+def test_call_size_limits(L):
+    """Calls larger than the launch grids allow are refused before any
+    launch: more than MSA_MAX_QUERIES queries per select / block-score /
+    top-k / attention / step call (65535 for the DSA selections), more than
+    MSA_MAX_ROWS rows per append or projection call; the workspace query
+    refuses them too.  The limits are
+    the header's (parsed from include/msa.h)."""
+    hdr = open(os.path.join(ROOT, "include", "msa.h")).read()
+    mq = int(re.search(r"#define MSA_MAX_QUERIES \(\(int64_t\)1 << (\d+)\)", hdr).group(1))
+    mr = int(re.search(r"#define MSA_MAX_ROWS \(\(int64_t\)1 << (\d+)\)", hdr).group(1))
+    assert (1 << mq, 1 << mr) == (M.MSA_MAX_QUERIES, M.MSA_MAX_ROWS)
+    Q, R = M.MSA_MAX_QUERIES, M.MSA_MAX_ROWS
+    # the attention launch's widest grid (4 groups x 8 splits of 256 threads
+    # per query) and the append's (128 threads per row) fit one dimension
+    assert Q * 4 * 8 * 256 < 1 << 32 and R * 128 < 1 << 32
+    d, dd = M.msa_dims(), M.dsa_dims(2048)
+    c = _cache(cap=1 << 20, n_stream=1)
+    big = 1 << 30
+    calls = {
+        "msa_select": lambda n: L.msa_select(ctypes.byref(d), ctypes.byref(c), A, A, A, n, 100, A, A, A, big, None),
+        "msa_block_scores": lambda n: L.msa_block_scores(ctypes.byref(d), ctypes.byref(c), A, A, A, n, 100, A, 8,
+                                                         None),
+        "msa_topk_blocks": lambda n: L.msa_topk_blocks(ctypes.byref(d), A, 8, A, n, 100, A, A, None),
+        "msa_attend_decode": lambda n: L.msa_attend_decode(ctypes.byref(d), ctypes.byref(c), A, A, A, n, 100, A, A,
+                                                           A, big, None),
+        "dsa_select": lambda n: L.dsa_select(ctypes.byref(dd), ctypes.byref(c), A, A, A, n, 100, A, A, A, big,
+                                             None),
+        "dsa_select_heads": lambda n: L.dsa_select_heads(ctypes.byref(dd), ctypes.byref(c), A, A, 32, A, A, n, 100,
+                                                         A, A, A, big, None),
+        "msa_select_prefill": lambda n: L.msa_select_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 0, n, A, A, A,
+                                                             big, None),
+        "msa_attend_prefill": lambda n: L.msa_attend_prefill(ctypes.byref(d), ctypes.byref(c), A, 0, 0, n, A, A, A,
+                                                             big, None),
+        "msa_decode_step": lambda n: L.msa_decode_step(ctypes.byref(d), ctypes.byref(c), A, A, n, 100, A, A, A, A,
+                                                       A, A, A, A, A, big, None),
+    }
+    for name, f in calls.items():
+        lim = 65535 if name.startswith("dsa_") else Q     # the DSA scans' query grid dimension
+        assert f(lim + 1) == UNSUP, name
+        assert f(lim) != UNSUP, name         # at the limit: accepted (fails later only for want of a GPU)
+    app = lambda n: L.msa_index_append(ctypes.byref(d), ctypes.byref(c), A, A, n, 100, A, A, A, None)
+    assert app(R + 1) == UNSUP
+    assert app(R) != UNSUP
+    bad = ctypes.c_size_t(-1).value
+    for op in (M.MSA_OP_SELECT, M.MSA_OP_ATTEND_DECODE, M.MSA_OP_ATTEND_PREFILL, M.MSA_OP_DECODE_STEP):
+        assert L.msa_workspace_bytes(ctypes.byref(d), op, Q + 1, 100) == bad, op
+        assert L.msa_workspace_bytes(ctypes.byref(d), op, Q, 100) < 1 << 40, op
+    assert L.msa_workspace_bytes(ctypes.byref(d), M.MSA_OP_INDEX_PROJECT, R + 1, 100) == bad
+    assert L.msa_workspace_bytes(ctypes.byref(d), M.MSA_OP_INDEX_PROJECT, R, 100) < 1 << 40
