@@ -188,3 +188,73 @@ def test_decode_step_graph_replay_matches_eager(ctx, n_stream):
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), f"replay {r}: output differs"
         assert torch.equal(sel, ref_sel) and torch.equal(n_sel, ref_n), f"replay {r}: selection differs"
+
+
+@pytest.mark.parametrize("fmt", ["f16_index", "int8_kv", "q4_kv"])
+def test_decode_step_other_cache_formats(fmt):
+    """msa_decode_step on an fp16 index cache, and on int8 and 4-bit K/V
+    caches (the separate calls' kernels inside one call), equals
+    msa_index_append + msa_select + msa_attend_decode bit for bit: the rows
+    it appends (codes and scales included), the selection and the output.
+    Every cache row is first written through the append entry point; the
+    step's own rows are then zeroed, so both forms must write them."""
+    wl = W.Workload(f"step_{fmt}", "msa_decode", 3, 3000, (0, 1, 2, 1), (2999, 1500, 130, 700))
+    log(f"[decode step] {fmt}: n_q={wl.n_q} max_pos={wl.max_pos}")
+    host, qs = W.caches(wl), W.queries(wl)
+    dims = M.msa_dims(wl.top_k, W.SCALE)
+    S, cap = wl.n_stream, wl.cap
+    st, ps = qs["stream"].astype(np.int64), qs["pos"].astype(np.int64)
+    ti, tp = torch.from_numpy(st), torch.from_numpy(ps)
+    kv_format = {"f16_index": M.KV_BF16, "int8_kv": M.KV_INT8, "q4_kv": M.KV_Q4}[fmt]
+    new_idx = dev(host["idx_k"][st, ps])
+    new_k = dev_bits(host["k"][st, ps], torch.bfloat16)
+    new_v = dev_bits(host["v"][st, ps], torch.bfloat16)
+    q, idx_q = dev_bits(qs["q"], torch.bfloat16), dev(qs["idx_q"])
+    stream, pos = dev(qs["stream"]), dev(qs["pos"])
+    all_st = torch.arange(S, dtype=torch.int32, device=DEV).repeat_interleave(cap)
+    all_ps = torch.arange(cap, dtype=torch.int32, device=DEV).repeat(S)
+    results = []
+    for fused in (False, True):
+        t = {}
+        if fmt == "f16_index":
+            t["idx_k_f16"] = torch.zeros((S, cap, 4, 128), dtype=torch.float16, device=DEV)
+        else:
+            t["idx_k"] = torch.zeros((S, cap, 4, 128), dtype=torch.float32, device=DEV)
+        if kv_format == M.KV_BF16:
+            t["k"] = torch.zeros((S, cap, 4, 128), dtype=torch.bfloat16, device=DEV)
+        else:
+            t["k"] = torch.zeros((S, cap, 4, 128 if kv_format == M.KV_INT8 else 64), dtype=torch.uint8, device=DEV)
+            t["k_scale"] = torch.zeros((S, cap, 4, 4), dtype=torch.float32, device=DEV)
+            t["v_scale"] = torch.zeros_like(t["k_scale"])
+        t["v"] = torch.zeros_like(t["k"])
+        cache = M.make_cache(kv_format=kv_format, **t)
+        M.msa_index_append(dims, cache, all_st, all_ps, cap - 1, idx_k_new=dev(host["idx_k"].reshape(S * cap, 4, 128)),
+                           k_new=dev_bits(host["k"].reshape(S * cap, 4, 128), torch.bfloat16),
+                           v_new=dev_bits(host["v"].reshape(S * cap, 4, 128), torch.bfloat16))
+        for name in t:
+            t[name][ti, tp] = 0
+        sel = torch.full((wl.n_q, 4, wl.top_k), -7, dtype=torch.int32, device=DEV)
+        n_sel = torch.full((wl.n_q, 4), -7, dtype=torch.int32, device=DEV)
+        out = torch.zeros((wl.n_q, 64, 128), dtype=torch.float32, device=DEV)
+        if fused:
+            ws = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_DECODE_STEP, wl.n_q, wl.max_pos), 256),
+                             dtype=torch.uint8, device=DEV)
+            M.msa_decode_step(dims, cache, stream, pos, wl.max_pos, new_idx, new_k, new_v, idx_q, q, sel, n_sel,
+                              out, ws)
+        else:
+            M.msa_index_append(dims, cache, stream, pos, wl.max_pos, idx_k_new=new_idx, k_new=new_k, v_new=new_v)
+            ws_s = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_SELECT, wl.n_q, wl.max_pos), 256),
+                               dtype=torch.uint8, device=DEV)
+            M.msa_select(dims, cache, idx_q, stream, pos, wl.max_pos, sel, n_sel, ws_s)
+            ws_a = torch.empty(max(M.workspace_bytes(dims, M.MSA_OP_ATTEND_DECODE, wl.n_q, wl.max_pos), 256),
+                               dtype=torch.uint8, device=DEV)
+            M.msa_attend_decode(dims, cache, q, stream, pos, wl.max_pos, sel, out, ws_a)
+        torch.cuda.synchronize()
+        r = {name: (x.view(torch.int16) if x.dtype in (torch.bfloat16, torch.float16) else x).cpu()
+             for name, x in t.items()}
+        r.update(sel=sel.cpu(), n_sel=n_sel.cpu(), out=out.cpu())
+        results.append(r)
+    for name in results[0]:
+        assert torch.equal(results[0][name], results[1][name]), f"{name}: the step differs from the separate calls"
+    assert torch.isfinite(results[1]["out"]).all()
+    assert (results[1]["n_sel"] > 0).all()
