@@ -102,42 +102,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
         const f32x4* rows = reinterpret_cast<const f32x4*>(
             idx_k + pg.block_row_uniform(q_stream[i], b) * (kGroups * kIdxDim)) + g * 32 + c;
         const int t_begin = (wave % kScanWavesPerBlock) * kScanTokensPerWave;
-        int t_end = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
-        bool own = false;             // step: this wave holds the query's own token (its last)
-        bool other = false;           // step: ... or another query's new row
-        if constexpr (kStep) {
-            own = t_begin < t_end && b * kBlock + t_end - 1 == p;
-            const int s = q_stream[i];
-            for (int64_t j0 = 0; j0 < st.n_q; j0 += 64) {
-                const int64_t j = j0 + lane;
-                bool hit = false;
-                if (j < st.n_q && j != i && q_stream[j] == s) {
-                    const int pj = q_pos[j] - b * kBlock;
-                    hit = pj >= t_begin && pj < t_end;
-                }
-                other = other || __builtin_amdgcn_ballot_w64(hit) != 0;
-            }
-            if (other) {
-                // token by token: the row of the query that appends it, if any
-                for (int t = t_begin; t < t_end; ++t) {
-                    const int tok = b * kBlock + t;
-                    int64_t src_q = tok == p ? i : -1;
-                    for (int64_t j0 = 0; j0 < st.n_q && src_q < 0; j0 += 64) {
-                        const int64_t j = j0 + lane;
-                        const bool hit = j < st.n_q && q_stream[j] == s && q_pos[j] == tok;
-                        const uint64_t mk = __builtin_amdgcn_ballot_w64(hit);
-                        if (mk) src_q = j0 + __builtin_ctzll(mk);
-                    }
-                    const f32x4* src = src_q >= 0
-                                           ? reinterpret_cast<const f32x4*>(st.idx_k_new + src_q * kGroups * kIdxDim) + g * 32 + c
-                                           : rows + t * kRowF4;
-                    m = fmaxf(m, row16_sum(dot8(q0, q1, src[0], src[16])));
-                }
-                t_end = t_begin;      // done
-            } else if (own) {
-                --t_end;              // the own token is scored from the input below
-            }
-        }
+        const int t_last = min(t_begin + kScanTokensPerWave, p - b * kBlock + 1);   // causal: tokens <= p
+        int t_end = t_last;
+        // step: this wave holds the query's own token (its last), scored
+        // from the input after the loop
+        const bool own = kStep && t_begin < t_end && b * kBlock + t_end - 1 == p;
+        if (own) --t_end;
         int t = t_begin;
         for (; t + kScanUnroll <= t_end; t += kScanUnroll) {
             f32x4 a[kScanUnroll], bb[kScanUnroll];
@@ -154,9 +124,44 @@ __global__ __launch_bounds__(64 * kScanWaves) void block_scores_decode_kernel(
             const f32x4 bb = rows[t * kRowF4 + 16];
             m = fmaxf(m, row16_sum(dot8(q0, q1, a, bb)));
         }
-        if (kStep && own && !other) {
+        if (own) {
             const f32x4* src = reinterpret_cast<const f32x4*>(st.idx_k_new + i * kGroups * kIdxDim) + g * 32 + c;
             m = fmaxf(m, row16_sum(dot8(q0, q1, src[0], src[16])));
+        }
+        if constexpr (kStep) {
+            // Rare: another query of the launch appends into this wave's
+            // tokens, so the rows read above may not hold it yet.  Checked
+            // after the loop (the loop's loads need not wait for this one),
+            // and the wave's tokens are then scored again one by one from
+            // wherever each lives.
+            const int s = q_stream[i];
+            bool other = false;
+            for (int64_t j0 = 0; j0 < st.n_q; j0 += 64) {
+                const int64_t j = j0 + lane;
+                bool hit = false;
+                if (j < st.n_q && j != i && q_stream[j] == s) {
+                    const int pj = q_pos[j] - b * kBlock;
+                    hit = pj >= t_begin && pj < t_last;
+                }
+                other = other || __builtin_amdgcn_ballot_w64(hit) != 0;
+            }
+            if (other) {
+                m = -INFINITY;
+                for (int tt = t_begin; tt < t_last; ++tt) {
+                    const int tok = b * kBlock + tt;
+                    int64_t src_q = tok == p ? i : -1;
+                    for (int64_t j0 = 0; j0 < st.n_q && src_q < 0; j0 += 64) {
+                        const int64_t j = j0 + lane;
+                        const bool hit = j < st.n_q && q_stream[j] == s && q_pos[j] == tok;
+                        const uint64_t mk = __builtin_amdgcn_ballot_w64(hit);
+                        if (mk) src_q = j0 + __builtin_ctzll(mk);
+                    }
+                    const f32x4* src = src_q >= 0
+                                           ? reinterpret_cast<const f32x4*>(st.idx_k_new + src_q * kGroups * kIdxDim) + g * 32 + c
+                                           : rows + tt * kRowF4;
+                    m = fmaxf(m, row16_sum(dot8(q0, q1, src[0], src[16])));
+                }
+            }
         }
     }
     __shared__ float red[kScanWaves][kGroups];
