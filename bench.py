@@ -442,8 +442,10 @@ def main():
 
 
 def measure_copy_bandwidth(torch, dev, n_bytes=1 << 30, iters=10):
-    """Plain device-to-device copy (read + write bytes / time): the
-    practical HBM ceiling the roofline fractions can be compared with."""
+    """Plain device-to-device copy (torch copy_, read + write bytes / time),
+    reported for context only: a copy that reads and writes runs below a
+    read-only stream (the decode scan reads faster than it), so it is no
+    ceiling for the kernels here; their fractions are of the 8 TB/s peak."""
     src = torch.empty(n_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     dst.copy_(src)
