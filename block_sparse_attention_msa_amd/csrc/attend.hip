@@ -31,7 +31,12 @@
 //    slice of S^T = K Q^T after its matrix-core product (one slice is one
 //    scale block), and V's are folded into the probabilities, one bf16 P
 //    operand per 32-dim block of the output, so the only rounding is that of
-//    the scaled probabilities, as in the bf16 path.
+//    the scaled probabilities, as in the bf16 path.  4-bit codes enter
+//    biased, as c + 136 (bf16 bits 0x4300 | nibble, two bit operations per
+//    pair instead of a conversion per value): each score slice subtracts
+//    136 x the sum of its query values before its scale, and the output
+//    subtracts 136 x the sum of the bf16 probabilities it applied (kept per
+//    lane and rescaled with the accumulators, subtracted once at the end).
 #include "common.hpp"
 #include "topk_regs.hpp"
 
@@ -289,16 +294,33 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         }
     };
     // 8 codes -> 8 bf16 values (exact): int8 bytes, or the low / high
-    // nibbles (stored + 8) of 8 bytes
+    // nibbles n (the code plus 8) of 8 bytes.  A nibble enters biased, as
+    // 128 + n (bf16 bits 0x4300 | n, so a pair is one byte permute and one
+    // and-or); the scores and the output subtract the bias's share after
+    // their products (kQBias below).
     auto codes8 = [&](uint32_t w0, uint32_t w1, int mode) __attribute__((always_inline)) {
+        if (mode != 0) {
+            u32x4 r;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t w = h < 2 ? w0 : w1;
+                // bytes 2 (h % 2), 2 (h % 2) + 1 of w at bits 0..7 and 16..23
+                uint32_t pr = __builtin_amdgcn_perm(0u, w, (h & 1) ? 0x0c030c02u : 0x0c010c00u);
+                if (mode == 2) pr >>= 4;
+                // (pr & 0x000f000f) | 0x43004300 in one instruction (VOP3 takes no
+                // literal here, so both constants sit in registers)
+                uint32_t o;
+                asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(o) : "v"(pr), "v"(0x000f000fu), "v"(0x43004300u));
+                r[h] = o;
+            }
+            return r;
+        }
         float f[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
             const uint32_t word = b < 4 ? w0 : w1;
             const int byte = static_cast<int>((word >> (8 * (b & 3))) & 0xffu);
-            const int code = mode == 0 ? static_cast<int>(static_cast<int8_t>(byte))
-                                       : (mode == 1 ? (byte & 15) : (byte >> 4)) - 8;
-            f[b] = static_cast<float>(code);
+            f[b] = static_cast<float>(static_cast<int8_t>(byte));
         }
         return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                      pack_bf16x2(f[6], f[7])};
@@ -333,6 +355,21 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         }
     };
     const float* ks_cur = kscl_s[0];           // scales of the unit being computed (quantized K, V)
+    // 4-bit codes enter as c + kQBias (c = n - 8): a score slice is
+    // scale * (K'Q - kQBias * sum of the slice's query values), the output
+    // O - kQBias * (sum of the applied probabilities of the dim block)
+    constexpr float kQBias = 136.f;
+    float qsum[4] = {0.f, 0.f, 0.f, 0.f};     // head l16, dims 32 ks .. 32 ks + 31
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};     // head l16, dim block b: this lane's applied probabilities
+    if constexpr (kQ == 2) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float t = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t += static_cast<float>(qb[ks][j]);
+            qsum[ks] = kQBias * sum_xor32(sum_xor16(t));
+        }
+    }
     const float* vs_cur = vscl_s[0];
 
     float m_run = -INFINITY, l_run = 0.f;
@@ -395,7 +432,8 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
                     for (int ks = 0; ks < 4; ++ks) {
                         const f32x4 part = mfma_16x16x32_bf16(kA[t][ks], qb[ks], f32x4{0.f, 0.f, 0.f, 0.f});
                         const f32x4 sc = *reinterpret_cast<const f32x4*>(ks_cur + ks * kUnit + 32 * wave + 16 * t + 4 * l4);
-                        st[t] += sc * part;
+                        if constexpr (kQ == 2) st[t] += sc * (part - qsum[ks]);
+                        else st[t] += sc * part;
                     }
                 }
 #pragma unroll
@@ -461,6 +499,19 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
                 for (int dt = 2 * b; dt < 2 * b + 2; ++dt) acc[dt] = mfma_16x16x32_bf16(va[dt], pb, acc[dt] * alpha);
+                if constexpr (kQ == 2) {
+                    // this lane's 8 of the probabilities the product applied, rescaled
+                    // as the accumulators are (the bias is subtracted after the loop)
+                    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                    const bf16x2_t ones2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);   // {1, 1}
+                    float ps = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t wj = pw[j];
+                        ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wj), ones2, ps, false);
+                    }
+                    psum[b] = psum[b] * alpha + ps;
+                }
             }
         }
     };
@@ -514,6 +565,15 @@ __global__ __launch_bounds__(kAttThreads, 1) void attend_kernel(KernelArgs ka) {
         }
     }
 
+    if constexpr (kQ == 2) {
+        // the 4-bit codes' bias: kQBias times the applied probabilities of head l16
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const float vb = kQBias * sum_xor32(sum_xor16(psum[b]));
+            acc[2 * b] -= f32x4{vb, vb, vb, vb};
+            acc[2 * b + 1] -= f32x4{vb, vb, vb, vb};
+        }
+    }
     // ---- merge the four waves (lane holds O^T[dim 16*dt + 4*l4 + r][head l16])
     __syncthreads();
     float* mrg = reinterpret_cast<float*>(kbuf0);  // [wave][head][dim]
